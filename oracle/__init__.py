@@ -1,0 +1,22 @@
+"""CPU oracle for Block-Union KV Selection and chunked-prefill attention (test infrastructure).
+
+Plain, slow, obviously correct numpy code in float64, written from the CompactAttention pages
+("CompactAttention: Accelerating Chunked Prefill with Block-Union KV Selection", abstract):
+the per-group KV block tables are the explicit OR of the per-head 2D block masks over the
+chunk's Q-blocks and over the query heads of one GQA group, and attention for every query head
+of the group runs over exactly the keys of those blocks.
+
+This package is test infrastructure.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import it.  It shares no code, header, table or constant with the HIP
+library, and it imports nothing from it.
+
+Pin status (what each function is checked against besides itself):
+  block_union_tables   pinned: brute-force loops, superset/minimality, all-ones/all-zero/G=1
+  paged_attention      pinned: dense causal attention via torch SDPA (all-ones masks),
+                       per-token brute force, per-query block-sparse SDPA special case,
+                       closed forms (constant V, q=0, single key), LSE-merge identity,
+                       page-permutation invariance
+  attention_rows       pinned: equals paged_attention on every row it is given
+"""
+from .union import block_union_tables  # noqa: F401
+from .attention import paged_attention, attention_rows  # noqa: F401
