@@ -1,0 +1,135 @@
+/*
+ * cpa.h - C ABI of the Block-Union KV Selection hot path for chunked prefill (MI355X, gfx950).
+ *
+ * The method is CompactAttention's Block-Union KV Selection ("CompactAttention: Accelerating
+ * Chunked Prefill with Block-Union KV Selection", abstract): per-head 2D block-sparse masks over
+ * (query block, KV block) are treated as KV-selection signals, not as kernel execution plans.
+ * A union over the chunk's query blocks and a union over the query heads that share one KV head
+ * turn them into the minimal per-group KV block tables that keep every selected block; attention
+ * for every query head of the group then reads exactly those blocks in place from the paged KV
+ * cache, with no KV compaction.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.  The caller allocates
+ *     and owns every buffer; the library allocates no device memory and keeps no global state,
+ *     so concurrent calls on different streams are safe.
+ *   - Calls only enqueue work on `stream` (0 = the default stream) and return without
+ *     synchronising.  Results are visible in stream order.
+ *   - Block size: query blocks, KV blocks and KV pages all hold CPA_BLOCK = 64 tokens.
+ *   - GQA grouping: query head h belongs to KV group h / (Hq / Hkv).
+ *   - Host-side argument checks run before any HIP call; on failure nothing is enqueued and a
+ *     CPA_ERR_* code is returned.  Device-resident data (lengths, tables, page ids) cannot be
+ *     checked on the host: the kernels clamp every index they derive from it so that no access
+ *     leaves the buffers described here, and the per-call notes say what such data must satisfy
+ *     for the result to be meaningful.
+ */
+#ifndef CPA_H
+#define CPA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPA_BLOCK 64
+#define CPA_MAX_KV_BLOCKS 65536 /* per sequence: 4M tokens */
+
+typedef enum {
+  CPA_OK = 0,
+  CPA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+  CPA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+  CPA_ERR_ALIGN = 3,       /* a pointer or stride breaks the alignment stated below         */
+  CPA_ERR_UNSUPPORTED = 4, /* dtype, head dim or group size this build does not implement  */
+  CPA_ERR_CAPACITY = 5,    /* table capacity smaller than the KV-block count               */
+  CPA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch                      */
+} cpa_status;
+
+typedef enum { CPA_F32 = 0, CPA_BF16 = 1 } cpa_dtype;
+
+/*
+ * cpa_build_block_tables - masks -> minimal GQA-aware per-group KV block tables + counts.
+ *
+ * Implements the Q-block union and the intra-group union of the CompactAttention abstract:
+ * logical KV block kb is in the table of (sequence b, KV group g) iff some query head h of
+ * group g and some query block qi of b's chunk have masks[b][h][qi][kb] != 0 with
+ * kb <= prefix_blocks[b] + qi (the block is causally reachable from that query block).
+ * Entries outside that causal region, and padding past a sequence's extent, are ignored.
+ *
+ *   masks          uint8 [B][Hq][nqb_max][nkvb_max], nonzero = selected.
+ *   prefix_blocks  int32 [B]: prefix length of sequence b in blocks (first query block's
+ *                  absolute block index).
+ *   chunk_blocks   int32 [B]: query blocks in sequence b's chunk (ceil(chunk_len / 64)).
+ *                  Device values are clamped to [0, nqb_max] and prefix + chunk to nkvb_max.
+ *   tables   (out) int32 [B][Hkv][table_cap]: selected logical KV-block ids in strictly
+ *                  ascending order, then -1 up to table_cap.  Requires table_cap >= nkvb_max.
+ *   counts   (out) int32 [B][Hkv]: number of ids in each table.
+ *
+ * Errors: CPA_ERR_NULL (any pointer NULL with B > 0), CPA_ERR_SHAPE (B, Hq, Hkv, nqb_max,
+ * nkvb_max negative; Hkv == 0; Hq % Hkv != 0; nkvb_max > CPA_MAX_KV_BLOCKS),
+ * CPA_ERR_CAPACITY (table_cap < nkvb_max), CPA_ERR_LAUNCH.
+ * The result is bit-exact: it has exactly one correct value.
+ */
+cpa_status cpa_build_block_tables(const uint8_t* masks, int B, int Hq, int Hkv, int nqb_max,
+                                  int nkvb_max, const int32_t* prefix_blocks,
+                                  const int32_t* chunk_blocks, int32_t* tables, int table_cap,
+                                  int32_t* counts, hipStream_t stream);
+
+/*
+ * cpa_chunked_prefill - attention of one prefill chunk per sequence over the selected blocks.
+ *
+ * For every sequence b, query head h (group g = h / (Hq/Hkv)) and chunk row r (absolute
+ * position p = prefix_len[b] + r), attends over the key tokens t of the blocks
+ * tables[b][g][0 .. counts[b][g]) with t <= p (causal cut on the chunk's own blocks), reading
+ * K/V in place from the paged cache through page_map; fp32 online softmax with scale sm_scale.
+ * This is the "selected KV blocks accessed in place without explicit KV compaction" step of
+ * the CompactAttention abstract.
+ *
+ *   q        [Tq][Hq][d] in `dtype`, d contiguous; rows of sequence b are cu_q[b] .. cu_q[b+1]
+ *            (Tq = cu_q[B]).  16-byte aligned.
+ *   k_pages, v_pages  paged cache in `dtype`: element (page, kv head, token-in-page, c) at
+ *            page*page_stride + head*head_stride + token*token_stride + c (strides in elements,
+ *            c contiguous); the dense layout [n_pages][Hkv][64][d] has page_stride = Hkv*64*d,
+ *            head_stride = 64*d, token_stride = d.  Base pointers 16-byte aligned and every
+ *            stride a multiple of 16 bytes.
+ *   n_pages  physical pages in the pool.  A page id outside [0, n_pages), or a table entry
+ *            outside [0, page_map_stride), is never dereferenced: its keys and values read as NaN.
+ *   page_map int32 [B][page_map_stride]: logical KV block -> physical page.
+ *   tables, counts, table_cap  as produced by cpa_build_block_tables (ids ascending; counts are
+ *            clamped to table_cap).
+ *   cu_q     int32 [B+1], prefix_len int32 [B]: device arrays; prefix_len[b] must be a multiple
+ *            of 64 (it is the absolute position of the chunk's first row) and the chunk's own K/V
+ *            must already be in the cache.  Chunk lengths are clamped to max_chunk_len.
+ *   max_chunk_len  host int >= every chunk length (sizes the grid).
+ *   sm_scale softmax scale, > 0; pass 0 for 1/sqrt(d).
+ *   o  (out) [Tq][Hq][d] in `dtype`.  A row with no visible key gets zeros.
+ *   lse (out, optional) float [Tq][Hq]: natural-log sum-exp of the scaled scores (-inf for a
+ *            row with no visible key).  NULL to skip.
+ *
+ * Supported: dtype CPA_BF16 (bf16 MFMA, fp32 accumulation and softmax, P rounded to bf16
+ * before the PV product) and CPA_F32 (fp32 MFMA end to end); d in {64, 128};
+ * G = Hq/Hkv in {1, 2, 4} or a multiple of 4 up to 32.
+ * Errors: CPA_ERR_NULL, CPA_ERR_SHAPE (negative sizes, Hq % Hkv != 0, table_cap < 0,
+ * page_map_stride < 1 with B > 0, strides too small to hold a page), CPA_ERR_ALIGN,
+ * CPA_ERR_UNSUPPORTED, CPA_ERR_LAUNCH.
+ */
+cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
+                               const void* v_pages, int64_t page_stride, int64_t head_stride,
+                               int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                               int page_map_stride, const int32_t* tables, int table_cap,
+                               const int32_t* counts, const int32_t* cu_q,
+                               const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                               int max_chunk_len, float sm_scale, void* o, float* lse,
+                               hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (host pointer, never NULL). */
+const char* cpa_status_string(cpa_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int cpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CPA_H */

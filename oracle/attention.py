@@ -83,15 +83,16 @@ def paged_attention(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
 
 
 def attention_rows(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, Hkv, samples,
-                   scale=None):
+                   scale=None, return_nvis=False):
     """Selected rows only.  samples int [n][3] of (b, h, r) with r the row within sequence b's
-    chunk.  Returns O float64 [n][d] and LSE float64 [n]."""
+    chunk.  Returns O float64 [n][d] and LSE float64 [n] (and the visible-key count per row)."""
     samples = np.asarray(samples, dtype=np.int64).reshape(-1, 3)
     Tq, Hq, d = q.shape
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     O = np.zeros((len(samples), d), dtype=np.float64)
     LSE = np.full(len(samples), -np.inf, dtype=np.float64)
+    NV = np.zeros(len(samples), dtype=np.int64)
     groups = {}
     for i, (b, h, r) in enumerate(samples):
         groups.setdefault((int(b), int(h) // G), []).append(i)
@@ -104,8 +105,11 @@ def attention_rows(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_l
         Q = q[int(cu_q[b]) + rs, hs, :].astype(np.float64)                      # [n][d]
         S = (Q @ K.T) * scale
         visible = pos[None, :] <= (int(prefix_len[b]) + rs)[:, None]
-        o, lse, _ = _softmax_rows(S, visible, V)
+        o, lse, nv = _softmax_rows(S, visible, V)
         O[idx] = o
         LSE[idx] = lse
+        NV[idx] = nv
+    if return_nvis:
+        return O, LSE, NV
     return O, LSE
 

@@ -1,0 +1,20 @@
+"""Block-Union KV Selection for chunked prefill on MI355X (gfx950).
+
+Two entry points, both thin wrappers over the C ABI in include/cpa.h:
+
+* build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv) -> (tables, counts)
+* chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len,
+                  max_chunk_len) -> (o, lse)
+
+The library must be built first (``python -m sparse_attention_long_reduce_amd.build``); nothing
+here falls back to another implementation.
+"""
+from .api import (  # noqa: F401
+    BLOCK,
+    attention_flops,
+    build_block_tables,
+    chunked_prefill,
+    status_string,
+    version,
+)
+from ._lib import CpaError, EXPORTS, LIB_PATH, load  # noqa: F401

@@ -1,0 +1,41 @@
+"""ctypes view of libcpa.so: loads the in-tree library and declares every exported symbol."""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpa.so")
+
+EXPORTS = ("cpa_build_block_tables", "cpa_chunked_prefill", "cpa_status_string", "cpa_version")
+
+_lib = None
+
+
+def load():
+    """Load libcpa.so once; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_attention_long_reduce_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    c = ctypes
+    vp, i32, i64, f32 = c.c_void_p, c.c_int, c.c_int64, c.c_float
+    lib.cpa_build_block_tables.restype = i32
+    lib.cpa_build_block_tables.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.cpa_chunked_prefill.restype = i32
+    lib.cpa_chunked_prefill.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, vp,
+                                        vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+    lib.cpa_status_string.restype = c.c_char_p
+    lib.cpa_status_string.argtypes = [i32]
+    lib.cpa_version.restype = i32
+    lib.cpa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+class CpaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = load().cpa_status_string(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+        self.status = status

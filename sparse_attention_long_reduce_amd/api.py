@@ -1,0 +1,128 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+torch supplies device memory and the current HIP stream; every step of the path runs in the
+library's HIP kernels.  Names and semantics follow include/cpa.h.
+"""
+import math
+
+import torch
+
+from ._lib import CpaError, load
+
+BLOCK = 64
+F32, BF16 = 0, 1
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev_i32(x, name):
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.int32 and x.is_contiguous()):
+        raise TypeError(f"{name} must be a contiguous int32 CUDA tensor")
+    return x
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv, table_cap=None, tables=None,
+                       counts=None, stream=None):
+    """masks uint8 [B][Hq][nqb_max][nkvb_max] (CUDA) -> (tables int32 [B][Hkv][cap], counts int32 [B][Hkv]).
+
+    prefix_blocks / chunk_blocks are int32 CUDA tensors [B].  Output tensors may be passed in.
+    """
+    if not (masks.is_cuda and masks.dtype == torch.uint8 and masks.is_contiguous() and masks.dim() == 4):
+        raise TypeError("masks must be a contiguous 4-D uint8 CUDA tensor")
+    B, Hq, nqb_max, nkvb_max = masks.shape
+    _dev_i32(prefix_blocks, "prefix_blocks")
+    _dev_i32(chunk_blocks, "chunk_blocks")
+    cap = nkvb_max if table_cap is None else int(table_cap)
+    if tables is None:
+        tables = torch.empty((B, Hkv, cap), dtype=torch.int32, device=masks.device)
+    if counts is None:
+        counts = torch.empty((B, Hkv), dtype=torch.int32, device=masks.device)
+    _dev_i32(tables, "tables")
+    _dev_i32(counts, "counts")
+    if tables.numel() != B * Hkv * cap or counts.numel() != B * Hkv:
+        raise ValueError("tables/counts have the wrong size")
+    st = load().cpa_build_block_tables(_ptr(masks), B, Hq, Hkv, nqb_max, nkvb_max,
+                                       _ptr(prefix_blocks), _ptr(chunk_blocks), _ptr(tables), cap,
+                                       _ptr(counts), _stream(stream))
+    if st != 0:
+        raise CpaError(st, "cpa_build_block_tables")
+    return tables, counts
+
+
+def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len,
+                    sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None):
+    """Attention of each sequence's chunk over its group's table blocks, K/V read in place.
+
+    q [Tq][Hq][d]; k_pages / v_pages [n_pages][Hkv][64][d] (or any strided view with d
+    contiguous); page_map int32 [B][stride]; tables int32 [B][Hkv][cap]; counts int32 [B][Hkv];
+    cu_q int32 [B+1]; prefix_len int32 [B]; max_chunk_len host int.  Returns (o, lse-or-None).
+    """
+    if q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q, k_pages and v_pages must share dtype float32 or bfloat16")
+    if q.dim() != 3 or not q.is_contiguous():
+        raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
+    Tq, Hq, d = q.shape
+    if k_pages.dim() != 4 or k_pages.shape[2] != BLOCK or k_pages.shape[3] != d:
+        raise ValueError("k_pages must be [n_pages][Hkv][64][d]")
+    if v_pages.shape != k_pages.shape or v_pages.stride() != k_pages.stride():
+        raise ValueError("v_pages must match k_pages in shape and strides")
+    if k_pages.stride(3) != 1:
+        raise ValueError("the head dimension of the pages must be contiguous")
+    n_pages, Hkv = k_pages.shape[0], k_pages.shape[1]
+    _dev_i32(page_map, "page_map")
+    _dev_i32(tables, "tables")
+    _dev_i32(counts, "counts")
+    _dev_i32(cu_q, "cu_q")
+    _dev_i32(prefix_len, "prefix_len")
+    B = prefix_len.numel()
+    if cu_q.numel() != B + 1 or counts.numel() != B * Hkv or page_map.dim() != 2 or page_map.shape[0] != B:
+        raise ValueError("inconsistent B across cu_q / prefix_len / counts / page_map")
+    cap = tables.shape[-1] if tables.numel() else 0
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
+    st = load().cpa_chunked_prefill(
+        _ptr(q), _DTYPES[q.dtype], _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1),
+        k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
+        _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
+        _ptr(lse), _stream(stream))
+    if st != 0:
+        raise CpaError(st, "cpa_chunked_prefill")
+    return out, lse
+
+
+def status_string(code: int) -> str:
+    return load().cpa_status_string(int(code)).decode()
+
+
+def version() -> int:
+    return load().cpa_version()
+
+
+def attention_flops(tables, counts, prefix_len, chunk_len, Hq, Hkv, d):
+    """Selected-block attention FLOPs, 4*d per causally visible (query, key) pair summed over
+    every query head, from host copies (numpy) of the tables.  Only pairs with key position
+    <= query position count (a diagonal block contributes 64*65/2 pairs per query block)."""
+    import numpy as np
+    G = Hq // Hkv
+    total = 0
+    for b in range(len(prefix_len)):
+        P, C = int(prefix_len[b]), int(chunk_len[b])
+        r = np.arange(C, dtype=np.int64)
+        for g in range(Hkv):
+            ids = np.asarray(tables[b, g, :counts[b, g]], dtype=np.int64)
+            full = ids[ids * BLOCK + BLOCK - 1 <= P]          # blocks wholly before the chunk
+            pairs = int(full.size) * BLOCK * C
+            for kb in ids[ids * BLOCK + BLOCK - 1 > P]:
+                pairs += int(np.clip(P + r - kb * BLOCK + 1, 0, BLOCK).sum())
+            total += pairs * G
+    return 4 * d * total

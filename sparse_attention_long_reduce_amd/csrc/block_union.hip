@@ -1,0 +1,186 @@
+// Block-Union KV Selection: per-head 2D block masks -> per-KV-group block tables.
+//
+// "CompactAttention: Accelerating Chunked Prefill with Block-Union KV Selection", abstract:
+// the masks are KV-selection signals; a union over the chunk's query blocks and over the
+// query heads of one GQA group yields the minimal per-group KV block table that keeps every
+// selected block.  The table holds logical KV-block ids in ascending order.
+//
+// One workgroup of 256 threads per (sequence, KV group).
+//   phase 1  OR-reduce the group's G * nqb mask rows, 16 KV blocks (one 16-byte load) per
+//            thread and row, with the causal clip kb <= prefix_blocks + qi applied per row;
+//            partial ORs of threads that share a column meet in LDS; each 16-block column
+//            becomes 16 bits of a 64-bit word in LDS.
+//   phase 2  popcount per word, exclusive scan over words in LDS, then each wave expands
+//            words: lane l of the wave owning word w writes 64w + l at (word offset +
+//            mbcnt rank) when bit l is set.  Positions count .. table_cap-1 get -1.
+// The result is unique (a set in ascending order), so the kernel is bit-exact by construction.
+#include "cpa_internal.h"
+
+namespace cpa {
+namespace {
+
+constexpr int UT = 256;               // threads per workgroup
+constexpr int MAX_WORDS = 65536 / 64;  // 64-bit words for the largest supported KV extent
+
+// 0x80 in every byte of x that is nonzero
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+  return (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+}
+
+// 16 mask bytes -> 16 bits (bit j set iff byte j nonzero)
+__device__ __forceinline__ uint32_t bytes_to_bits(const uint32_t v[4]) {
+  uint32_t bits = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t t = nonzero_bytes(v[w]);
+    bits |= ((t >> 7) & 1u) << (4 * w + 0);
+    bits |= ((t >> 15) & 1u) << (4 * w + 1);
+    bits |= ((t >> 23) & 1u) << (4 * w + 2);
+    bits |= ((t >> 31) & 1u) << (4 * w + 3);
+  }
+  return bits;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
+  __shared__ unsigned long long words[MAX_WORDS];
+  __shared__ uint4 red[UT];
+  __shared__ int wpre[MAX_WORDS];
+  __shared__ int tsum[UT];
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / a.Hkv;
+  const int g = blockIdx.x % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+
+  // clamp device-side lengths so that every access stays inside the buffers
+  int qb0 = a.prefix_blocks[b];
+  int nqb = a.chunk_blocks[b];
+  qb0 = min(max(qb0, 0), a.nkvb_max);
+  nqb = min(max(nqb, 0), a.nqb_max);
+  nqb = min(nqb, a.nkvb_max - qb0);
+  const int nkvb = qb0 + nqb;
+  const int nwords = (nkvb + 63) >> 6;
+
+  for (int w = tid; w < nwords; w += UT) words[w] = 0ull;
+  __syncthreads();
+
+  // ---- phase 1: OR over (head in group, query block), causal clip per row -----------------
+  const int nchunk = (nkvb + 15) >> 4;
+  int lg = 0;
+  while ((1 << lg) < nchunk && (1 << lg) < UT) ++lg;
+  const int cols = 1 << lg;
+  const int rsplit = UT >> lg;
+  const size_t row_stride = (size_t)a.nkvb_max;
+  const uint8_t* gbase = a.masks + ((size_t)b * a.Hq + (size_t)g * G) * a.nqb_max * row_stride;
+
+  for (int c0 = 0; c0 < nchunk; c0 += cols) {
+    const int c = c0 + (tid & (cols - 1));
+    const int s = tid >> lg;
+    uint32_t acc[4] = {0u, 0u, 0u, 0u};
+    if (c < nchunk) {
+      const int kb0 = c << 4;
+      const int qi_lo = max(0, kb0 - qb0);  // first query block that can reach column kb0
+      const int nq = nqb - qi_lo;
+      for (int t = s; t < G * nq; t += rsplit) {
+        const int hh = t / nq;
+        const int qi = qi_lo + (t - hh * nq);
+        const uint8_t* rowp = gbase + ((size_t)hh * a.nqb_max + qi) * row_stride + kb0;
+        uint32_t v[4];
+        if (VEC) {
+          const uint4 x = *reinterpret_cast<const uint4*>(rowp);
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+          const int lim = min(16, a.nkvb_max - kb0);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int j = 4 * w + k;
+              if (j < lim) word |= (uint32_t)rowp[j] << (8 * k);
+            }
+            v[w] = word;
+          }
+        }
+        const int nallow = qb0 + qi - kb0 + 1;  // bytes 0 .. nallow-1 are causally reachable
+        if (nallow < 16) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int keep = min(max(nallow - 4 * w, 0), 4);
+            const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : ((1u << (8 * keep)) - 1u);
+            v[w] &= m;
+          }
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[w] |= v[w];
+      }
+    }
+    red[tid] = make_uint4(acc[0], acc[1], acc[2], acc[3]);
+    __syncthreads();
+    if (s == 0 && c < nchunk) {
+      for (int k = 1; k < rsplit; ++k) {
+        const uint4 o = red[tid + (k << lg)];
+        acc[0] |= o.x; acc[1] |= o.y; acc[2] |= o.z; acc[3] |= o.w;
+      }
+      const uint32_t bits = bytes_to_bits(acc);
+      reinterpret_cast<unsigned short*>(words)[c] = (unsigned short)bits;  // little endian
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 2: popcount, exclusive scan over words, expansion ----------------------------
+  constexpr int WPT = MAX_WORDS / UT;  // words per thread in the scan
+  int pc[WPT];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int w = tid * WPT + k;
+    pc[k] = (w < nwords) ? __popcll(words[w]) : 0;
+    mine += pc[k];
+  }
+  tsum[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < UT; off <<= 1) {  // inclusive Hillis-Steele scan of per-thread sums
+    const int add = (tid >= off) ? tsum[tid - off] : 0;
+    __syncthreads();
+    tsum[tid] += add;
+    __syncthreads();
+  }
+  int run = tsum[tid] - mine;
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int w = tid * WPT + k;
+    if (w < nwords) wpre[w] = run;
+    run += pc[k];
+  }
+  const int total = tsum[UT - 1];
+  __syncthreads();
+
+  int32_t* tab = a.tables + ((size_t)b * a.Hkv + g) * a.table_cap;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int w = wave; w < nwords; w += UT / 64) {
+    const unsigned long long word = words[w];
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0u));
+    if ((word >> lane) & 1ull) tab[wpre[w] + (int)rank] = (w << 6) + lane;
+  }
+  for (int i = total + tid; i < a.table_cap; i += UT) tab[i] = -1;
+  if (tid == 0) a.counts[(size_t)b * a.Hkv + g] = total;
+}
+
+}  // namespace
+
+hipError_t launch_block_union(const UnionArgs& a, hipStream_t s) {
+  if (a.B == 0 || a.Hkv == 0) return hipSuccess;
+  const bool vec = (a.nkvb_max % 16 == 0) && ((uintptr_t)a.masks % 16 == 0);
+  dim3 grid((unsigned)(a.B * a.Hkv)), block(UT);
+  if (vec)
+    hipLaunchKernelGGL(block_union_kernel<true>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(block_union_kernel<false>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace cpa

@@ -1,0 +1,95 @@
+// C ABI: host-side argument checks, work decomposition and launches (see include/cpa.h).
+#include "../../include/cpa.h"
+#include "cpa_internal.h"
+
+#include <cmath>
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* cpa_status_string(cpa_status s) {
+  switch (s) {
+    case CPA_OK: return "ok";
+    case CPA_ERR_NULL: return "a required pointer is NULL";
+    case CPA_ERR_SHAPE: return "invalid or inconsistent size";
+    case CPA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case CPA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or group size";
+    case CPA_ERR_CAPACITY: return "table capacity smaller than the KV-block count";
+    case CPA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int cpa_version(void) { return 10000; }
+
+cpa_status cpa_build_block_tables(const uint8_t* masks, int B, int Hq, int Hkv, int nqb_max,
+                                  int nkvb_max, const int32_t* prefix_blocks,
+                                  const int32_t* chunk_blocks, int32_t* tables, int table_cap,
+                                  int32_t* counts, hipStream_t stream) {
+  if (B < 0 || Hq < 0 || Hkv <= 0 || nqb_max < 0 || nkvb_max < 0 || table_cap < 0) return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
+  if (table_cap < nkvb_max) return CPA_ERR_CAPACITY;
+  if (B == 0) return CPA_OK;
+  if (!prefix_blocks || !chunk_blocks || !counts) return CPA_ERR_NULL;
+  if (table_cap > 0 && !tables) return CPA_ERR_NULL;
+  if (Hq > 0 && nqb_max > 0 && nkvb_max > 0 && !masks) return CPA_ERR_NULL;
+  cpa::UnionArgs a{masks, B, Hq, Hkv, nqb_max, nkvb_max, prefix_blocks, chunk_blocks, tables, table_cap, counts};
+  return cpa::launch_block_union(a, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
+                               const void* v_pages, int64_t page_stride, int64_t head_stride,
+                               int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                               int page_map_stride, const int32_t* tables, int table_cap,
+                               const int32_t* counts, const int32_t* cu_q,
+                               const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                               int max_chunk_len, float sm_scale, void* o, float* lse,
+                               hipStream_t stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || table_cap < 0 || n_pages < 0)
+    return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (!(sm_scale >= 0.f) || std::isinf(sm_scale)) return CPA_ERR_SHAPE;
+  if (dtype != CPA_F32 && dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (!(G == 1 || G == 2 || G == 4 || (G % 4 == 0 && G <= 32))) return CPA_ERR_UNSUPPORTED;
+  if (B == 0 || max_chunk_len == 0) return CPA_OK;
+  if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
+    return CPA_ERR_SHAPE;
+  if (!q || !k_pages || !v_pages || !page_map || !counts || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
+  if (table_cap > 0 && !tables) return CPA_ERR_NULL;
+  const int eb = dtype == CPA_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return CPA_ERR_ALIGN;
+  if ((token_stride * eb) % 16 || (head_stride * eb) % 16 || (page_stride * eb) % 16) return CPA_ERR_ALIGN;
+
+  cpa::PrefillArgs a{};
+  a.q = q; a.k = k_pages; a.v = v_pages;
+  a.page_stride = page_stride; a.head_stride = head_stride; a.token_stride = token_stride;
+  a.n_pages = n_pages;
+  a.page_map = page_map; a.page_map_stride = page_map_stride;
+  a.tables = tables; a.table_cap = table_cap; a.counts = counts;
+  a.cu_q = cu_q; a.prefix_len = prefix_len;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_chunk_len = max_chunk_len;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt((float)d);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o = o; a.lse = lse;
+  a.G = G;
+  a.hpw = G >= 4 ? 4 : G;
+  a.qpw = 4 / a.hpw;
+  a.hsplit = G / a.hpw;
+  const int nqb_max = (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK;
+  a.n_qtiles = (nqb_max + a.qpw - 1) / a.qpw;
+  a.tiles_per_group = a.n_qtiles * a.hsplit;
+  a.n_groups = B * Hkv;
+  a.xcd_remap = a.n_groups >= 8 ? 1 : 0;
+  return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal launch interface shared by the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpa {
+
+struct UnionArgs {
+  const uint8_t* masks;
+  int B, Hq, Hkv, nqb_max, nkvb_max;
+  const int32_t* prefix_blocks;
+  const int32_t* chunk_blocks;
+  int32_t* tables;
+  int table_cap;
+  int32_t* counts;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t page_stride, head_stride, token_stride, n_pages;  // elements / pages
+  const int32_t* page_map;
+  int page_map_stride;
+  const int32_t* tables;
+  int table_cap;
+  const int32_t* counts;
+  const int32_t* cu_q;
+  const int32_t* prefix_len;
+  int B, Hq, Hkv, max_chunk_len;
+  float scale_log2;  // softmax scale * log2(e)
+  void* o;
+  float* lse;
+  // work decomposition (filled by the launcher)
+  int G;                // query heads per KV group
+  int hpw;              // query heads per workgroup (one wave each, per query block)
+  int qpw;              // query blocks per workgroup
+  int hsplit;           // workgroups per (group, query-block tile) along the heads: G / hpw
+  int n_qtiles;         // query-block tiles per group: ceil(max query blocks / qpw)
+  int tiles_per_group;  // n_qtiles * hsplit
+  int n_groups;         // B * Hkv
+  int xcd_remap;        // 1: keep each KV group's tiles on one XCD (see the prefill kernel)
+};
+
+// Both return hipSuccess or the launch error; they never synchronise.
+hipError_t launch_block_union(const UnionArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
+
+}  // namespace cpa

@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every symbol include/cpa.h declares, and rejects invalid
+arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_long_reduce_amd as cpa
+from sparse_attention_long_reduce_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cpa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libcpa.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"cpa_build_block_tables", "cpa_chunked_prefill", "cpa_status_string", "cpa_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_lib.EXPORTS) == set(names)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.cpa_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.cpa_status_string(99).decode() == "unknown status"
+    assert lib.cpa_version() == 10000
+
+
+NULL = None
+FAKE = 0x1000  # never dereferenced: every call below fails validation before touching memory
+
+
+def bt(lib, masks=FAKE, B=1, Hq=8, Hkv=2, nqb=4, nkvb=16, pb=FAKE, cb=FAKE, tab=FAKE, cap=16, cnt=FAKE):
+    return lib.cpa_build_block_tables(masks, B, Hq, Hkv, nqb, nkvb, pb, cb, tab, cap, cnt, None)
+
+
+def test_build_tables_validation(lib):
+    assert bt(lib, Hkv=0) == 2
+    assert bt(lib, Hq=6, Hkv=4) == 2
+    assert bt(lib, B=-1) == 2
+    assert bt(lib, nkvb=65537, cap=70000) == 2
+    assert bt(lib, cap=15) == 5
+    assert bt(lib, pb=NULL) == 1
+    assert bt(lib, cnt=NULL) == 1
+    assert bt(lib, masks=NULL) == 1
+    assert bt(lib, tab=NULL) == 1
+    assert bt(lib, B=0, masks=NULL, pb=NULL, cb=NULL, tab=NULL, cnt=NULL) == 0
+
+
+def pf(lib, q=FAKE, dtype=1, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE,
+       pms=16, tab=FAKE, cap=16, cnt=FAKE, cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256,
+       scale=0.0, o=FAKE, lse=NULL):
+    return lib.cpa_chunked_prefill(q, dtype, k, v, ps, hs, ts, npages, pm, pms, tab, cap, cnt, cu, pl,
+                                   B, Hq, Hkv, d, mcl, scale, o, lse, None)
+
+
+def test_prefill_validation(lib):
+    assert pf(lib, d=96) == 4
+    assert pf(lib, d=256) == 4
+    assert pf(lib, dtype=7) == 4
+    assert pf(lib, Hq=24, Hkv=8) == 4  # G = 3
+    assert pf(lib, Hq=30, Hkv=8) == 2
+    assert pf(lib, Hq=36, Hkv=1) == 4  # G=36 > 32
+    assert pf(lib, scale=-1.0) == 2
+    assert pf(lib, scale=float("nan")) == 2
+    assert pf(lib, scale=float("inf")) == 2
+    assert pf(lib, ts=64) == 2
+    assert pf(lib, hs=63 * 128) == 2
+    assert pf(lib, ps=7 * 64 * 128) == 2
+    assert pf(lib, pms=0) == 2
+    assert pf(lib, q=NULL) == 1
+    assert pf(lib, o=NULL) == 1
+    assert pf(lib, pm=NULL) == 1
+    assert pf(lib, tab=NULL) == 1
+    assert pf(lib, q=FAKE + 8) == 3
+    assert pf(lib, k=FAKE + 2) == 3
+    assert pf(lib, ts=132, hs=64 * 132, ps=8 * 64 * 132) == 3    # bf16 row of 264 B
+    assert pf(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
+    assert pf(lib, mcl=0, q=NULL) == 0
+
+
+def test_python_layer_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        cpa.build_block_tables(torch.zeros((1, 8, 4, 16), dtype=torch.uint8),
+                               torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 2)
+
+
+def test_attention_flops_matches_oracle_visible_counts():
+    import numpy as np
+    import oracle
+    from workloads import make_workload
+    from workloads.configs import mask_bernoulli
+    w = make_workload("f", [128, 320, 0], [128, 100, 64], 8, 2, 8, "f32",
+                      lambda rng, *a: mask_bernoulli(rng, *a, p=0.2, local=1), 3)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    _, _, NV = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q,
+                                      w.prefix_len, w.Hkv, return_nvis=True)
+    assert cpa.attention_flops(T, C, w.prefix_len, w.chunk_len, w.Hq, w.Hkv, w.d) == 4 * w.d * int(NV.sum())

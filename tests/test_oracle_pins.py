@@ -40,9 +40,10 @@ def small(seed, G=2, Hkv=2, d=16, prefix=(128, 320), chunk=(128, 64), p=0.15, no
 def contiguous_kv(w, b, g):
     """Logical K/V of sequence b, group g, in token order (test-side gather via the page map)."""
     L = int(w.prefix_len[b] + w.chunk_len[b])
-    phys = w.page_map[b, :L // BLOCK]
-    return (w.k_pages[phys, g].reshape(L, w.d).astype(np.float64),
-            w.v_pages[phys, g].reshape(L, w.d).astype(np.float64))
+    nb = (L + BLOCK - 1) // BLOCK
+    phys = w.page_map[b, :nb]
+    return (w.k_pages[phys, g].reshape(nb * BLOCK, w.d)[:L].astype(np.float64),
+            w.v_pages[phys, g].reshape(nb * BLOCK, w.d)[:L].astype(np.float64))
 
 
 # ------------------------------------------------------------------------------------------
@@ -165,8 +166,9 @@ def sdpa_dense(w, token_mask=None):
     return out, lse
 
 
-def test_all_ones_is_dense_causal_attention():
-    w = small(11, G=2, Hkv=2, d=32, prefix=(128, 320), chunk=(192, 64),
+@pytest.mark.parametrize("chunk", [(192, 64), (150, 37)])
+def test_all_ones_is_dense_causal_attention(chunk):
+    w = small(11, G=2, Hkv=2, d=32, prefix=(128, 320), chunk=chunk,
               fn=lambda rng, *a: mask_all(rng, *a, value=1))
     O, L = run_oracle(w)
     Od, Ld = sdpa_dense(w)
@@ -191,7 +193,7 @@ def test_union_of_qblock_constant_group_shared_masks_is_block_sparse_attention()
         blk = np.zeros((Cn, P + Cn), dtype=bool)
         for r in range(Cn):
             qi = r // BLOCK
-            sel = np.nonzero(w.masks[b, h, qi, :(P + Cn) // BLOCK])[0]
+            sel = np.nonzero(w.masks[b, h, qi, :(P + Cn + BLOCK - 1) // BLOCK])[0]
             for kb in sel:
                 blk[r, kb * BLOCK:(kb + 1) * BLOCK] = True
         return blk
@@ -228,8 +230,9 @@ def brute_force(w, T, C):
     return O
 
 
-def test_brute_force_tiny():
-    w = small(13, G=2, Hkv=2, d=4, prefix=(128, 64), chunk=(64, 128), p=0.2)
+@pytest.mark.parametrize("chunk", [(64, 128), (23, 100)])
+def test_brute_force_tiny(chunk):
+    w = small(13, G=2, Hkv=2, d=4, prefix=(128, 64), chunk=chunk, p=0.2)
     T, C = tables_of(w)
     O, _ = run_oracle(w, T, C)
     Ob = brute_force(w, T, C)

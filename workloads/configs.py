@@ -43,7 +43,7 @@ class Workload:
     d: int
     dtype: str                 # "f32" or "bf16"
     prefix_len: np.ndarray     # int32 [B], tokens, multiple of 64
-    chunk_len: np.ndarray      # int32 [B], tokens, multiple of 64
+    chunk_len: np.ndarray      # int32 [B], tokens (need not be a multiple of 64)
     q: np.ndarray              # float32 [Tq][Hq][d]
     k_pages: np.ndarray        # float32 [n_pages][Hkv][64][d]
     v_pages: np.ndarray        # float32 [n_pages][Hkv][64][d]
@@ -70,7 +70,7 @@ class Workload:
 
     @property
     def chunk_blocks(self) -> np.ndarray:
-        return (self.chunk_len // BLOCK).astype(np.int32)
+        return ((self.chunk_len + BLOCK - 1) // BLOCK).astype(np.int32)
 
     @property
     def nqb_max(self) -> int:
@@ -92,7 +92,7 @@ class Workload:
         """Boolean [n_pages]: pages some logical block of some sequence maps to."""
         used = np.zeros(self.n_pages, dtype=bool)
         for b in range(self.B):
-            nk = int((self.prefix_len[b] + self.chunk_len[b]) // BLOCK)
+            nk = int((self.prefix_len[b] + self.chunk_len[b] + BLOCK - 1) // BLOCK)
             used[self.page_map[b, :nk]] = True
         return used
 
@@ -177,13 +177,13 @@ def make_workload(name, prefix_len, chunk_len, Hq, Hkv, d, dtype, mask_fn, seed,
     """
     prefix_len = np.asarray(prefix_len, dtype=np.int32)
     chunk_len = np.asarray(chunk_len, dtype=np.int32)
-    if np.any(prefix_len % BLOCK) or np.any(chunk_len % BLOCK):
-        raise ValueError("prefix and chunk lengths must be multiples of 64")
+    if np.any(prefix_len % BLOCK) or np.any(prefix_len < 0) or np.any(chunk_len < 0):
+        raise ValueError("prefix lengths must be non-negative multiples of 64")
     B = prefix_len.shape[0]
     ss = np.random.SeedSequence(seed)
     rq, rk, rv, rm, rp = [np.random.default_rng(s) for s in ss.spawn(5)]
     qb0 = prefix_len // BLOCK
-    nqb = chunk_len // BLOCK
+    nqb = (chunk_len + BLOCK - 1) // BLOCK   # a ragged chunk ends in a partial query block
     nkvb = qb0 + nqb
     nqb_max = int(nqb.max()) if B else 0
     nkvb_max = int(nkvb.max()) if B else 0
