@@ -44,7 +44,7 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("prefill.hip", "cpa_internal.h"):
+    for f in ("prefill_bf16.hip", "prefill_common.h", "cpa_internal.h"):
         with open(os.path.join(ROOT, "sparse_attention_long_reduce_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

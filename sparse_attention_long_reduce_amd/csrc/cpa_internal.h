@@ -45,5 +45,8 @@ struct PrefillArgs {
 // Both return hipSuccess or the launch error; they never synchronise.
 hipError_t launch_block_union(const UnionArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
+// register-staged variant (V transposed through registers); serves fp32 and is kept for bf16
+// as the reference point of the direct-to-LDS bf16 kernel
+hipError_t launch_prefill_regstaged(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
 
 }  // namespace cpa

@@ -1,0 +1,62 @@
+// Device helpers shared by the prefill kernels.
+#pragma once
+#include "cpa_internal.h"
+#include <climits>
+
+namespace cpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+// log2 headroom before the output accumulators must be rescaled to a new row maximum
+constexpr float kRescaleThreshold = 8.0f;
+
+// max / sum of x over lanes l and l^32 (the two lanes that share a query row)
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Number of the last `nqb` table entries (the only ones that can lie past a query block of the
+// chunk when the table is ascending) whose id exceeds `lim`; wave-uniform.
+__device__ __forceinline__ int count_above(const int32_t* tab, int cnt, int nqb, int lim, int lane) {
+  int c = 0;
+  for (int base = max(0, cnt - nqb); base < cnt; base += 64) {
+    const int i = base + lane;
+    const int v = (i < cnt) ? tab[i] : INT_MIN;
+    c += __popcll(__builtin_amdgcn_ballot_w64(v > lim));
+  }
+  return c;
+}
+
+// Workgroup -> (KV group index gi = b*Hkv + g, tile rank).  Workgroups are dispatched
+// round-robin over the 8 XCDs (blockIdx % 8); with xcd_remap every tile of one KV group lands on
+// the same XCD so that the group's pages are shared through that XCD's L2, and tiles of rank 0
+// (the last query blocks, which see the most pages) start first.  Returns false for padding.
+__device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int& gi, int& rank) {
+  if (a.xcd_remap) {
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int ngx = (a.n_groups - xcd + 7) >> 3;  // groups gi with gi % 8 == xcd
+    if (slot >= ngx * a.tiles_per_group) return false;
+    gi = xcd + 8 * (slot % ngx);
+    rank = slot / ngx;
+  } else {
+    if ((int)blockIdx.x >= a.n_groups * a.tiles_per_group) return false;
+    gi = blockIdx.x % a.n_groups;
+    rank = blockIdx.x / a.n_groups;
+  }
+  return true;
+}
+
+inline int prefill_grid(const PrefillArgs& a) {
+  return a.xcd_remap ? 8 * ((a.n_groups + 7) / 8) * a.tiles_per_group : a.n_groups * a.tiles_per_group;
+}
+
+}  // namespace cpa
