@@ -11,7 +11,7 @@
 // group's four heads on one query block; G = 2 (1) packs 2 (4) query blocks; G > 4 splits the
 // heads over G/4 workgroups.  Every selected KV page is brought into LDS once per workgroup
 // and read by all eight waves, i.e. by every head and row of the tile.  Two waves share each
-// SIMD, so one wave's MFMAs overlap the other's softmax.
+// SIMD, so one wave's MFMAs can overlap the other's softmax.
 //
 // Page staging.  Each page (64 tokens x d, K and V) is copied HBM -> LDS by the gfx950
 // direct-to-LDS loads (global_load_lds_dwordx4): every instruction moves 64 16-byte chunks,
@@ -22,10 +22,11 @@
 //   V: natural [token][d] rows with chunk c at c ^ swz_v(r); the PV operand (8 consecutive
 //      keys of one column per lane) is produced by two ds_read_b64_tr_b16 transposed reads,
 //      which the swizzle keeps free of bank conflicts.
-// No staging registers and no LDS stores are needed.  Pages are double-buffered in two pairs of
-// statically distinct LDS arrays (the loop is unrolled by two), so the compiler can tell the
-// buffer being read from the one being filled and never waits for the prefetch early.  The
-// page ids of the table are resolved a window at a time into LDS.
+// No staging registers and no LDS stores are needed.  Pages are processed two per barrier and
+// double-buffered in statically distinct LDS arrays (the loop is unrolled over the two buffer
+// sets), so the compiler can tell the tiles being read from the ones being filled and never
+// waits for the prefetch early.  The page ids of the table are resolved a window at a time
+// into LDS.
 //
 // Per page (64 keys) and wave (32 query rows), in the transposed domain so that each lane owns
 // whole query rows:
@@ -34,6 +35,10 @@
 //   online softmax in fp32, log2 domain, softmax scale folded into one FMA; a row's 64 scores
 //   live in lanes l and l^32 (one permlane32 swap per row maximum).  The output is rescaled
 //   only when a row maximum grows by more than 2^8 over the reference it was accumulated with.
+//   The row sum adds the bf16-rounded weights that enter the PV product (v_dot2_f32_bf16 with
+//   ones, two weights per instruction), so the result is normalised by exactly the weights used.
+//   This file is compiled without NaN semantics so that maxima need no operand quieting; NaN
+//   inputs still propagate through the exponentials and the MFMAs to the output.
 //   O^T[dv][row] += V^T . P^T   A = V^T by transposed LDS reads, B = P^T rounded to bf16
 //                               straight from the score accumulators
 #include "prefill_common.h"
@@ -45,6 +50,7 @@ constexpr int THREADS = 512;
 constexpr int WIN = 1024;  // page ids resolved per window
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D>
@@ -75,10 +81,14 @@ __device__ __forceinline__ v4i16 ds_read_tr(const __bf16* p) {
 template <int D>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
   using GE = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 k0s[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 v0s[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 k1s[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 v1s[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kA0[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vA0[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kA1[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vA1[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kB0[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vB0[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kB1[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vB1[GE::PAGE];
   __shared__ int win_kb[WIN];
   __shared__ int win_ph[WIN];
 
@@ -148,33 +158,37 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   }
   const int dma_dst = (wave & 3) * GE::NPW * 64 * 8;  // elements; + j * 512
 
-  auto issue = [&](int kb, int ph, __bf16* ks, __bf16* vs) {
+  // A page fill is planned once and then issued one direct-to-LDS instruction at a time in
+  // between the MFMAs of the QK product, so that the vector-memory queue drains while the matrix
+  // core works instead of stalling the issuing wave.  Pages that are unresolved (NaN) or end
+  // inside the sequence (rows past the end read as 0) are filled at once through registers.
+  struct Fill {
+    bool on;             // direct-to-LDS instructions still to issue
+    const __bf16* src;   // this wave's tensor (K or V) of the page
+    __bf16* dst;         // this wave's part of the destination tile
+  };
+  auto plan = [&](int kb, int ph, __bf16* ks, __bf16* vs) __attribute__((always_inline)) {
     const int nv_tok = min(max(L - 64 * kb, 0), 64);
     const __bf16* src = (vrole ? vg : kg) + (size_t)(ph < 0 ? 0 : ph) * a.page_stride;
-    if (ph >= 0 && nv_tok == 64) {
-      if (vrole) {
-#pragma unroll
-        for (int j = 0; j < GE::NPW; ++j)
-          lds_dma16(src + dma_off[j], vs + dma_dst + j * 512);
-      } else {
-#pragma unroll
-        for (int j = 0; j < GE::NPW; ++j)
-          lds_dma16(src + dma_off[j], ks + dma_dst + j * 512);
-      }
-    } else {
-      // unresolved page -> NaN; rows at or past the sequence end -> 0 (through registers)
-      const uint32_t f = ph < 0 ? 0x7FC07FC0u : 0u;
-      __bf16* dst = vrole ? vs : ks;
+    __bf16* dst = (vrole ? vs : ks) + dma_dst;
+    Fill f{ph >= 0 && nv_tok == 64, src, dst};
+    if (!f.on) {
+      const uint32_t fv = ph < 0 ? 0x7FC07FC0u : 0u;
 #pragma unroll
       for (int j = 0; j < GE::NPW; ++j) {
-        uint4 v = make_uint4(f, f, f, f);
+        uint4 v = make_uint4(fv, fv, fv, fv);
         if (ph >= 0 && dma_row[j] < nv_tok) v = *reinterpret_cast<const uint4*>(src + dma_off[j]);
-        *reinterpret_cast<uint4*>(dst + dma_dst + j * 512 + lane * 8) = v;
+        *reinterpret_cast<uint4*>(dst + j * 512 + lane * 8) = v;
       }
     }
+    return f;
   };
+  auto fill_one = [&](const Fill& f, int j) __attribute__((always_inline)) {
+    if (f.on) lds_dma16(f.src + dma_off[j], f.dst + j * 512);
+  };
+  const Fill no_fill{false, nullptr, nullptr};
 
-  auto load_window = [&](int base) {
+  auto load_window = [&](int base) __attribute__((always_inline)) {
     for (int j = tid; j < WIN && base + j < n_iter; j += THREADS) {
       const int kb = tab[base + j];
       int ph = -1;
@@ -205,6 +219,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 
   // ---- running softmax state and output accumulators ------------------------------------
   const float cs = a.scale_log2;
+  const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
   float m_run = -INFINITY;   // reference maximum (log2 domain) the accumulators are scaled to
   float l_run = 0.f;         // this lane's share of the row sum
   f32x16 o[GE::DT];
@@ -215,8 +230,10 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int row_pos = P + row;
   const int wave_pos0 = P + row0;
 
-  auto compute = [&](const __bf16* Kl, const __bf16* Vl, int kb) {
-    f32x16 s0, s1;  // S^T for keys 0-31 and 32-63 of the page
+  f32x16 s0, s1;  // S^T of the page in flight, keys 0-31 and 32-63
+
+  // S^T = K Q^T for the page in LDS tile Kl, issuing the fill f along the way
+  auto qk = [&](const __bf16* Kl, const Fill& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) { s0[j] = 0.f; s1[j] = 0.f; }
 #pragma unroll
@@ -226,8 +243,16 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(Kl + off + 32 * D);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb[ks], s1, 0, 0, 0);
+      if (ks % ((D / 16) / GE::NPW) == 0) fill_one(f, ks / ((D / 16) / GE::NPW));
     }
+  };
+  auto fill_all = [&](const Fill& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < GE::NPW; ++j) fill_one(f, j);
+  };
 
+  // causal cut, online softmax and O^T += V^T P^T for page kb (scores in s0/s1, V tile Vl)
+  auto softmax_pv = [&](const __bf16* Vl, int kb) __attribute__((always_inline)) {
     // causal cut: key position 64*kb + key index must not exceed the row position
     if (64 * kb + 63 > wave_pos0) {
 #pragma unroll
@@ -239,9 +264,9 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     }
 
     // online softmax (log2 domain), lazy rescale
-    float mx = -INFINITY;
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
     mx = xhalf_max(mx) * cs;
     const bool need = mx > m_run + kRescaleThreshold;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -255,14 +280,11 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       m_run = m_new;
     }
     const float ref = (m_run == -INFINITY) ? 0.f : m_run;
-    float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       s0[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], cs, -ref));
       s1[j] = __builtin_amdgcn_exp2f(fmaf(s1[j], cs, -ref));
-      sum += s0[j] + s1[j];
     }
-    l_run += sum;
 
     // O^T += V^T P^T; keys of step (kt, u) for lane half hl, element e:
     //   32*kt + 16*u + 8*(e / 4) + 4*hl + e % 4
@@ -273,6 +295,12 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
         bf16x8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[e] = (__bf16)(kt == 0 ? s0[8 * u + e] : s1[8 * u + e]);
+        // the row sum accumulates the same bf16 weights the PV product uses, two per dot2
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pp = {pb[e], pb[e + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, l_run, false);
+        }
         const int krow = (32 * kt + 16 * u) * D;
 #pragma unroll
         for (int dt = 0; dt < GE::DT; ++dt) {
@@ -286,34 +314,63 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     }
   };
 
-  // ---- main loop (unrolled by two over the two static LDS buffers) ----------------------------
+  // ---- main loop ---------------------------------------------------------------------------
+  // Pages go two per iteration.  Tile set A holds pages 2j and 2j+1 while set B receives pages
+  // 2j+2 and 2j+3 (and the other way round on the next iteration); the loop is unrolled over
+  // the two sets so that every LDS read names its tile and the compiler never has to wait for an
+  // unrelated prefetch.  The page ids an iteration prefetches were read from the window one
+  // iteration earlier, so no LDS latency sits in front of the prefetch.  One barrier per two
+  // pages.
   if (n_iter > 0) {
     load_window(0);
     __syncthreads();
-    int kb_cur = win_kb[0];
-    issue(kb_cur, win_ph[0], k0s, v0s);
+    int kb0 = win_kb[0], ph0 = win_ph[0];
+    int kb1 = n_iter > 1 ? win_kb[1] : 0, ph1 = n_iter > 1 ? win_ph[1] : 0;
+    fill_all(plan(kb0, ph0, kA0, vA0));
+    if (n_iter > 1) fill_all(plan(kb1, ph1, kA1, vA1));
+    // ids of the next pair
+    int kb2 = n_iter > 2 ? win_kb[2] : 0, ph2 = n_iter > 2 ? win_ph[2] : 0;
+    int kb3 = n_iter > 3 ? win_kb[3] : 0, ph3 = n_iter > 3 ? win_ph[3] : 0;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS fills have landed
     __syncthreads();
 
-    auto step = [&](int i, const __bf16* ck, const __bf16* cv, __bf16* nk, __bf16* nv) {
-      const bool has_next = i + 1 < n_iter;
-      int kb_nx = 0;
-      if (has_next) {
-        if ((i + 1) % WIN == 0) {
-          load_window(i + 1);
+    // pages p and p+1 sit in (ck0, cv0) and (ck1, cv1); pages p+2, p+3 go to (nk0, nv0), (nk1, nv1)
+    auto pair = [&](int p, const __bf16* ck0, const __bf16* cv0, const __bf16* ck1, const __bf16* cv1,
+                    __bf16* nk0, __bf16* nv0, __bf16* nk1, __bf16* nv1) __attribute__((always_inline)) {
+      const Fill f0 = p + 2 < n_iter ? plan(kb2, ph2, nk0, nv0) : no_fill;
+      const Fill f1 = p + 3 < n_iter ? plan(kb3, ph3, nk1, nv1) : no_fill;
+      const int kc0 = kb0, kc1 = kb1;
+      kb0 = kb2; kb1 = kb3;
+      if (p + 4 < n_iter) {
+        if ((p + 4) % WIN == 0) {
+          load_window(p + 4);
           __syncthreads();
         }
-        kb_nx = win_kb[(i + 1) % WIN];
-        issue(kb_nx, win_ph[(i + 1) % WIN], nk, nv);
+        kb2 = win_kb[(p + 4) % WIN];
+        ph2 = win_ph[(p + 4) % WIN];
+        if (p + 5 < n_iter) {
+          kb3 = win_kb[(p + 5) % WIN];
+          ph3 = win_ph[(p + 5) % WIN];
+        }
       }
-      if (i < n_vis) compute(ck, cv, kb_cur);
+      if (p < n_vis) {
+        qk(ck0, f0);
+        softmax_pv(cv0, kc0);
+      } else {
+        fill_all(f0);
+      }
+      if (p + 1 < n_vis) {
+        qk(ck1, f1);
+        softmax_pv(cv1, kc1);
+      } else {
+        fill_all(f1);
+      }
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
-      kb_cur = kb_nx;
     };
-    for (int i = 0; i < n_iter; i += 2) {
-      step(i, k0s, v0s, k1s, v1s);
-      if (i + 1 < n_iter) step(i + 1, k1s, v1s, k0s, v0s);
+    for (int p = 0; p < n_iter; p += 4) {
+      pair(p, kA0, vA0, kA1, vA1, kB0, vB0, kB1, vB1);
+      if (p + 2 < n_iter) pair(p + 2, kB0, vB0, kB1, vB1, kA0, vA0, kA1, vA1);
     }
   }
 

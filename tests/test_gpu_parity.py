@@ -79,7 +79,9 @@ def test_small_tables_and_prefill(name):
     fin = np.isfinite(Lr)
     assert np.array_equal(np.isfinite(lg), fin)
     if fin.any():
-        assert np.max(np.abs(lg[fin] - Lr[fin])) < 1e-3
+        # bf16 path: the row sum adds the bf16-rounded weights (relative rounding <= 2^-9 each)
+        tol = 2 ** -8 if w.dtype == "bf16" else 1e-4
+        assert np.max(np.abs(lg[fin] - Lr[fin])) < tol
     if name == "all_zero_bf16":
         assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
 
