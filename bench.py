@@ -1,16 +1,18 @@
 """Benchmark of the Block-Union KV Selection hot path on one MI355X.
 
-One step = the whole path over one batch: the table build (masks -> per-group tables) and the
-chunked-prefill attention over those tables, both through the C ABI.  Default workload: the last
-2048-token chunk of a 131072-token sequence (prefix 129024), LLaMA-3.1-8B attention-layer shape
-(32 query heads, 8 KV heads, head dim 128), bf16, structured per-head block masks (vertical
-stripes, slash diagonals, Bernoulli noise, sink block and a 4-block local window), K/V in a
-randomly permuted paged pool.  All inputs are seeded synthetic data resident in HBM before the
-timed region.
+One step = the whole path over one batch: the table build (masks -> per-group KV block tables)
+and the chunked-prefill attention over those tables, both through the C ABI.  Default workload:
+the last 2048-token chunk of a 131072-token sequence (prefix 129024), LLaMA-3.1-8B
+attention-layer shape (32 query heads, 8 KV heads, head dim 128), bf16, structured per-head
+block masks (vertical stripes, slash diagonals, Bernoulli noise, sink block and a 4-block local
+window), K/V in a randomly permuted paged pool.  Other workloads: --workload c2 (32K context),
+c4 (the full chunked prefill of one 131072-token sequence: 64 chunks of 2048, one step = all 64
+chunks in order), c5a / c5b (varlen batch of four sequences, last 4096-token chunks).  All
+inputs are seeded synthetic data resident in HBM before the timed region.
 
-Prints one JSON line with the selected-block attention TFLOP/s (whole step), the speedup over
-the same kernels run with all-ones masks (dense), the roofline of the dominant kernel (prefill,
-measured with HIP events on the stream it runs on) and the CPU oracle timed on a bounded sample.
+Prints one JSON line: selected-block attention TFLOP/s of the whole step, the speedup over the
+same kernels run with all-ones masks (dense), the roofline of the dominant kernel (prefill,
+timed with HIP events on the stream it runs on) and the CPU oracle timed on a bounded sample.
 """
 import argparse
 import hashlib
@@ -23,7 +25,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (no fp32 MFMA headline beyond the vector rate)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 
 WORKLOADS = {
@@ -31,8 +32,10 @@ WORKLOADS = {
            "Hq 32 / Hkv 8 / d 128, bf16, structured masks"),
     "c2": ("c2_32k_bf16", "32K context: prefix 30720 + chunk 2048, Hq 32 / Hkv 8 / d 128, bf16, "
            "Bernoulli(0.1) masks + sink + 4-block local"),
-    "c5a": ("c5a_varlen_shared", "varlen 4 x last 4096 of {8K,32K,64K,128K}, Hq 32 / Hkv 8 / d 128, "
-            "bf16, group-shared stripes 0.1"),
+    "c4": ("c4_128k_chunked", "full chunked prefill of one 131072-token sequence: 64 chunks of "
+           "2048, Hq 32 / Hkv 8 / d 128, bf16, structured masks per chunk"),
+    "c5a": ("c5a_varlen_shared", "varlen 4 x last 4096 of {8K,32K,64K,128K}, Hq 32 / Hkv 8 / "
+            "d 128, bf16, group-shared stripes 0.1"),
     "c5b": ("c5b_varlen_independent", "varlen 4 x last 4096 of {8K,32K,64K,128K}, Hq 32 / Hkv 8 / "
             "d 128, bf16, per-head stripes 0.1"),
 }
@@ -63,7 +66,7 @@ def read_traffic(workload_key):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, T, C, max_seconds=20.0):
+def cpu_baseline(w, T, C, max_seconds=15.0):
     """The fp64 oracle (tables in full + attention on a bounded row sample) on the host cores."""
     import numpy as np
     import oracle
@@ -75,31 +78,116 @@ def cpu_baseline(w, T, C, max_seconds=20.0):
     t0 = time.perf_counter()
     oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
     t_tab = time.perf_counter() - t0
-    # rows: whole query blocks of group 0's heads, last blocks first (the heaviest), until time runs out
+    # whole query blocks of one KV group's heads, longest sequence and last blocks first
     flops = 0
     t_att = 0.0
     n_rows = 0
-    rng = np.random.default_rng(0)
-    b = w.B - 1
+    b = int(np.argmax(w.prefix_len + w.chunk_len))
     C_b = int(w.chunk_len[b])
-    for qi in range((C_b + 63) // 64 - 1, -1, -1):
-        rows = np.arange(64 * qi, min(C_b, 64 * qi + 64))
-        S = np.array([(b, h, r) for h in range(w.G) for r in rows], dtype=np.int64)
-        t0 = time.perf_counter()
-        _, _, nv = oracle.attention_rows(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q,
-                                         w.prefix_len, w.Hkv, S, return_nvis=True)
-        t_att += time.perf_counter() - t0
-        flops += 4 * w.d * int(nv.sum())
-        n_rows += len(S)
-        if t_att + t_tab > max_seconds:
+    done = False
+    for g in range(w.Hkv):
+        for qi in range((C_b + 63) // 64 - 1, -1, -1):
+            rows = np.arange(64 * qi, min(C_b, 64 * qi + 64))
+            S = np.array([(b, h, r) for h in range(g * w.G, (g + 1) * w.G) for r in rows], dtype=np.int64)
+            t0 = time.perf_counter()
+            _, _, nv = oracle.attention_rows(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q,
+                                             w.prefix_len, w.Hkv, S, return_nvis=True)
+            t_att += time.perf_counter() - t0
+            flops += 4 * w.d * int(nv.sum())
+            n_rows += len(S)
+            if t_att + t_tab > max_seconds:
+                done = True
+                break
+        if done:
             break
-    del rng
     secs = t_tab + t_att
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"numpy fp64 oracle: full table build ({t_tab:.2f} s) + attention for {n_rows} "
-                      f"query rows (group 0's heads, last query blocks first) of sequence {b} "
-                      f"({t_att:.2f} s); value = selected FLOPs of those rows / wall time",
+    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"numpy fp64 oracle: table build for the whole batch ({t_tab:.2f} s) + attention for "
+                      f"{n_rows} query rows (whole query blocks of KV groups in order, last blocks first) of "
+                      f"sequence {b} ({t_att:.2f} s); value = selected FLOPs of those rows / wall time",
             "seconds": round(secs, 3)}
+
+
+class Batch:
+    """One launch pair (table build + prefill) with its inputs resident on the device."""
+
+    def __init__(self, w, dev, kp=None, vp=None):
+        import torch
+        bf = torch.bfloat16
+        self.w = w
+        self.masks = torch.from_numpy(w.masks).to(dev)
+        self.masks_dense = torch.ones_like(self.masks)   # entries outside the causal region are ignored
+        self.pb = torch.from_numpy(w.prefix_blocks).to(dev)
+        self.cb = torch.from_numpy(w.chunk_blocks).to(dev)
+        self.q = torch.from_numpy(w.q).to(dev).to(bf)
+        self.kp = torch.from_numpy(w.k_pages).to(dev).to(bf) if kp is None else kp
+        self.vp = torch.from_numpy(w.v_pages).to(dev).to(bf) if vp is None else vp
+        self.pm = torch.from_numpy(w.page_map).to(dev)
+        self.cu = torch.from_numpy(w.cu_q).to(dev)
+        self.pl = torch.from_numpy(w.prefix_len).to(dev)
+        self.tables = torch.empty((w.B, w.Hkv, w.nkvb_max), dtype=torch.int32, device=dev)
+        self.counts = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((self.q.shape[0], w.Hq), dtype=torch.float32, device=dev)
+
+    def build(self, cpa, dense):
+        cpa.build_block_tables(self.masks_dense if dense else self.masks, self.pb, self.cb, self.w.Hkv,
+                               tables=self.tables, counts=self.counts)
+
+    def prefill(self, cpa):
+        cpa.chunked_prefill(self.q, self.kp, self.vp, self.pm, self.tables, self.counts, self.cu, self.pl,
+                            self.w.max_chunk_len, out=self.out, lse=self.lse)
+
+    def flops(self, cpa):
+        w = self.w
+        return cpa.attention_flops(self.tables.cpu().numpy(), self.counts.cpu().numpy(), w.prefix_len,
+                                   w.chunk_len, w.Hq, w.Hkv, w.d)
+
+
+def make_batches(key, dev):
+    from workloads import make_config
+    from workloads.configs import chunked_sequence_chunk
+    name, _ = WORKLOADS[key]
+    if key != "c4":
+        return [Batch(make_config(name), dev)]
+    batches = []
+    kp = vp = None
+    for k in range(64):
+        w = chunked_sequence_chunk(k)
+        bt = Batch(w, dev, kp, vp)
+        kp, vp = bt.kp, bt.vp     # one paged pool shared by all chunks of the sequence
+        batches.append(bt)
+    return batches
+
+
+def timed(cpa, batches, dense, steps, warmup):
+    """Runs warmup + steps steps; HIP events around every launch on torch's current stream
+    (the stream the library launches on)."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        for bt in batches:
+            bt.build(cpa, dense)
+            bt.prefill(cpa)
+    torch.cuda.synchronize()
+    nb = len(batches)
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, bt in enumerate(batches):
+            ev[s][i][0].record()
+            bt.build(cpa, dense)
+            ev[s][i][1].record()
+            bt.prefill(cpa)
+            ev[s][i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    build = np.array([[e[0].elapsed_time(e[1]) for e in st] for st in ev])   # [steps][batches] ms
+    pre = np.array([[e[1].elapsed_time(e[2]) for e in st] for st in ev])
+    total_ms = ev[0][0][0].elapsed_time(ev[-1][-1][2])
+    return {"step_ms": total_ms / steps, "build_ms": float(build.sum(1).mean()),
+            "prefill_ms": float(pre.sum(1).mean()), "prefill_ms_median": float(np.median(pre.sum(1))),
+            "prefill_launch_ms": float(pre.mean()), "wall_s": wall, "launches_per_step": nb}
 
 
 def main():
@@ -119,7 +207,6 @@ def main():
               "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_calibration:
@@ -132,81 +219,36 @@ def main():
         return
 
     import sparse_attention_long_reduce_amd as cpa
-    from workloads import make_config
 
     name, desc = WORKLOADS[args.workload]
-    t0 = time.perf_counter()
-    w = make_config(name)
-    log(f"[bench] generated {name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    bf = torch.bfloat16
-    masks = torch.from_numpy(w.masks).to(dev)
-    masks_dense = torch.ones_like(masks)   # entries outside the causal region are ignored
-    pb = torch.from_numpy(w.prefix_blocks).to(dev)
-    cb = torch.from_numpy(w.chunk_blocks).to(dev)
-    q = torch.from_numpy(w.q).to(dev).to(bf)
-    kp = torch.from_numpy(w.k_pages).to(dev).to(bf)
-    vp = torch.from_numpy(w.v_pages).to(dev).to(bf)
-    pm = torch.from_numpy(w.page_map).to(dev)
-    cu = torch.from_numpy(w.cu_q).to(dev)
-    pl = torch.from_numpy(w.prefix_len).to(dev)
-    tables = torch.empty((w.B, w.Hkv, w.nkvb_max), dtype=torch.int32, device=dev)
-    counts = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
-    out = torch.empty_like(q)
-    lse = torch.empty((q.shape[0], w.Hq), dtype=torch.float32, device=dev)
+    t0 = time.perf_counter()
+    batches = make_batches(args.workload, dev)
     torch.cuda.synchronize()
-    log("[bench] inputs resident on the GPU")
+    log(f"[bench] {name}: {len(batches)} launch pair(s) per step, inputs resident on the GPU "
+        f"({time.perf_counter() - t0:.1f} s)")
 
-    def step(m):
-        cpa.build_block_tables(m, pb, cb, w.Hkv, tables=tables, counts=counts)
-        cpa.chunked_prefill(q, kp, vp, pm, tables, counts, cu, pl, w.max_chunk_len, out=out, lse=lse)
-
-    def timed(m, steps, warmup):
-        for _ in range(warmup):
-            step(m)
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        t0 = time.perf_counter()
-        for i in range(steps):
-            ev[i][0].record()
-            cpa.build_block_tables(m, pb, cb, w.Hkv, tables=tables, counts=counts)
-            ev[i][1].record()
-            cpa.chunked_prefill(q, kp, vp, pm, tables, counts, cu, pl, w.max_chunk_len, out=out, lse=lse)
-            ev[i][2].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        build_ms = [e[0].elapsed_time(e[1]) for e in ev]
-        pre_ms = [e[1].elapsed_time(e[2]) for e in ev]
-        total_ms = ev[0][0].elapsed_time(ev[-1][2])
-        return {"step_ms": total_ms / steps, "build_ms": float(np.mean(build_ms)),
-                "prefill_ms": float(np.mean(pre_ms)), "prefill_ms_median": float(np.median(pre_ms)),
-                "prefill_ms_min": float(np.min(pre_ms)), "wall_s": wall}
-
-    # sparse (the method)
-    r = timed(masks, args.steps, args.warmup)
-    T = tables.cpu().numpy()
-    Cn = counts.cpu().numpy()
-    flops = cpa.attention_flops(T, Cn, w.prefix_len, w.chunk_len, w.Hq, w.Hkv, w.d)
+    r = timed(cpa, batches, False, args.steps, args.warmup)
+    flops = sum(bt.flops(cpa) for bt in batches)
+    union = sum(int(bt.counts.sum()) for bt in batches)
     log(f"[bench] sparse: step {r['step_ms']:.3f} ms, prefill {r['prefill_ms']:.3f} ms, "
-        f"build {r['build_ms'] * 1e3:.1f} us, union blocks {int(Cn.sum())} of "
-        f"{int(w.B * w.Hkv * w.nkvb_max)}")
-    # dense (all-ones masks through the same kernels)
+        f"build {r['build_ms'] * 1e3:.1f} us, union blocks {union}")
     d = None
     if not args.no_dense:
-        d = timed(masks_dense, max(5, args.steps // 2), 2)
-        Td = tables.cpu().numpy()
-        Cd = counts.cpu().numpy()
-        dflops = cpa.attention_flops(Td, Cd, w.prefix_len, w.chunk_len, w.Hq, w.Hkv, w.d)
+        d = timed(cpa, batches, True, max(5, args.steps // 2), 2)
+        dflops = sum(bt.flops(cpa) for bt in batches)
         log(f"[bench] dense: step {d['step_ms']:.3f} ms, prefill {d['prefill_ms']:.3f} ms")
-        cpa.build_block_tables(masks, pb, cb, w.Hkv, tables=tables, counts=counts)
+        for bt in batches:      # leave the sparse tables in place
+            bt.build(cpa, False)
         torch.cuda.synchronize()
 
+    w0 = batches[-1].w
     step_tflops = flops / (r["step_ms"] * 1e-3) / 1e12
     pre_tflops = flops / (r["prefill_ms"] * 1e-3) / 1e12
-    mask_bytes = int(w.masks.nbytes)
-    tab_bytes = int(T.nbytes + Cn.nbytes)
-    traffic = read_traffic(args.workload)
+    mask_bytes = sum(int(bt.w.masks.nbytes) for bt in batches)
+    tab_bytes = sum(int(bt.tables.numel() * 4 + bt.counts.numel() * 4) for bt in batches)
+    context = int(max(int(bt.w.prefix_len.max() + bt.w.chunk_len.max()) for bt in batches))
     result = {
         "metric": "selected-block attention TFLOP/s + speedup vs dense at 128K context, chunk 2048",
         "value": round(step_tflops, 2),
@@ -220,21 +262,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, synthetic block masks, permuted paged KV pool)",
-        "config": {"workload": desc, "sequences": int(w.B), "chunk_len": int(w.max_chunk_len),
-                   "context": int(w.prefix_len.max() + w.max_chunk_len), "Hq": w.Hq, "Hkv": w.Hkv,
-                   "head_dim": w.d, "block": 64},
+        "config": {"workload": desc, "sequences": int(w0.B), "chunk_len": int(w0.max_chunk_len),
+                   "context": context, "Hq": w0.Hq, "Hkv": w0.Hkv, "head_dim": w0.d, "block": 64,
+                   "launch_pairs_per_step": len(batches)},
         "selected_flop": int(flops),
-        "union_blocks": int(Cn.sum()),
+        "union_blocks": union,
         "prefill_tflops": round(pre_tflops, 2),
         "prefill_ms": round(r["prefill_ms"], 4),
         "table_build_us": round(r["build_ms"] * 1e3, 2),
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "prefill_kernel<bf16,128>"},
-        "table_build_roofline": {"bound": "hbm", "achieved": round((mask_bytes + tab_bytes) / (r["build_ms"] * 1e-3) / 1e9, 1),
-                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round((mask_bytes + tab_bytes) / (r["build_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-                                 "algorithmic_bytes": mask_bytes + tab_bytes},
+                     "traffic": read_traffic(args.workload), "kernel": "prefill_bf16_kernel<128>"},
+        "table_build_roofline": {
+            "bound": "hbm", "achieved": round((mask_bytes + tab_bytes) / (r["build_ms"] * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round((mask_bytes + tab_bytes) / (r["build_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+            "algorithmic_bytes": mask_bytes + tab_bytes},
     }
     if d is not None:
         result["dense"] = {"step_ms": round(d["step_ms"], 4), "prefill_ms": round(d["prefill_ms"], 4),
@@ -245,7 +288,8 @@ def main():
                                "LLaMA-3.1-8B-Instruct (hardware not stated); context only")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(w, T, Cn)
+        bt = batches[-1]
+        result["cpu_baseline"] = cpu_baseline(bt.w, bt.tables.cpu().numpy(), bt.counts.cpu().numpy())
     print(json.dumps(result), flush=True)
 
 
