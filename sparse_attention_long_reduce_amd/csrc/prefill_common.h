@@ -35,18 +35,38 @@ __device__ __forceinline__ int count_above(const int32_t* tab, int cnt, int nqb,
   return c;
 }
 
+// Position of lane j's KV group (j < ngx, the groups gi = xcd + 8*j) when the groups of one XCD
+// are sorted by table length, longest first (ties by j); wave-uniform loop over ngx <= 64.
+__device__ __forceinline__ int weight_rank(const PrefillArgs& a, int xcd, int ngx, int lane) {
+  const int c = lane < ngx ? min(max(a.counts[xcd + 8 * lane], 0), a.table_cap) : -1;
+  int r = 0;
+  for (int i = 0; i < ngx; ++i) {
+    const int ci = __shfl(c, i);
+    r += (ci > c) || (ci == c && i < lane);
+  }
+  return r;
+}
+
 // Workgroup -> (KV group index gi = b*Hkv + g, tile rank).  Workgroups are dispatched
-// round-robin over the 8 XCDs (blockIdx % 8); with xcd_remap every tile of one KV group lands on
-// the same XCD so that the group's pages are shared through that XCD's L2, and tiles of rank 0
-// (the last query blocks, which see the most pages) start first.  Returns false for padding.
-__device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int& gi, int& rank) {
+// round-robin over the 8 XCDs (blockIdx % 8) and, within an XCD, in blockIdx order as CUs free
+// up.  With xcd_remap every tile of one KV group lands on the same XCD, so the group's pages
+// are shared through that XCD's L2.  Work is handed out longest first: the groups of an XCD in
+// decreasing table length (a tile visits about as many pages as its group's table holds), and
+// within a group the tiles of rank 0 (the last query blocks, which see the most pages) first.
+// Beyond 64 groups per XCD the groups go in index order.  Returns false for padding.
+__device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int lane, int& gi, int& rank) {
   if (a.xcd_remap) {
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
     const int ngx = (a.n_groups - xcd + 7) >> 3;  // groups gi with gi % 8 == xcd
     if (slot >= ngx * a.tiles_per_group) return false;
-    gi = xcd + 8 * (slot % ngx);
-    rank = slot / ngx;
+    int k = slot / a.tiles_per_group;
+    rank = slot - k * a.tiles_per_group;
+    if (ngx <= 64) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(weight_rank(a, xcd, ngx, lane) == k);
+      k = __builtin_ctzll(hit);
+    }
+    gi = xcd + 8 * k;
   } else {
     if ((int)blockIdx.x >= a.n_groups * a.tiles_per_group) return false;
     gi = blockIdx.x % a.n_groups;

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
 
   // ---- tile decode ---------------------------------------------------------------------
   int gi, rank;
-  if (!decode_tile(a, gi, rank)) return;
+  if (!decode_tile(a, lane, gi, rank)) return;
   const int b = gi / a.Hkv;
   const int g = gi - b * a.Hkv;
   const int hsub = rank % a.hsplit;
