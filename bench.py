@@ -127,20 +127,28 @@ class Batch:
         self.pl = torch.from_numpy(w.prefix_len).to(dev)
         self.tables = torch.empty((w.B, w.Hkv, w.nkvb_max), dtype=torch.int32, device=dev)
         self.counts = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
+        self.tables_dense = torch.empty_like(self.tables)
+        self.counts_dense = torch.empty_like(self.counts)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((self.q.shape[0], w.Hq), dtype=torch.float32, device=dev)
 
     def build(self, cpa, dense):
-        cpa.build_block_tables(self.masks_dense if dense else self.masks, self.pb, self.cb, self.w.Hkv,
-                               tables=self.tables, counts=self.counts)
+        if dense:
+            cpa.build_block_tables(self.masks_dense, self.pb, self.cb, self.w.Hkv,
+                                   tables=self.tables_dense, counts=self.counts_dense)
+        else:
+            cpa.build_block_tables(self.masks, self.pb, self.cb, self.w.Hkv,
+                                   tables=self.tables, counts=self.counts)
 
-    def prefill(self, cpa):
-        cpa.chunked_prefill(self.q, self.kp, self.vp, self.pm, self.tables, self.counts, self.cu, self.pl,
+    def prefill(self, cpa, dense):
+        t, c = (self.tables_dense, self.counts_dense) if dense else (self.tables, self.counts)
+        cpa.chunked_prefill(self.q, self.kp, self.vp, self.pm, t, c, self.cu, self.pl,
                             self.w.max_chunk_len, out=self.out, lse=self.lse)
 
-    def flops(self, cpa):
+    def flops(self, cpa, dense=False):
         w = self.w
-        return cpa.attention_flops(self.tables.cpu().numpy(), self.counts.cpu().numpy(), w.prefix_len,
+        t, c = (self.tables_dense, self.counts_dense) if dense else (self.tables, self.counts)
+        return cpa.attention_flops(t.cpu().numpy(), c.cpu().numpy(), w.prefix_len,
                                    w.chunk_len, w.Hq, w.Hkv, w.d)
 
 
@@ -160,34 +168,40 @@ def make_batches(key, dev):
     return batches
 
 
-def timed(cpa, batches, dense, steps, warmup):
-    """Runs warmup + steps steps; HIP events around every launch on torch's current stream
-    (the stream the library launches on)."""
+def timed(cpa, batches, modes, steps, warmup):
+    """Runs warmup + steps steps; a step runs every launch pair of the workload once for each
+    mode in `modes` (False = the workload's masks, True = all-ones masks), the modes taking turns
+    so that both see the same clock and thermal state.  HIP events around every launch on torch's
+    current stream (the stream the library launches on).  Returns one summary per mode."""
     import numpy as np
     import torch
     for _ in range(warmup):
-        for bt in batches:
-            bt.build(cpa, dense)
-            bt.prefill(cpa)
+        for dense in modes:
+            for bt in batches:
+                bt.build(cpa, dense)
+                bt.prefill(cpa, dense)
     torch.cuda.synchronize()
-    nb = len(batches)
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)] for _ in range(steps)]
-    t0 = time.perf_counter()
+    nb, nm = len(batches), len(modes)
+    ev = [[[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nb)] for _ in range(nm)]
+          for _ in range(steps)]
     for s in range(steps):
-        for i, bt in enumerate(batches):
-            ev[s][i][0].record()
-            bt.build(cpa, dense)
-            ev[s][i][1].record()
-            bt.prefill(cpa)
-            ev[s][i][2].record()
+        for m, dense in enumerate(modes):
+            for i, bt in enumerate(batches):
+                ev[s][m][i][0].record()
+                bt.build(cpa, dense)
+                ev[s][m][i][1].record()
+                bt.prefill(cpa, dense)
+                ev[s][m][i][2].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    build = np.array([[e[0].elapsed_time(e[1]) for e in st] for st in ev])   # [steps][batches] ms
-    pre = np.array([[e[1].elapsed_time(e[2]) for e in st] for st in ev])
-    total_ms = ev[0][0][0].elapsed_time(ev[-1][-1][2])
-    return {"step_ms": total_ms / steps, "build_ms": float(build.sum(1).mean()),
-            "prefill_ms": float(pre.sum(1).mean()), "prefill_ms_median": float(np.median(pre.sum(1))),
-            "prefill_launch_ms": float(pre.mean()), "wall_s": wall, "launches_per_step": nb}
+    out = []
+    for m in range(nm):
+        build = np.array([[e[0].elapsed_time(e[1]) for e in ev[s][m]] for s in range(steps)])   # ms
+        pre = np.array([[e[1].elapsed_time(e[2]) for e in ev[s][m]] for s in range(steps)])
+        step = np.array([ev[s][m][0][0].elapsed_time(ev[s][m][-1][2]) for s in range(steps)])
+        out.append({"step_ms": float(step.mean()), "build_ms": float(build.sum(1).mean()),
+                    "prefill_ms": float(pre.sum(1).mean()), "prefill_ms_median": float(np.median(pre.sum(1))),
+                    "prefill_launch_ms": float(pre.mean()), "launches_per_step": nb})
+    return out
 
 
 def main():
@@ -229,19 +243,18 @@ def main():
     log(f"[bench] {name}: {len(batches)} launch pair(s) per step, inputs resident on the GPU "
         f"({time.perf_counter() - t0:.1f} s)")
 
-    r = timed(cpa, batches, False, args.steps, args.warmup)
+    modes = (False,) if args.no_dense else (False, True)
+    res = timed(cpa, batches, modes, args.steps, args.warmup)
+    r = res[0]
     flops = sum(bt.flops(cpa) for bt in batches)
     union = sum(int(bt.counts.sum()) for bt in batches)
     log(f"[bench] sparse: step {r['step_ms']:.3f} ms, prefill {r['prefill_ms']:.3f} ms, "
         f"build {r['build_ms'] * 1e3:.1f} us, union blocks {union}")
     d = None
     if not args.no_dense:
-        d = timed(cpa, batches, True, max(5, args.steps // 2), 2)
-        dflops = sum(bt.flops(cpa) for bt in batches)
+        d = res[1]
+        dflops = sum(bt.flops(cpa, dense=True) for bt in batches)
         log(f"[bench] dense: step {d['step_ms']:.3f} ms, prefill {d['prefill_ms']:.3f} ms")
-        for bt in batches:      # leave the sparse tables in place
-            bt.build(cpa, False)
-        torch.cuda.synchronize()
 
     w0 = batches[-1].w
     step_tflops = flops / (r["step_ms"] * 1e-3) / 1e12
