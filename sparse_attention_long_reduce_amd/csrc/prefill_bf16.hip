@@ -10,8 +10,7 @@
 // 32 chunk rows; two waves cover the 64 rows of a query block.  For G = 4 the workgroup is the
 // group's four heads on one query block; G = 2 (1) packs 2 (4) query blocks; G > 4 splits the
 // heads over G/4 workgroups.  Every selected KV page is brought into LDS once per workgroup
-// and read by all eight waves, i.e. by every head and row of the tile.  Two waves share each
-// SIMD, so one wave's MFMAs can overlap the other's softmax.
+// and read by all eight waves, i.e. by every head and row of the tile.
 //
 // Page staging.  Each page (64 tokens x d, K and V) is copied HBM -> LDS by the gfx950
 // direct-to-LDS loads (global_load_lds_dwordx4): every instruction moves 64 16-byte chunks,
@@ -22,32 +21,45 @@
 //   V: natural [token][d] rows with chunk c at c ^ swz_v(r); the PV operand (8 consecutive
 //      keys of one column per lane) is produced by two ds_read_b64_tr_b16 transposed reads,
 //      which the swizzle keeps free of bank conflicts.
-// No staging registers and no LDS stores are needed.  Pages are processed two per barrier and
-// double-buffered in statically distinct LDS arrays (the loop is unrolled over the two buffer
-// sets), so the compiler can tell the tiles being read from the ones being filled and never
-// waits for the prefetch early.  The page ids of the table are resolved a window at a time
-// into LDS.
+// No staging registers and no LDS stores are needed.  Waves 0-3 copy K, waves 4-7 copy V.
 //
-// Per page (64 keys) and wave (32 query rows), in the transposed domain so that each lane owns
-// whole query rows:
-//   S^T[key][row] = K . Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q^T in registers
-//   causal cut (only when the page reaches past the wave's first row position)
-//   online softmax in fp32, log2 domain, softmax scale folded into one FMA; a row's 64 scores
-//   live in lanes l and l^32 (one permlane32 swap per row maximum).  The output is rescaled
-//   only when a row maximum grows by more than 2^8 over the reference it was accumulated with.
-//   The row sum adds the bf16-rounded weights that enter the PV product (v_dot2_f32_bf16 with
-//   ones, two weights per instruction), so the result is normalised by exactly the weights used.
-//   This file is compiled without NaN semantics so that maxima need no operand quieting; NaN
-//   inputs still propagate through the exponentials and the MFMAs to the output.
-//   O^T[dv][row] += V^T . P^T   A = V^T by transposed LDS reads, B = P^T rounded to bf16
-//                               straight from the score accumulators
+// Software pipeline.  Per page (64 keys) and wave (32 query rows), in the transposed domain so
+// that each lane owns whole query rows:
+//   QK   S^T[key][row] = K . Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q^T in VGPRs
+//   SM   causal cut (only on pages that reach past the wave's first row), online softmax in
+//        fp32, log2 domain, softmax scale folded into one FMA; a row's 64 scores live in lanes
+//        l and l^32 (one permlane32 swap per row maximum); P^T rounded to bf16
+//   PV   O^T[dv][row] += V^T . P^T   A = V^T by transposed LDS reads, B = P^T
+// The pipeline works on units of 32 keys (half a page): unit u runs SM of unit u together with
+// QK of unit u+1 and PV of unit u-1.  The three are independent, so each wave's softmax VALU
+// work issues in the shadow of its own MFMAs instead of waiting for them.  Iteration i of the
+// page loop is units 2i+1 and 2i+2: it reads K of page i+1 and V of page i only.  Copies run
+// two iterations ahead (iteration i issues K of page i+4 and V of page i+3 and its barrier
+// waits for the copies of iteration i-2), so K and V each live in a ring of four LDS tiles.
+// The loop is unrolled over four iterations so that every ring tile is named statically; the
+// compiler can then tell the tiles being read from the ones being filled and never waits for a
+// copy early.  A wave with nothing to copy (table end) or whose page cannot be copied directly
+// (an unresolved page id, or the sequence's partial last page, both written through registers
+// instead) sends its copy instructions to a scratch LDS tile, so every wave issues the same
+// number of copies per iteration.
+//
+// Rescaling is lazy: the output accumulators are rescaled only when a row maximum grows by more
+// than 2^8 over the reference it was accumulated with, after PV of the previous unit has added
+// the weights taken against the old reference.  The row sum adds the bf16-rounded weights that
+// enter the PV product (v_dot2_f32_bf16 with ones, two weights per instruction), so the result
+// is normalised by exactly the weights used.  This file is compiled without NaN semantics so
+// that maxima need no operand quieting; NaN inputs still propagate through the exponentials and
+// the MFMAs to the output.
 #include "prefill_common.h"
+
+#include <type_traits>
 
 namespace cpa {
 namespace {
 
 constexpr int THREADS = 512;
-constexpr int WIN = 1024;  // page ids resolved per window
+constexpr int WIN = 1024;  // circular window of resolved page ids
+constexpr int CH = 512;    // ids resolved at a time
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -59,6 +71,7 @@ struct Geo {
   static constexpr int PAGE = 64 * D;   // bf16 elements of one K (or V) page
   static constexpr int NPW = CPR / 4;   // direct-to-LDS instructions per wave per page and tensor
   static constexpr int DT = D / 32;     // 32-wide output column tiles
+  static constexpr int KS = D / 16;     // k-steps of the QK product
 };
 
 // chunk position of K chunk c of row r is c ^ swz_k(r); of V chunk c is c ^ swz_v(r)
@@ -78,23 +91,39 @@ __device__ __forceinline__ v4i16 ds_read_tr(const __bf16* p) {
       (lds_v4i16*)((__attribute__((address_space(3))) char*)(__attribute__((address_space(3))) void*)p));
 }
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8); }
+
+// Workgroup barrier that waits only for this wave's LDS traffic and for all but its newest `VM`
+// vector-memory operations (the copies issued in the current iteration stay in flight).  The
+// asm statement keeps the compiler from moving memory accesses across it.
+template <int VM>
+__device__ __forceinline__ void barrier_keep_vm() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, 0));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
 template <int D>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
   using GE = Geo<D>;
-  __shared__ __attribute__((aligned(1024))) __bf16 kA0[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 vA0[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 kA1[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 vA1[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 kB0[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 vB0[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 kB1[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 vB1[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kR0[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kR1[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kR2[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 kR3[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vR0[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vR1[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vR2[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 vR3[GE::PAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sink[GE::NPW * 512];  // target of idle copies
   __shared__ int win_kb[WIN];
   __shared__ int win_ph[WIN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hl = lane >> 5;  // lane half
 
@@ -135,9 +164,9 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int row = row0 + l32;               // this lane's chunk row
   const bool row_ok = active && row < Cn;
   const __bf16* qsrc = reinterpret_cast<const __bf16*>(a.q) + ((size_t)(q0 + (row_ok ? row : 0)) * a.Hq + head) * D;
-  bf16x8 qb[D / 16];
+  bf16x8 qb[GE::KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
+  for (int ks = 0; ks < GE::KS; ++ks) {
     const uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qsrc + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
     qb[ks] = __builtin_bit_cast(bf16x8, u);
   }
@@ -146,6 +175,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // waves 0-3 move K, waves 4-7 move V; wave w's instruction j fills LDS chunks
   // [(4w' + j) * 64, +64) of its tensor (w' = w % 4), lane l the chunk at position +l.
   const bool vrole = wave >= 4;
+  const __bf16* const tg = vrole ? vg : kg;  // this wave's tensor of group g
   int dma_off[GE::NPW];   // element offset of the lane's source chunk within a page
   int dma_row[GE::NPW];
 #pragma unroll
@@ -158,46 +188,48 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   }
   const int dma_dst = (wave & 3) * GE::NPW * 64 * 8;  // elements; + j * 512
 
-  // A page fill is planned once and then issued one direct-to-LDS instruction at a time in
-  // between the MFMAs of the QK product, so that the vector-memory queue drains while the matrix
-  // core works instead of stalling the issuing wave.  Pages that are unresolved (NaN) or end
-  // inside the sequence (rows past the end read as 0) are filled at once through registers.
+  // A copy is planned at the top of an iteration and issued one direct-to-LDS instruction at a
+  // time in between the iteration's MFMAs.  Pages that are unresolved (NaN) or end inside the
+  // sequence (rows past the end read as 0) are written through registers at once; their copy
+  // instructions, like those of an idle wave, read page 0 of the pool into the sink tile.
   struct Fill {
-    bool on;             // direct-to-LDS instructions still to issue
     const __bf16* src;   // this wave's tensor (K or V) of the page
     __bf16* dst;         // this wave's part of the destination tile
   };
-  auto plan = [&](int kb, int ph, __bf16* ks, __bf16* vs) __attribute__((always_inline)) {
+  const Fill idle{tg, sink};
+  auto plan = [&](bool valid, int kb, int ph, __bf16* tile) __attribute__((always_inline)) {
+    if (!valid) return idle;
     const int nv_tok = min(max(L - 64 * kb, 0), 64);
-    const __bf16* src = (vrole ? vg : kg) + (size_t)(ph < 0 ? 0 : ph) * a.page_stride;
-    __bf16* dst = (vrole ? vs : ks) + dma_dst;
-    Fill f{ph >= 0 && nv_tok == 64, src, dst};
-    if (!f.on) {
-      const uint32_t fv = ph < 0 ? 0x7FC07FC0u : 0u;
+    if (ph >= 0 && nv_tok == 64) return Fill{tg + (size_t)ph * a.page_stride, tile + dma_dst};
+    const __bf16* src = tg + (size_t)(ph < 0 ? 0 : ph) * a.page_stride;
+    const uint32_t fv = ph < 0 ? 0x7FC07FC0u : 0u;
 #pragma unroll
-      for (int j = 0; j < GE::NPW; ++j) {
-        uint4 v = make_uint4(fv, fv, fv, fv);
-        if (ph >= 0 && dma_row[j] < nv_tok) v = *reinterpret_cast<const uint4*>(src + dma_off[j]);
-        *reinterpret_cast<uint4*>(dst + j * 512 + lane * 8) = v;
-      }
+    for (int j = 0; j < GE::NPW; ++j) {
+      uint4 v = make_uint4(fv, fv, fv, fv);
+      if (ph >= 0 && dma_row[j] < nv_tok) v = *reinterpret_cast<const uint4*>(src + dma_off[j]);
+      *reinterpret_cast<uint4*>(tile + dma_dst + j * 512 + lane * 8) = v;
     }
-    return f;
+    return idle;
   };
   auto fill_one = [&](const Fill& f, int j) __attribute__((always_inline)) {
-    if (f.on) lds_dma16(f.src + dma_off[j], f.dst + j * 512);
+    lds_dma16(f.src + dma_off[j], f.dst + j * 512);
   };
-  const Fill no_fill{false, nullptr, nullptr};
+  auto fill_all = [&](const Fill& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < GE::NPW; ++j) fill_one(f, j);
+  };
 
-  auto load_window = [&](int base) __attribute__((always_inline)) {
-    for (int j = tid; j < WIN && base + j < n_iter; j += THREADS) {
+  // resolve table entries [base, base + CH) into window slots (base + j) % WIN
+  auto load_chunk = [&](int base) __attribute__((always_inline)) {
+    for (int j = tid; j < CH && base + j < n_iter; j += THREADS) {
       const int kb = tab[base + j];
       int ph = -1;
       if (kb >= 0 && kb < a.page_map_stride) {
         ph = pmap[kb];
         if (ph < 0 || (int64_t)ph >= a.n_pages) ph = -1;
       }
-      win_kb[j] = kb;
-      win_ph[j] = ph;
+      win_kb[(base + j) % WIN] = kb;
+      win_ph[(base + j) % WIN] = ph;
     }
   };
 
@@ -230,148 +262,224 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int row_pos = P + row;
   const int wave_pos0 = P + row0;
 
-  f32x16 s0, s1;  // S^T of the page in flight, keys 0-31 and 32-63
+  // scores of the unit in softmax and of the unit in QK (the two alternate), and the bf16
+  // weights of two units as PV operands
+  f32x16 sx, sy;
+  bf16x8 px0, px1, py0, py1;
 
-  // S^T = K Q^T for the page in LDS tile Kl, issuing the fill f along the way
-  auto qk = [&](const __bf16* Kl, const Fill& f) __attribute__((always_inline)) {
+  // ---- the three stages, on units of 32 keys (page half h) ----------------------------------
+  // QK: S^T = K Q^T for half h of the page in LDS tile Kl; copy instructions j0 .. j0+NJ-1 of f
+  // go out in between
+  constexpr int NJ = GE::NPW / 2 > 0 ? GE::NPW / 2 : 1;   // copy instructions per unit
+  auto qk = [&](const __bf16* Kl, int h, f32x16& s, const Fill& f, int j0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) { s0[j] = 0.f; s1[j] = 0.f; }
+    for (int j = 0; j < 16; ++j) s[j] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int off = k_row_off + (((2 * ks + hl) ^ k_sw) << 3);
-      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(Kl + off);
-      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(Kl + off + 32 * D);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka0, qb[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka1, qb[ks], s1, 0, 0, 0);
-      if (ks % ((D / 16) / GE::NPW) == 0) fill_one(f, ks / ((D / 16) / GE::NPW));
+    for (int ks = 0; ks < GE::KS; ++ks) {
+      const int off = k_row_off + 32 * h * D + (((2 * ks + hl) ^ k_sw) << 3);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kl + off);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s, 0, 0, 0);
+      if (ks % (GE::KS / NJ) == 0 && j0 + ks / (GE::KS / NJ) < GE::NPW) fill_one(f, j0 + ks / (GE::KS / NJ));
     }
   };
-  auto fill_all = [&](const Fill& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < GE::NPW; ++j) fill_one(f, j);
-  };
-
-  // causal cut, online softmax and O^T += V^T P^T for page kb (scores in s0/s1, V tile Vl)
-  auto softmax_pv = [&](const __bf16* Vl, int kb) __attribute__((always_inline)) {
-    // causal cut: key position 64*kb + key index must not exceed the row position
-    if (64 * kb + 63 > wave_pos0) {
+  // SM, causal cut of half h of page kb: key position must not exceed the row position
+  auto causal = [&](f32x16& s, int kb, int h) __attribute__((always_inline)) {
+    const int k0 = 64 * kb + 32 * h;
+    if (k0 + 31 > wave_pos0) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = 64 * kb + 8 * (j >> 2) + 4 * hl + (j & 3);
-        if (key > row_pos) s0[j] = -INFINITY;
-        if (key + 32 > row_pos) s1[j] = -INFINITY;
-      }
-    }
-
-    // online softmax (log2 domain), lazy rescale
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(s0[j], s1[j]));
-    mx = xhalf_max(mx) * cs;
-    const bool need = mx > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < GE::DT; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
-      m_run = m_new;
-    }
-    const float ref = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s0[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], cs, -ref));
-      s1[j] = __builtin_amdgcn_exp2f(fmaf(s1[j], cs, -ref));
-    }
-
-    // O^T += V^T P^T; keys of step (kt, u) for lane half hl, element e:
-    //   32*kt + 16*u + 8*(e / 4) + 4*hl + e % 4
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)(kt == 0 ? s0[8 * u + e] : s1[8 * u + e]);
-        // the row sum accumulates the same bf16 weights the PV product uses, two per dot2
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pp = {pb[e], pb[e + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, kOnes2, l_run, false);
-        }
-        const int krow = (32 * kt + 16 * u) * D;
-#pragma unroll
-        for (int dt = 0; dt < GE::DT; ++dt) {
-          const v4i16 lo = ds_read_tr(Vl + krow + v_off[dt]);
-          const v4i16 hi = ds_read_tr(Vl + krow + 8 * D + v_off[dt]);
-          const v4i16 both[2] = {lo, hi};
-          const bf16x8 va = __builtin_bit_cast(bf16x8, both);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-        }
+        const int key = k0 + 8 * (j >> 2) + 4 * hl + (j & 3);
+        if (key > row_pos) s[j] = -INFINITY;
       }
     }
   };
-
-  // ---- main loop ---------------------------------------------------------------------------
-  // Pages go two per iteration.  Tile set A holds pages 2j and 2j+1 while set B receives pages
-  // 2j+2 and 2j+3 (and the other way round on the next iteration); the loop is unrolled over
-  // the two sets so that every LDS read names its tile and the compiler never has to wait for an
-  // unrelated prefetch.  The page ids an iteration prefetches were read from the window one
-  // iteration earlier, so no LDS latency sits in front of the prefetch.  One barrier per two
-  // pages.
-  if (n_iter > 0) {
-    load_window(0);
-    __syncthreads();
-    int kb0 = win_kb[0], ph0 = win_ph[0];
-    int kb1 = n_iter > 1 ? win_kb[1] : 0, ph1 = n_iter > 1 ? win_ph[1] : 0;
-    fill_all(plan(kb0, ph0, kA0, vA0));
-    if (n_iter > 1) fill_all(plan(kb1, ph1, kA1, vA1));
-    // ids of the next pair
-    int kb2 = n_iter > 2 ? win_kb[2] : 0, ph2 = n_iter > 2 ? win_ph[2] : 0;
-    int kb3 = n_iter > 3 ? win_kb[3] : 0, ph3 = n_iter > 3 ? win_ph[3] : 0;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS fills have landed
-    __syncthreads();
-
-    // pages p and p+1 sit in (ck0, cv0) and (ck1, cv1); pages p+2, p+3 go to (nk0, nv0), (nk1, nv1)
-    auto pair = [&](int p, const __bf16* ck0, const __bf16* cv0, const __bf16* ck1, const __bf16* cv1,
-                    __bf16* nk0, __bf16* nv0, __bf16* nk1, __bf16* nv1) __attribute__((always_inline)) {
-      const Fill f0 = p + 2 < n_iter ? plan(kb2, ph2, nk0, nv0) : no_fill;
-      const Fill f1 = p + 3 < n_iter ? plan(kb3, ph3, nk1, nv1) : no_fill;
-      const int kc0 = kb0, kc1 = kb1;
-      kb0 = kb2; kb1 = kb3;
-      if (p + 4 < n_iter) {
-        if ((p + 4) % WIN == 0) {
-          load_window(p + 4);
-          __syncthreads();
-        }
-        kb2 = win_kb[(p + 4) % WIN];
-        ph2 = win_ph[(p + 4) % WIN];
-        if (p + 5 < n_iter) {
-          kb3 = win_kb[(p + 5) % WIN];
-          ph3 = win_ph[(p + 5) % WIN];
-        }
-      }
-      if (p < n_vis) {
-        qk(ck0, f0);
-        softmax_pv(cv0, kc0);
-      } else {
-        fill_all(f0);
-      }
-      if (p + 1 < n_vis) {
-        qk(ck1, f1);
-        softmax_pv(cv1, kc1);
-      } else {
-        fill_all(f1);
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-    };
-    for (int p = 0; p < n_iter; p += 4) {
-      pair(p, kA0, vA0, kA1, vA1, kB0, vB0, kB1, vB1);
-      if (p + 2 < n_iter) pair(p + 2, kB0, vB0, kB1, vB1, kA0, vA0, kA1, vA1);
+  // SM, row maximum and reference update; returns whether this lane moved its reference (the
+  // accumulators then take the factor alpha once PV of the previous unit is in)
+  auto reference = [&](const f32x16& s, float& alpha) __attribute__((always_inline)) {
+    float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s[j], s[j + 1]));
+    mx = xhalf_max(mx) * cs;
+    const bool need = mx > m_run + kRescaleThreshold;
+    alpha = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+    m_run = need ? mx : m_run;
+    l_run *= alpha;
+    return need;
+  };
+  // SM, weights against the reference, rounded to bf16 as the PV operands, and row sums.
+  //   key of operand u (0, 1), element e, lane half hl: 16*u + 8*(e / 4) + 4*hl + e % 4
+  auto weights = [&](f32x16& s, bf16x8& p0, bf16x8& p1) __attribute__((always_inline)) {
+    const float ref = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], cs, -ref));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p0[e] = (__bf16)s[e];
+      p1[e] = (__bf16)s[8 + e];
     }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[e], p0[e + 1]}, kOnes2, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[e], p1[e + 1]}, kOnes2, l_run, false);
+    }
+  };
+  // PV: O^T += V^T P^T for half h of the page in LDS tile Vl
+  auto pv = [&](const __bf16* Vl, int h, const bf16x8& p0, const bf16x8& p1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int krow = (32 * h + 16 * u) * D;
+#pragma unroll
+      for (int dt = 0; dt < GE::DT; ++dt) {
+        const v4i16 lo = ds_read_tr(Vl + krow + v_off[dt]);
+        const v4i16 hi = ds_read_tr(Vl + krow + 8 * D + v_off[dt]);
+        const v4i16 both[2] = {lo, hi};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, both);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, u == 0 ? p0 : p1, o[dt], 0, 0, 0);
+      }
+    }
+  };
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < GE::DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[dt][j] *= alpha;
+  };
+  // One unit: SM of the scores in sm (half hs of page kbs) into weights pc0/pc1, QK of half hq
+  // of the page in tile Kq into sq, PV of half hv of the page in tile Vp with weights pp0/pp1.
+  // Apart from the causal cut (on the last pages only) and the rescale, it is one basic block,
+  // so that the scheduler can interleave the three stages.
+  auto unit = [&](f32x16& sm, int kbs, int hs, bf16x8& pc0, bf16x8& pc1, const __bf16* Kq, int hq, f32x16& sq,
+                  const __bf16* Vp, int hv, const bf16x8& pp0, const bf16x8& pp1,
+                  const Fill& f, int j0) __attribute__((always_inline)) {
+    causal(sm, kbs, hs);
+    float alpha;
+    const bool need = reference(sm, alpha);
+    qk(Kq, hq, sq, f, j0);
+    weights(sm, pc0, pc1);
+    pv(Vp, hv, pp0, pp1);
+    // the weights belong to this block: keep the compiler from sinking their computation past
+    // the rescale branch into the next unit
+    asm volatile("" ::"v"(pc0), "v"(pc1), "v"(l_run));
+    if (__builtin_amdgcn_ballot_w64(need)) rescale(alpha);
+  };
+
+  // ---- page loop ---------------------------------------------------------------------------
+  // A wave computes the pages [0, n_vis) of the table; the workgroup walks [0, n_iter), and
+  // n_iter > n_vis only for waves on earlier query blocks of a multi-block tile.  Per wave:
+  //   prologue     QK of units 0 and 1, SM of unit 0
+  //   i in [0, n_vis - 1)    iteration i in full (units 2i+1, 2i+2)
+  //   i = n_vis - 1          drain: SM of unit 2i+1, PV of units 2i and 2i+1
+  //   i in [n_vis, n_iter)   copies and barriers only
+  if (n_iter > 0) {
+    load_chunk(0);
+    __syncthreads();
+    auto kb_at = [&](int j) __attribute__((always_inline)) { return win_kb[j % WIN]; };
+    auto ph_at = [&](int j) __attribute__((always_inline)) { return win_ph[j % WIN]; };
+    auto kr = [&](int t) __attribute__((always_inline)) { return t == 0 ? kR0 : t == 1 ? kR1 : t == 2 ? kR2 : kR3; };
+    auto vr = [&](int t) __attribute__((always_inline)) { return t == 0 ? vR0 : t == 1 ? vR1 : t == 2 ? vR2 : vR3; };
+    // prologue copies: K of pages 0, 1 and V of page 0 resident; K of pages 2, 3 and V of pages
+    // 1, 2 in flight (the copies of iterations -2 and -1)
+    if (!vrole) {
+      fill_all(plan(true, kb_at(0), ph_at(0), kR0));
+      fill_all(plan(n_iter > 1, kb_at(1), ph_at(1), kR1));
+    } else {
+      fill_all(plan(true, kb_at(0), ph_at(0), vR0));
+    }
+    barrier_keep_vm<0>();
+    fill_all(vrole ? plan(n_iter > 1, kb_at(1), ph_at(1), vR1) : plan(n_iter > 2, kb_at(2), ph_at(2), kR2));
+    const Fill fm1 = vrole ? plan(n_iter > 2, kb_at(2), ph_at(2), vR2) : plan(n_iter > 3, kb_at(3), ph_at(3), kR3);
+    if (n_vis > 0) {
+      qk(kR0, 0, sx, fm1, 0);
+      causal(sx, kb_at(0), 0);
+      float alpha;
+      reference(sx, alpha);   // the first reference; nothing to rescale yet
+      qk(kR0, 1, sy, fm1, NJ);
+      weights(sx, px0, px1);
+    } else {
+      fill_all(fm1);
+    }
+    asm volatile("s_barrier" ::: "memory");
+
+    // ids used by iteration i: pages i and i+1 (causal cut) and the page this wave copies
+    int kb_c0 = kb_at(0);
+    int kb_c1 = n_iter > 1 ? kb_at(1) : 0;
+    const int fo = vrole ? 3 : 4;   // iteration i copies page i + fo
+    int kb_f = n_iter > fo ? kb_at(fo) : 0;
+    int ph_f = n_iter > fo ? ph_at(fo) : -1;
+    // iteration i (R = i mod 4): units 2i+1 and 2i+2; K of page i+1 in tile (R+1)%4, V of page
+    // i in tile R; copies of K of page i+4 into tile R and of V of page i+3 into tile (R+3)%4
+    auto step = [&](auto Rc, const int i) __attribute__((always_inline)) {
+      constexpr int r = decltype(Rc)::value;
+      const Fill f = plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) % 4) : kr(r));
+      if ((i + 5) % CH == 0 && i + 5 < n_iter) {
+        load_chunk(i + 5);
+        __syncthreads();
+      }
+      const int nkb_c1 = i + 2 < n_iter ? kb_at(i + 2) : 0;
+      const int nkb_f = i + fo + 1 < n_iter ? kb_at(i + fo + 1) : 0;
+      const int nph_f = i + fo + 1 < n_iter ? ph_at(i + fo + 1) : -1;
+      unit(sy, kb_c0, 1, py0, py1, kr((r + 1) % 4), 0, sx, vr(r), 0, px0, px1, f, 0);
+      unit(sx, kb_c1, 0, px0, px1, kr((r + 1) % 4), 1, sy, vr(r), 1, py0, py1, f, NJ);
+      barrier_keep_vm<2 * GE::NPW>();
+      kb_c0 = kb_c1;
+      kb_c1 = nkb_c1;
+      kb_f = nkb_f;
+      ph_f = nph_f;
+    };
+    // copies and barrier only (the wave has no page i)
+    auto idle_step = [&](const int i) __attribute__((always_inline)) {
+      const int r = i & 3;
+      fill_all(plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r)));
+      if ((i + 5) % CH == 0 && i + 5 < n_iter) {
+        load_chunk(i + 5);
+        __syncthreads();
+      }
+      const int nkb_f = i + fo + 1 < n_iter ? kb_at(i + fo + 1) : 0;
+      const int nph_f = i + fo + 1 < n_iter ? ph_at(i + fo + 1) : -1;
+      barrier_keep_vm<2 * GE::NPW>();
+      kb_f = nkb_f;
+      ph_f = nph_f;
+    };
+
+    const int n_full = n_vis - 1;   // iterations in full
+    int i = 0;
+    for (; i + 4 <= n_full; i += 4) {
+      step(IC<0>{}, i);
+      step(IC<1>{}, i + 1);
+      step(IC<2>{}, i + 2);
+      step(IC<3>{}, i + 3);
+    }
+    if (i < n_full) {
+      step(IC<0>{}, i);
+      if (i + 1 < n_full) step(IC<1>{}, i + 1);
+      if (i + 2 < n_full) step(IC<2>{}, i + 2);
+      i = n_full;
+    }
+    if (n_vis > 0) {
+      // drain (iteration n_vis - 1): SM of its last unit, PV of its last two units
+      const int r = i & 3;
+      const Fill f = plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r));
+      fill_all(f);
+      if ((i + 5) % CH == 0 && i + 5 < n_iter) {
+        load_chunk(i + 5);
+        __syncthreads();
+      }
+      const int nkb_f = i + fo + 1 < n_iter ? kb_at(i + fo + 1) : 0;
+      const int nph_f = i + fo + 1 < n_iter ? ph_at(i + fo + 1) : -1;
+      causal(sy, kb_c0, 1);
+      float alpha;
+      const bool need = reference(sy, alpha);
+      weights(sy, py0, py1);
+      pv(vr(r), 0, px0, px1);
+      if (__builtin_amdgcn_ballot_w64(need)) rescale(alpha);
+      pv(vr(r), 1, py0, py1);
+      barrier_keep_vm<2 * GE::NPW>();
+      kb_f = nkb_f;
+      ph_f = nph_f;
+      ++i;
+    }
+    for (; i < n_iter; ++i) idle_step(i);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));  // idle copies into the sink have landed
   }
 
   // ---- epilogue ----------------------------------------------------------------------------
