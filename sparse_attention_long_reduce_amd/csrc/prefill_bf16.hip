@@ -16,8 +16,9 @@
 // direct-to-LDS loads (global_load_lds_dwordx4): every instruction moves 64 16-byte chunks,
 // one per lane, into 1 KiB of LDS, and each lane fetches whichever chunk belongs at its LDS
 // slot.  That makes the LDS layouts free to choose:
-//   K: chunk c of token row r is stored at chunk c ^ swz_k(r), so the 16 rows read together by
-//      one 16-byte MFMA-operand load hit 16 different bank groups;
+//   K: in MFMA operand order.  Slab (h, ks) (1 KiB) holds, at 16-byte slot l, key 32h + l % 32,
+//      chunk 2ks + l / 32: the operand of lane l for k-step ks of key half h.  Every operand
+//      load is then one contiguous, conflict-free 1 KiB read at an immediate offset;
 //   V: natural [token][d] rows with chunk c at c ^ swz_v(r); the PV operand (8 consecutive
 //      keys of one column per lane) is produced by two ds_read_b64_tr_b16 transposed reads,
 //      which the swizzle keeps free of bank conflicts.
@@ -74,15 +75,15 @@ struct Geo {
   static constexpr int KS = D / 16;     // k-steps of the QK product
 };
 
-// chunk position of K chunk c of row r is c ^ swz_k(r); of V chunk c is c ^ swz_v(r)
-template <int D>
-__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+// chunk position of V chunk c of row r is c ^ swz_v(r)
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// 16-byte direct-to-LDS copy: each lane's chunk at gsrc lands at ldst + 16 * lane
-__device__ __forceinline__ void lds_dma16(const __bf16* gsrc, __bf16* ldst) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)gsrc,
+// 16-byte direct-to-LDS copy: each lane's chunk at byte offset `off` from the wave-uniform
+// `base` lands at ldst + 16 * lane (a 32-bit offset keeps the base in scalar registers)
+__device__ __forceinline__ void lds_dma16(const __bf16* base, uint32_t off, __bf16* ldst) {
+  const char* g = reinterpret_cast<const char*>(base) + off;
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
 }
 
@@ -164,27 +165,39 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int row = row0 + l32;               // this lane's chunk row
   const bool row_ok = active && row < Cn;
   const __bf16* qsrc = reinterpret_cast<const __bf16*>(a.q) + ((size_t)(q0 + (row_ok ? row : 0)) * a.Hq + head) * D;
+  // Q is taken pre-multiplied by the softmax scale and log2(e) (rounded back to bf16), so that
+  // the scores come out of the MFMA in log2 units
+  const float cs = a.scale_log2;
   bf16x8 qb[GE::KS];
 #pragma unroll
   for (int ks = 0; ks < GE::KS; ++ks) {
     const uint4 u = row_ok ? *reinterpret_cast<const uint4*>(qsrc + 16 * ks + 8 * hl) : make_uint4(0, 0, 0, 0);
-    qb[ks] = __builtin_bit_cast(bf16x8, u);
+    const bf16x8 raw = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qb[ks][e] = (__bf16)((float)raw[e] * cs);
   }
 
   // ---- direct-to-LDS plan ------------------------------------------------------------------
-  // waves 0-3 move K, waves 4-7 move V; wave w's instruction j fills LDS chunks
-  // [(4w' + j) * 64, +64) of its tensor (w' = w % 4), lane l the chunk at position +l.
+  // waves 0-3 move K, waves 4-7 move V; wave w's instruction j fills the 1 KiB slab
+  // s = 4w' + j of its tensor (w' = w % 4), lane l the 16-byte slot l of that slab.
   const bool vrole = wave >= 4;
   const __bf16* const tg = vrole ? vg : kg;  // this wave's tensor of group g
-  int dma_off[GE::NPW];   // element offset of the lane's source chunk within a page
-  int dma_row[GE::NPW];
+  uint32_t dma_off[GE::NPW];   // byte offset of the lane's source chunk within a page
+  int dma_row[GE::NPW];        // its token row
 #pragma unroll
   for (int j = 0; j < GE::NPW; ++j) {
-    const int p = ((wave & 3) * GE::NPW + j) * 64 + lane;
-    const int r = p / GE::CPR;
-    const int c = (p % GE::CPR) ^ (vrole ? swz_v<D>(r) : swz_k<D>(r));
+    const int sl = (wave & 3) * GE::NPW + j;
+    int r, c;
+    if (vrole) {   // natural rows, swizzled chunks
+      const int p = sl * 64 + lane;
+      r = p / GE::CPR;
+      c = (p % GE::CPR) ^ swz_v<D>(r);
+    } else {       // operand order: slab (h, ks)
+      r = 32 * (sl / GE::KS) + l32;
+      c = 2 * (sl % GE::KS) + hl;
+    }
     dma_row[j] = r;
-    dma_off[j] = r * ts + c * 8;
+    dma_off[j] = (uint32_t)(r * ts + c * 8) * 2u;
   }
   const int dma_dst = (wave & 3) * GE::NPW * 64 * 8;  // elements; + j * 512
 
@@ -206,13 +219,14 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 #pragma unroll
     for (int j = 0; j < GE::NPW; ++j) {
       uint4 v = make_uint4(fv, fv, fv, fv);
-      if (ph >= 0 && dma_row[j] < nv_tok) v = *reinterpret_cast<const uint4*>(src + dma_off[j]);
+      if (ph >= 0 && dma_row[j] < nv_tok)
+        v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) + dma_off[j]);
       *reinterpret_cast<uint4*>(tile + dma_dst + j * 512 + lane * 8) = v;
     }
     return idle;
   };
   auto fill_one = [&](const Fill& f, int j) __attribute__((always_inline)) {
-    lds_dma16(f.src + dma_off[j], f.dst + j * 512);
+    lds_dma16(f.src, dma_off[j], f.dst + j * 512);
   };
   auto fill_all = [&](const Fill& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -234,9 +248,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   };
 
   // ---- per-lane LDS read offsets (elements) ---------------------------------------------------
-  // K operand: row l32 (+32 for keys 32-63), logical chunk 2*ks + hl
-  const int k_row_off = l32 * D;
-  const int k_sw = swz_k<D>(l32);
+  // K operand of k-step ks, key half h: slot `lane` of slab (h, ks)
+  const int k_lane_off = lane * 8;
   // V operand by transposed reads: source lane s = lane % 16 points at row +(s / 4), columns
   // 32*dt + 16*((lane / 16) & 1) + 4*(s % 4) .. +3
   const int s16 = lane & 15;
@@ -250,10 +263,17 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   for (int dt = 0; dt < GE::DT; ++dt) v_off[dt] = v_row_off + (((4 * dt + v_lo) ^ v_sw) << 3) + v_in;
 
   // ---- running softmax state and output accumulators ------------------------------------
-  const float cs = a.scale_log2;
+  // Scores are kept relative to the row's reference m_run (log2 units): the first MFMA of each
+  // QK product starts from cm = -m_run instead of 0, so a weight is exp2 of the score as it
+  // comes.  The reference is set from the first unit and moves (rarely) when a row maximum
+  // exceeds it by more than 2^8; the accumulators, the row sum and the scores taken against the
+  // old reference then follow.
   const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
-  float m_run = -INFINITY;   // reference maximum (log2 domain) the accumulators are scaled to
+  float m_run = 0.f;
   float l_run = 0.f;         // this lane's share of the row sum
+  f32x16 cm;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) cm[j] = 0.f;
   f32x16 o[GE::DT];
 #pragma unroll
   for (int dt = 0; dt < GE::DT; ++dt)
@@ -271,14 +291,13 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // QK: S^T = K Q^T for half h of the page in LDS tile Kl; copy instructions j0 .. j0+NJ-1 of f
   // go out in between
   constexpr int NJ = GE::NPW / 2 > 0 ? GE::NPW / 2 : 1;   // copy instructions per unit
-  auto qk = [&](const __bf16* Kl, int h, f32x16& s, const Fill& f, int j0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = 0.f;
+  auto qk = [&](const __bf16* Kl, int h, f32x16& s, const f32x16& c0, const Fill& f, int j0)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < GE::KS; ++ks) {
-      const int off = k_row_off + 32 * h * D + (((2 * ks + hl) ^ k_sw) << 3);
+      const int off = k_lane_off + (h * GE::KS + ks) * 512;
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kl + off);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], ks == 0 ? c0 : s, 0, 0, 0);
       if (ks % (GE::KS / NJ) == 0 && j0 + ks / (GE::KS / NJ) < GE::NPW) fill_one(f, j0 + ks / (GE::KS / NJ));
     }
   };
@@ -293,25 +312,31 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       }
     }
   };
-  // SM, row maximum and reference update; returns whether this lane moved its reference (the
-  // accumulators then take the factor alpha once PV of the previous unit is in)
-  auto reference = [&](const f32x16& s, float& alpha) __attribute__((always_inline)) {
-    float mx = fmaxf(s[0], s[1]);
+  // SM, row maximum of a unit's scores (over the 32 keys held by lanes l and l^32)
+  auto rowmax = [&](const f32x16& s) __attribute__((always_inline)) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int j = 2; j < 16; j += 2) mx = fmaxf(mx, fmaxf(s[j], s[j + 1]));
-    mx = xhalf_max(mx) * cs;
-    const bool need = mx > m_run + kRescaleThreshold;
-    alpha = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
-    m_run = need ? mx : m_run;
+    for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, s[j]), s[j + 1]);
+    return xhalf_max(fmaxf(mx, s[15]));
+  };
+  // SM, move the reference of the rows in which this unit's maximum mx exceeds it by more than
+  // the threshold: d = mx there, 0 elsewhere; the unit's scores, the row sum and cm follow at
+  // once, the accumulators (alpha = 2^-d) once PV of the previous unit is in
+  auto move_reference = [&](f32x16& s, float mx, float& d, float& alpha) __attribute__((always_inline)) {
+    d = mx > kRescaleThreshold ? mx : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s[j] -= d;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cm[j] -= d;
+    m_run += d;
+    alpha = __builtin_amdgcn_exp2f(-d);
     l_run *= alpha;
-    return need;
   };
   // SM, weights against the reference, rounded to bf16 as the PV operands, and row sums.
   //   key of operand u (0, 1), element e, lane half hl: 16*u + 8*(e / 4) + 4*hl + e % 4
   auto weights = [&](f32x16& s, bf16x8& p0, bf16x8& p1) __attribute__((always_inline)) {
-    const float ref = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(fmaf(s[j], cs, -ref));
+    for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(s[j]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       p0[e] = (__bf16)s[e];
@@ -352,15 +377,21 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
                   const __bf16* Vp, int hv, const bf16x8& pp0, const bf16x8& pp1,
                   const Fill& f, int j0) __attribute__((always_inline)) {
     causal(sm, kbs, hs);
-    float alpha;
-    const bool need = reference(sm, alpha);
-    qk(Kq, hq, sq, f, j0);
+    qk(Kq, hq, sq, cm, f, j0);
+    const float mx = rowmax(sm);
+    const bool moved = __builtin_amdgcn_ballot_w64(mx > kRescaleThreshold) != 0;
+    float d = 0.f, alpha = 1.f;
+    if (moved) move_reference(sm, mx, d, alpha);
     weights(sm, pc0, pc1);
     pv(Vp, hv, pp0, pp1);
     // the weights belong to this block: keep the compiler from sinking their computation past
-    // the rescale branch into the next unit
+    // the branch below into the next unit
     asm volatile("" ::"v"(pc0), "v"(pc1), "v"(l_run));
-    if (__builtin_amdgcn_ballot_w64(need)) rescale(alpha);
+    if (moved) {
+      rescale(alpha);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sq[j] -= d;   // taken against the old reference
+    }
   };
 
   // ---- page loop ---------------------------------------------------------------------------
@@ -389,11 +420,17 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     fill_all(vrole ? plan(n_iter > 1, kb_at(1), ph_at(1), vR1) : plan(n_iter > 2, kb_at(2), ph_at(2), kR2));
     const Fill fm1 = vrole ? plan(n_iter > 2, kb_at(2), ph_at(2), vR2) : plan(n_iter > 3, kb_at(3), ph_at(3), kR3);
     if (n_vis > 0) {
-      qk(kR0, 0, sx, fm1, 0);
+      qk(kR0, 0, sx, cm, fm1, 0);   // cm = 0: raw scores
       causal(sx, kb_at(0), 0);
-      float alpha;
-      reference(sx, alpha);   // the first reference; nothing to rescale yet
-      qk(kR0, 1, sy, fm1, NJ);
+      // the first reference: the row maximum of unit 0 (a key of it is visible to every row)
+      const float mx = rowmax(sx);
+      m_run = mx > -INFINITY ? mx : 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        sx[j] -= m_run;
+        cm[j] = -m_run;
+      }
+      qk(kR0, 1, sy, cm, fm1, NJ);
       weights(sx, px0, px1);
     } else {
       fill_all(fm1);
@@ -467,11 +504,13 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       const int nkb_f = i + fo + 1 < n_iter ? kb_at(i + fo + 1) : 0;
       const int nph_f = i + fo + 1 < n_iter ? ph_at(i + fo + 1) : -1;
       causal(sy, kb_c0, 1);
-      float alpha;
-      const bool need = reference(sy, alpha);
+      const float mx = rowmax(sy);
+      const bool moved = __builtin_amdgcn_ballot_w64(mx > kRescaleThreshold) != 0;
+      float d = 0.f, alpha = 1.f;
+      if (moved) move_reference(sy, mx, d, alpha);
       weights(sy, py0, py1);
       pv(vr(r), 0, px0, px1);
-      if (__builtin_amdgcn_ballot_w64(need)) rescale(alpha);
+      if (moved) rescale(alpha);
       pv(vr(r), 1, py0, py1);
       barrier_keep_vm<2 * GE::NPW>();
       kb_f = nkb_f;
