@@ -377,11 +377,13 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
                   const __bf16* Vp, int hv, const bf16x8& pp0, const bf16x8& pp1,
                   const Fill& f, int j0) __attribute__((always_inline)) {
     causal(sm, kbs, hs);
+    __builtin_amdgcn_s_setprio(1);
     qk(Kq, hq, sq, cm, f, j0);
     const float mx = rowmax(sm);
     const bool moved = __builtin_amdgcn_ballot_w64(mx > kRescaleThreshold) != 0;
     float d = 0.f, alpha = 1.f;
     if (moved) move_reference(sm, mx, d, alpha);
+    __builtin_amdgcn_s_setprio(0);
     weights(sm, pc0, pc1);
     pv(Vp, hv, pp0, pp1);
     // the weights belong to this block: keep the compiler from sinking their computation past
@@ -437,45 +439,50 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     }
     asm volatile("s_barrier" ::: "memory");
 
-    // ids used by iteration i: pages i and i+1 (causal cut) and the page this wave copies
-    int kb_c0 = kb_at(0);
-    int kb_c1 = n_iter > 1 ? kb_at(1) : 0;
+    // Ids used by iteration i: pages i and i+1 (causal cut) and page i + fo, the one this wave
+    // copies.  Those of iteration i+2 are read from the window during iteration i and held in
+    // registers, so the reads' latency is covered by the iteration's work.  Slots past the table
+    // hold stale ids; they are read but never used (every use is guarded by the page's range).
     const int fo = vrole ? 3 : 4;   // iteration i copies page i + fo
-    int kb_f = n_iter > fo ? kb_at(fo) : 0;
-    int ph_f = n_iter > fo ? ph_at(fo) : -1;
+    int vzero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+    int kb_c0 = kb_at(0), kb_c1 = kb_at(1), kb_c1n = kb_at(2);
+    int kb_f = kb_at(fo), ph_f = ph_at(fo), kb_fn = kb_at(fo + 1), ph_fn = ph_at(fo + 1);
+    // end of iteration i: resolve the next chunk of the window when entry i+6 (the furthest
+    // read below) starts one, read the ids of iteration i+2, shift the queue
+    auto advance = [&](const int i) __attribute__((always_inline)) {
+      if ((i + 6) % CH == 0 && i + 6 < n_iter) {
+        load_chunk(i + 6);
+        __syncthreads();
+      }
+      // the fresh ids stay in vector registers (the opaque zero in the slot index keeps the
+      // compiler from moving them to scalar registers, which would wait for the reads here);
+      // they move to scalar registers one iteration later, long after the reads completed
+      const int l_kb = kb_at(i + 3 + vzero), l_kbf = kb_at(i + 2 + fo + vzero), l_phf = ph_at(i + 2 + fo + vzero);
+      kb_c0 = kb_c1;
+      kb_c1 = __builtin_amdgcn_readfirstlane(kb_c1n);
+      kb_c1n = l_kb;
+      kb_f = __builtin_amdgcn_readfirstlane(kb_fn);
+      ph_f = __builtin_amdgcn_readfirstlane(ph_fn);
+      kb_fn = l_kbf;
+      ph_fn = l_phf;
+    };
     // iteration i (R = i mod 4): units 2i+1 and 2i+2; K of page i+1 in tile (R+1)%4, V of page
     // i in tile R; copies of K of page i+4 into tile R and of V of page i+3 into tile (R+3)%4
     auto step = [&](auto Rc, const int i) __attribute__((always_inline)) {
       constexpr int r = decltype(Rc)::value;
       const Fill f = plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) % 4) : kr(r));
-      if ((i + 5) % CH == 0 && i + 5 < n_iter) {
-        load_chunk(i + 5);
-        __syncthreads();
-      }
-      const int nkb_c1 = i + 2 < n_iter ? kb_at(i + 2) : 0;
-      const int nkb_f = i + fo + 1 < n_iter ? kb_at(i + fo + 1) : 0;
-      const int nph_f = i + fo + 1 < n_iter ? ph_at(i + fo + 1) : -1;
       unit(sy, kb_c0, 1, py0, py1, kr((r + 1) % 4), 0, sx, vr(r), 0, px0, px1, f, 0);
       unit(sx, kb_c1, 0, px0, px1, kr((r + 1) % 4), 1, sy, vr(r), 1, py0, py1, f, NJ);
       barrier_keep_vm<2 * GE::NPW>();
-      kb_c0 = kb_c1;
-      kb_c1 = nkb_c1;
-      kb_f = nkb_f;
-      ph_f = nph_f;
+      advance(i);
     };
     // copies and barrier only (the wave has no page i)
     auto idle_step = [&](const int i) __attribute__((always_inline)) {
       const int r = i & 3;
       fill_all(plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r)));
-      if ((i + 5) % CH == 0 && i + 5 < n_iter) {
-        load_chunk(i + 5);
-        __syncthreads();
-      }
-      const int nkb_f = i + fo + 1 < n_iter ? kb_at(i + fo + 1) : 0;
-      const int nph_f = i + fo + 1 < n_iter ? ph_at(i + fo + 1) : -1;
       barrier_keep_vm<2 * GE::NPW>();
-      kb_f = nkb_f;
-      ph_f = nph_f;
+      advance(i);
     };
 
     const int n_full = n_vis - 1;   // iterations in full
@@ -495,14 +502,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     if (n_vis > 0) {
       // drain (iteration n_vis - 1): SM of its last unit, PV of its last two units
       const int r = i & 3;
-      const Fill f = plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r));
-      fill_all(f);
-      if ((i + 5) % CH == 0 && i + 5 < n_iter) {
-        load_chunk(i + 5);
-        __syncthreads();
-      }
-      const int nkb_f = i + fo + 1 < n_iter ? kb_at(i + fo + 1) : 0;
-      const int nph_f = i + fo + 1 < n_iter ? ph_at(i + fo + 1) : -1;
+      fill_all(plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r)));
       causal(sy, kb_c0, 1);
       const float mx = rowmax(sy);
       const bool moved = __builtin_amdgcn_ballot_w64(mx > kRescaleThreshold) != 0;
@@ -513,8 +513,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       if (moved) rescale(alpha);
       pv(vr(r), 1, py0, py1);
       barrier_keep_vm<2 * GE::NPW>();
-      kb_f = nkb_f;
-      ph_f = nph_f;
+      advance(i);
       ++i;
     }
     for (; i < n_iter; ++i) idle_step(i);
