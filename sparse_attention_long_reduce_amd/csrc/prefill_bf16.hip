@@ -59,6 +59,8 @@ namespace cpa {
 namespace {
 
 constexpr int THREADS = 512;
+// a lane's 16 weights of one unit may sum to this before the reference must move (2^30)
+constexpr float kSumLimit = 1073741824.0f;
 constexpr int WIN = 1024;  // circular window of resolved page ids
 constexpr int CH = 512;    // ids resolved at a time
 
@@ -332,21 +334,25 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     alpha = __builtin_amdgcn_exp2f(-d);
     l_run *= alpha;
   };
-  // SM, weights against the reference, rounded to bf16 as the PV operands, and row sums.
+  // SM, weights of scores s (left as they are) against the reference, rounded to bf16 as the PV
+  // operands; returns this lane's sum of them.
   //   key of operand u (0, 1), element e, lane half hl: 16*u + 8*(e / 4) + 4*hl + e % 4
-  auto weights = [&](f32x16& s, bf16x8& p0, bf16x8& p1) __attribute__((always_inline)) {
+  auto weights = [&](const f32x16& s, bf16x8& p0, bf16x8& p1) __attribute__((always_inline)) {
+    float w[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = __builtin_amdgcn_exp2f(s[j]);
+    for (int j = 0; j < 16; ++j) w[j] = __builtin_amdgcn_exp2f(s[j]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p0[e] = (__bf16)s[e];
-      p1[e] = (__bf16)s[8 + e];
+      p0[e] = (__bf16)w[e];
+      p1[e] = (__bf16)w[8 + e];
     }
+    float lu = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[e], p0[e + 1]}, kOnes2, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[e], p1[e + 1]}, kOnes2, l_run, false);
+      lu = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[e], p0[e + 1]}, kOnes2, lu, false);
+      lu = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[e], p1[e + 1]}, kOnes2, lu, false);
     }
+    return lu;
   };
   // PV: O^T += V^T P^T for half h of the page in LDS tile Vl
   auto pv = [&](const __bf16* Vl, int h, const bf16x8& p0, const bf16x8& p1) __attribute__((always_inline)) {
@@ -371,29 +377,32 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   };
   // One unit: SM of the scores in sm (half hs of page kbs) into weights pc0/pc1, QK of half hq
   // of the page in tile Kq into sq, PV of half hv of the page in tile Vp with weights pp0/pp1.
-  // Apart from the causal cut (on the last pages only) and the rescale, it is one basic block,
-  // so that the scheduler can interleave the three stages.
+  // Apart from the causal cut (on the last pages only) and the reference move, it is one basic
+  // block, so that the scheduler can interleave the three stages.  The weights are taken against
+  // the current reference without looking at the unit's maximum first: a lane whose 16 weights
+  // sum to kSumLimit or more (a weight of 2^26 or more), or to inf or NaN, sends the wave down the
+  // rare branch, which moves the reference to the row maximum and takes the weights again.
   auto unit = [&](f32x16& sm, int kbs, int hs, bf16x8& pc0, bf16x8& pc1, const __bf16* Kq, int hq, f32x16& sq,
                   const __bf16* Vp, int hv, const bf16x8& pp0, const bf16x8& pp1,
                   const Fill& f, int j0) __attribute__((always_inline)) {
     causal(sm, kbs, hs);
     __builtin_amdgcn_s_setprio(1);
     qk(Kq, hq, sq, cm, f, j0);
-    const float mx = rowmax(sm);
-    const bool moved = __builtin_amdgcn_ballot_w64(mx > kRescaleThreshold) != 0;
-    float d = 0.f, alpha = 1.f;
-    if (moved) move_reference(sm, mx, d, alpha);
     __builtin_amdgcn_s_setprio(0);
-    weights(sm, pc0, pc1);
+    float lu = weights(sm, pc0, pc1);
     pv(Vp, hv, pp0, pp1);
     // the weights belong to this block: keep the compiler from sinking their computation past
     // the branch below into the next unit
-    asm volatile("" ::"v"(pc0), "v"(pc1), "v"(l_run));
-    if (moved) {
-      rescale(alpha);
+    asm volatile("" ::"v"(pc0), "v"(pc1), "v"(lu));
+    if (__builtin_amdgcn_ballot_w64(!(lu < kSumLimit))) {
+      float d, alpha;
+      move_reference(sm, rowmax(sm), d, alpha);
+      lu = weights(sm, pc0, pc1);
+      rescale(alpha);                            // PV of the previous unit is in
 #pragma unroll
       for (int j = 0; j < 16; ++j) sq[j] -= d;   // taken against the old reference
     }
+    l_run += lu;
   };
 
   // ---- page loop ---------------------------------------------------------------------------
@@ -433,7 +442,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
         cm[j] = -m_run;
       }
       qk(kR0, 1, sy, cm, fm1, NJ);
-      weights(sx, px0, px1);
+      l_run = weights(sx, px0, px1);
     } else {
       fill_all(fm1);
     }
@@ -504,11 +513,14 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       const int r = i & 3;
       fill_all(plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r)));
       causal(sy, kb_c0, 1);
-      const float mx = rowmax(sy);
-      const bool moved = __builtin_amdgcn_ballot_w64(mx > kRescaleThreshold) != 0;
+      float lu = weights(sy, py0, py1);
+      const bool moved = __builtin_amdgcn_ballot_w64(!(lu < kSumLimit)) != 0;
       float d = 0.f, alpha = 1.f;
-      if (moved) move_reference(sy, mx, d, alpha);
-      weights(sy, py0, py1);
+      if (moved) {
+        move_reference(sy, rowmax(sy), d, alpha);
+        lu = weights(sy, py0, py1);
+      }
+      l_run += lu;
       pv(vr(r), 0, px0, px1);
       if (moved) rescale(alpha);
       pv(vr(r), 1, py0, py1);
