@@ -7,8 +7,10 @@ attention-layer shape (32 query heads, 8 KV heads, head dim 128), bf16, structur
 block masks (vertical stripes, slash diagonals, Bernoulli noise, sink block and a 4-block local
 window), K/V in a randomly permuted paged pool.  Other workloads: --workload c2 (32K context),
 c4 (the full chunked prefill of one 131072-token sequence: 64 chunks of 2048, one step = all 64
-chunks in order), c5a / c5b (varlen batch of four sequences, last 4096-token chunks).  All
-inputs are seeded synthetic data resident in HBM before the timed region.
+chunks in order), c5a / c5b (varlen batch of four sequences, last 4096-token chunks), c3s (one KV
+group's share of the 128K workload, too few tiles for the GPU: run with split-KV, the unsplit
+time reported beside it).  All inputs are seeded synthetic data resident in HBM before the timed
+region.
 
 Prints one JSON line: selected-block attention TFLOP/s of the whole step, the speedup over the
 same kernels run with all-ones masks (dense), the roofline of the dominant kernel (prefill,
@@ -38,6 +40,9 @@ WORKLOADS = {
             "d 128, bf16, group-shared stripes 0.1"),
     "c5b": ("c5b_varlen_independent", "varlen 4 x last 4096 of {8K,32K,64K,128K}, Hq 32 / Hkv 8 / "
             "d 128, bf16, per-head stripes 0.1"),
+    "c3s": ("c3s_128k_one_group", "one KV group's share of the 128K last chunk (the per-GPU share of "
+            "an 8-way head split): prefix 129024 + chunk 2048, Hq 4 / Hkv 1 / d 128, bf16, "
+            "structured masks, split-KV"),
 }
 
 
@@ -111,8 +116,9 @@ def cpu_baseline(w, T, C, max_seconds=15.0):
 class Batch:
     """One launch pair (table build + prefill) with its inputs resident on the device."""
 
-    def __init__(self, w, dev, kp=None, vp=None):
+    def __init__(self, w, dev, kp=None, vp=None, split=False):
         import torch
+        import sparse_attention_long_reduce_amd as cpa
         bf = torch.bfloat16
         self.w = w
         self.masks = torch.from_numpy(w.masks).to(dev)
@@ -131,6 +137,13 @@ class Batch:
         self.counts_dense = torch.empty_like(self.counts)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((self.q.shape[0], w.Hq), dtype=torch.float32, device=dev)
+        self.split_pages = 0
+        self.workspace = None
+        if split:
+            n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+            self.split_pages = cpa.plan_split_pages(w.B, w.Hq, w.Hkv, w.max_chunk_len, w.nkvb_max, n_cus)
+            need = cpa.split_workspace_bytes(self.q.shape[0], w.Hq, w.d, w.nkvb_max, self.split_pages)
+            self.workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def build(self, cpa, dense):
         if dense:
@@ -143,7 +156,8 @@ class Batch:
     def prefill(self, cpa, dense):
         t, c = (self.tables_dense, self.counts_dense) if dense else (self.tables, self.counts)
         cpa.chunked_prefill(self.q, self.kp, self.vp, self.pm, t, c, self.cu, self.pl,
-                            self.w.max_chunk_len, out=self.out, lse=self.lse)
+                            self.w.max_chunk_len, out=self.out, lse=self.lse,
+                            split_pages=self.split_pages, workspace=self.workspace)
 
     def flops(self, cpa, dense=False):
         w = self.w
@@ -157,7 +171,7 @@ def make_batches(key, dev):
     from workloads.configs import chunked_sequence_chunk
     name, _ = WORKLOADS[key]
     if key != "c4":
-        return [Batch(make_config(name), dev)]
+        return [Batch(make_config(name), dev, split=(key == "c3s"))]
     batches = []
     kp = vp = None
     for k in range(64):
@@ -256,6 +270,16 @@ def main():
         dflops = sum(bt.flops(cpa, dense=True) for bt in batches)
         log(f"[bench] dense: step {d['step_ms']:.3f} ms, prefill {d['prefill_ms']:.3f} ms")
 
+    unsplit = None
+    if any(bt.split_pages for bt in batches):
+        saved = [bt.split_pages for bt in batches]
+        for bt in batches:
+            bt.split_pages = 0
+        unsplit = timed(cpa, batches, (False,), max(5, args.steps // 2), 2)[0]
+        for bt, sp in zip(batches, saved):
+            bt.split_pages = sp
+        log(f"[bench] unsplit: prefill {unsplit['prefill_ms']:.3f} ms (split pages {saved[0]})")
+
     w0 = batches[-1].w
     step_tflops = flops / (r["step_ms"] * 1e-3) / 1e12
     pre_tflops = flops / (r["prefill_ms"] * 1e-3) / 1e12
@@ -297,6 +321,10 @@ def main():
                            "flop": int(dflops), "prefill_tflops": round(dflops / (d["prefill_ms"] * 1e-3) / 1e12, 2)}
         result["speedup_vs_dense"] = {"kernel": round(d["prefill_ms"] / r["prefill_ms"], 4),
                                       "end_to_end": round(d["step_ms"] / r["step_ms"], 4)}
+    if unsplit is not None:
+        result["split_kv"] = {"split_pages": batches[0].split_pages,
+                              "unsplit_prefill_ms": round(unsplit["prefill_ms"], 4),
+                              "speedup_over_unsplit": round(unsplit["prefill_ms"] / r["prefill_ms"], 4)}
     result["pages_context"] = ("CompactAttention reports up to 2.72x attention speedup at 128K on "
                                "LLaMA-3.1-8B-Instruct (hardware not stated); context only")
     if not args.no_cpu_baseline:

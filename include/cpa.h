@@ -123,6 +123,46 @@ cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pag
                                int max_chunk_len, float sm_scale, void* o, float* lse,
                                hipStream_t stream);
 
+/*
+ * cpa_chunked_prefill_split - cpa_chunked_prefill with each (group, query tile) cut along its
+ * table into ranges of split_pages pages (split-KV), for calls with too few tiles to fill the
+ * GPU or with tables of very different lengths.
+ *
+ * Each range is run by its own workgroup, which writes the normalised partial output of its
+ * rows and their LSE over that range into `workspace`.  A second kernel then combines the
+ * ranges of each row, O = sum_s e^(lse_s - LSE) O_s with LSE = log sum_s e^lse_s, and writes
+ * o and lse.  The result equals cpa_chunked_prefill's up to rounding (the partials are fp32).
+ * Softmax over the union of a partition of the keys is the LSE-weighted merge of the softmaxes
+ * over the parts; the CompactAttention abstract's per-group tables are unchanged.
+ *
+ * Arguments as cpa_chunked_prefill, plus:
+ *   total_q     rows of all sequences (Tq = cu_q[B]); sizes the workspace rows.
+ *   split_pages pages per range, >= 1.  n_splits = ceil(table_cap / split_pages) ranges per tile;
+ *               with n_splits == 1 this is cpa_chunked_prefill and the workspace is unused.
+ *   workspace   device memory owned by the caller, 16-byte aligned, at least
+ *               cpa_split_workspace_bytes(total_q, Hq, d, table_cap, split_pages) bytes; its
+ *               contents on entry do not matter and on return are unspecified.  Calls that use
+ *               the same workspace must not overlap.
+ * Supported: dtype CPA_BF16 with token_stride <= 2^24 elements (else CPA_ERR_UNSUPPORTED
+ * when n_splits > 1).  Errors: those of cpa_chunked_prefill, CPA_ERR_SHAPE (split_pages < 1,
+ * total_q < 0), CPA_ERR_NULL (no workspace), CPA_ERR_ALIGN, CPA_ERR_CAPACITY (workspace too
+ * small).
+ */
+cpa_status cpa_chunked_prefill_split(const void* q, cpa_dtype dtype, const void* k_pages,
+                                     const void* v_pages, int64_t page_stride, int64_t head_stride,
+                                     int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                                     int page_map_stride, const int32_t* tables, int table_cap,
+                                     const int32_t* counts, const int32_t* cu_q,
+                                     const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                                     int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     int total_q, int split_pages, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace cpa_chunked_prefill_split needs (0 when it needs none, or for
+ * non-positive arguments): ceil(table_cap / split_pages) * total_q * Hq * (d + 1) * 4 when
+ * that split count exceeds 1. */
+size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int split_pages);
+
 /* Static, NUL-terminated description of a status code (host pointer, never NULL). */
 const char* cpa_status_string(cpa_status s);
 

@@ -4,7 +4,8 @@ Two entry points, both thin wrappers over the C ABI in include/cpa.h:
 
 * build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv) -> (tables, counts)
 * chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len,
-                  max_chunk_len) -> (o, lse)
+                  max_chunk_len, split_pages=0) -> (o, lse)
+  (split_pages > 0: split-KV over page ranges with an LSE merge; plan_split_pages picks one)
 
 The library must be built first (``python -m sparse_attention_long_reduce_amd.build``); nothing
 here falls back to another implementation.
@@ -14,6 +15,9 @@ from .api import (  # noqa: F401
     attention_flops,
     build_block_tables,
     chunked_prefill,
+    plan_split_pages,
+    prefill_tiles,
+    split_workspace_bytes,
     status_string,
     version,
 )

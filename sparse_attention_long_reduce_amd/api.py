@@ -57,13 +57,42 @@ def build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv, table_cap=None, 
     return tables, counts
 
 
+def prefill_tiles(B, Hq, Hkv, max_chunk_len):
+    """Workgroups cpa_chunked_prefill launches without split-KV (one per group and query tile):
+    a tile is the group's heads (up to 4 per workgroup) times 1, 2 or 4 query blocks."""
+    G = Hq // Hkv
+    hpw = min(G, 4)
+    qpw = 4 // hpw
+    nqb = -(-int(max_chunk_len) // BLOCK)
+    return B * Hkv * -(-nqb // qpw) * (G // hpw)
+
+
+def plan_split_pages(B, Hq, Hkv, max_chunk_len, table_cap, n_cus, max_splits=16):
+    """Pages per split-KV range so that the tiles times their ranges cover every CU once when the
+    tiles alone would leave CUs idle; 0 (no split) when there are at least as many tiles as CUs."""
+    tiles = prefill_tiles(B, Hq, Hkv, max_chunk_len)
+    if tiles == 0 or tiles >= n_cus or table_cap <= 1:
+        return 0
+    splits = min(max_splits, -(-n_cus // tiles), table_cap)
+    return -(-table_cap // splits) if splits > 1 else 0
+
+
+def split_workspace_bytes(total_q, Hq, d, table_cap, split_pages):
+    return int(load().cpa_split_workspace_bytes(int(total_q), int(Hq), int(d), int(table_cap), int(split_pages)))
+
+
 def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len,
-                    sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None):
+                    sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None, split_pages=0,
+                    workspace=None):
     """Attention of each sequence's chunk over its group's table blocks, K/V read in place.
 
     q [Tq][Hq][d]; k_pages / v_pages [n_pages][Hkv][64][d] (or any strided view with d
     contiguous); page_map int32 [B][stride]; tables int32 [B][Hkv][cap]; counts int32 [B][Hkv];
     cu_q int32 [B+1]; prefix_len int32 [B]; max_chunk_len host int.  Returns (o, lse-or-None).
+
+    split_pages > 0 runs split-KV (cpa_chunked_prefill_split) with ranges of that many pages;
+    the workspace (a CUDA uint8 tensor of split_workspace_bytes(...) bytes) is allocated here
+    when not given.
     """
     if q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("q, k_pages and v_pages must share dtype float32 or bfloat16")
@@ -90,11 +119,22 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
-    st = load().cpa_chunked_prefill(
-        _ptr(q), _DTYPES[q.dtype], _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1),
-        k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
-        _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
-        _ptr(lse), _stream(stream))
+    args = (_ptr(q), _DTYPES[q.dtype], _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1),
+            k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
+            _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
+            _ptr(lse))
+    if split_pages and split_pages > 0:
+        need = split_workspace_bytes(Tq, Hq, d, cap, split_pages)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        if not workspace.is_cuda:
+            raise TypeError("workspace must be a CUDA tensor")
+        st = load().cpa_chunked_prefill_split(*args, Tq, int(split_pages), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(), _stream(stream))
+        if st != 0:
+            raise CpaError(st, "cpa_chunked_prefill_split")
+        return out, lse
+    st = load().cpa_chunked_prefill(*args, _stream(stream))
     if st != 0:
         raise CpaError(st, "cpa_chunked_prefill")
     return out, lse

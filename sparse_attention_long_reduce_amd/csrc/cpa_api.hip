@@ -10,6 +10,67 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
+extern "C" size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int split_pages);
+
+namespace {
+// Checks the arguments of a prefill call and fills the launch arguments (no HIP call).
+// *nothing: the call has no work (B == 0 or max_chunk_len == 0).
+cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
+                           const void* v_pages, int64_t page_stride, int64_t head_stride,
+                           int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                           int page_map_stride, const int32_t* tables, int table_cap,
+                           const int32_t* counts, const int32_t* cu_q,
+                           const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                           int max_chunk_len, float sm_scale, void* o, float* lse,
+                           cpa::PrefillArgs& a, bool* nothing) {
+  *nothing = false;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || table_cap < 0 || n_pages < 0)
+    return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (!(sm_scale >= 0.f) || std::isinf(sm_scale)) return CPA_ERR_SHAPE;
+  if (dtype != CPA_F32 && dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (!(G == 1 || G == 2 || G == 4 || (G % 4 == 0 && G <= 32))) return CPA_ERR_UNSUPPORTED;
+  if (B == 0 || max_chunk_len == 0) {
+    *nothing = true;
+    return CPA_OK;
+  }
+  if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
+    return CPA_ERR_SHAPE;
+  if (!q || !k_pages || !v_pages || !page_map || !counts || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
+  if (table_cap > 0 && !tables) return CPA_ERR_NULL;
+  const int eb = dtype == CPA_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return CPA_ERR_ALIGN;
+  if ((token_stride * eb) % 16 || (head_stride * eb) % 16 || (page_stride * eb) % 16) return CPA_ERR_ALIGN;
+
+  a = cpa::PrefillArgs{};
+  a.q = q; a.k = k_pages; a.v = v_pages;
+  a.page_stride = page_stride; a.head_stride = head_stride; a.token_stride = token_stride;
+  a.n_pages = n_pages;
+  a.page_map = page_map; a.page_map_stride = page_map_stride;
+  a.tables = tables; a.table_cap = table_cap; a.counts = counts;
+  a.cu_q = cu_q; a.prefix_len = prefix_len;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_chunk_len = max_chunk_len;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt((float)d);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o = o; a.lse = lse;
+  a.G = G;
+  a.hpw = G >= 4 ? 4 : G;
+  a.qpw = 4 / a.hpw;
+  a.hsplit = G / a.hpw;
+  const int nqb_max = (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK;
+  a.n_qtiles = (nqb_max + a.qpw - 1) / a.qpw;
+  a.tiles_per_group = a.n_qtiles * a.hsplit;
+  a.n_groups = B * Hkv;
+  a.xcd_remap = a.n_groups >= 8 ? 1 : 0;
+  a.n_splits = 1;
+  return CPA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* cpa_status_string(cpa_status s) {
@@ -19,7 +80,7 @@ const char* cpa_status_string(cpa_status s) {
     case CPA_ERR_SHAPE: return "invalid or inconsistent size";
     case CPA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case CPA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or group size";
-    case CPA_ERR_CAPACITY: return "table capacity smaller than the KV-block count";
+    case CPA_ERR_CAPACITY: return "table capacity smaller than the KV-block count, or workspace too small";
     case CPA_ERR_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";
@@ -51,45 +112,55 @@ cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pag
                                const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
                                int max_chunk_len, float sm_scale, void* o, float* lse,
                                hipStream_t stream) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || table_cap < 0 || n_pages < 0)
-    return CPA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
-  if (!(sm_scale >= 0.f) || std::isinf(sm_scale)) return CPA_ERR_SHAPE;
-  if (dtype != CPA_F32 && dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
-  const int G = Hq / Hkv;
-  if (!(G == 1 || G == 2 || G == 4 || (G % 4 == 0 && G <= 32))) return CPA_ERR_UNSUPPORTED;
-  if (B == 0 || max_chunk_len == 0) return CPA_OK;
-  if (page_map_stride < 1) return CPA_ERR_SHAPE;
-  if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
-    return CPA_ERR_SHAPE;
-  if (!q || !k_pages || !v_pages || !page_map || !counts || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
-  if (table_cap > 0 && !tables) return CPA_ERR_NULL;
-  const int eb = dtype == CPA_BF16 ? 2 : 4;
-  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return CPA_ERR_ALIGN;
-  if ((token_stride * eb) % 16 || (head_stride * eb) % 16 || (page_stride * eb) % 16) return CPA_ERR_ALIGN;
-
-  cpa::PrefillArgs a{};
-  a.q = q; a.k = k_pages; a.v = v_pages;
-  a.page_stride = page_stride; a.head_stride = head_stride; a.token_stride = token_stride;
-  a.n_pages = n_pages;
-  a.page_map = page_map; a.page_map_stride = page_map_stride;
-  a.tables = tables; a.table_cap = table_cap; a.counts = counts;
-  a.cu_q = cu_q; a.prefix_len = prefix_len;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_chunk_len = max_chunk_len;
-  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt((float)d);
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.o = o; a.lse = lse;
-  a.G = G;
-  a.hpw = G >= 4 ? 4 : G;
-  a.qpw = 4 / a.hpw;
-  a.hsplit = G / a.hpw;
-  const int nqb_max = (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK;
-  a.n_qtiles = (nqb_max + a.qpw - 1) / a.qpw;
-  a.tiles_per_group = a.n_qtiles * a.hsplit;
-  a.n_groups = B * Hkv;
-  a.xcd_remap = a.n_groups >= 8 ? 1 : 0;
+  cpa::PrefillArgs a;
+  bool nothing;
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride,
+                                        n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
+                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
+  if (st != CPA_OK || nothing) return st;
   return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int split_pages) {
+  if (total_q <= 0 || Hq <= 0 || d <= 0 || table_cap <= 0 || split_pages <= 0) return 0;
+  const size_t n_splits = ((size_t)table_cap + split_pages - 1) / split_pages;
+  if (n_splits <= 1) return 0;
+  return n_splits * (size_t)total_q * (size_t)Hq * (size_t)(d + 1) * sizeof(float);
+}
+
+cpa_status cpa_chunked_prefill_split(const void* q, cpa_dtype dtype, const void* k_pages,
+                                     const void* v_pages, int64_t page_stride, int64_t head_stride,
+                                     int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                                     int page_map_stride, const int32_t* tables, int table_cap,
+                                     const int32_t* counts, const int32_t* cu_q,
+                                     const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                                     int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     int total_q, int split_pages, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  if (split_pages <= 0 || total_q < 0) return CPA_ERR_SHAPE;
+  cpa::PrefillArgs a;
+  bool nothing;
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride,
+                                        n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
+                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
+  if (st != CPA_OK || nothing) return st;
+  const int n_splits = (table_cap + split_pages - 1) / split_pages;
+  if (n_splits <= 1)   // one range: the plain path
+    return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+  if (dtype != CPA_BF16 || token_stride > (1 << 24)) return CPA_ERR_UNSUPPORTED;
+  if (total_q == 0) return CPA_OK;
+  const size_t need = cpa_split_workspace_bytes(total_q, Hq, d, table_cap, split_pages);
+  if (workspace == nullptr) return CPA_ERR_NULL;
+  if (!aligned16(workspace)) return CPA_ERR_ALIGN;
+  if (workspace_bytes < need) return CPA_ERR_CAPACITY;
+  a.n_splits = n_splits;
+  a.split_pages = split_pages;
+  a.total_q = total_q;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + (size_t)n_splits * total_q * Hq * d;
+  if (cpa::launch_prefill(a, true, d, stream) != hipSuccess) return CPA_ERR_LAUNCH;
+  cpa::MergeArgs m{a.part_o, a.part_lse, n_splits, total_q, Hq, o, lse};
+  return cpa::launch_split_merge(m, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -40,11 +40,29 @@ struct PrefillArgs {
   int tiles_per_group;  // n_qtiles * hsplit
   int n_groups;         // B * Hkv
   int xcd_remap;        // 1: keep each KV group's tiles on one XCD (see the prefill kernel)
+  // split-KV: each tile's table is cut into n_splits ranges of split_pages pages; range s of a
+  // tile writes its rows' normalised partial output (fp32 part_o[s][row][head][d]) and LSE
+  // (part_lse[s][row][head], natural log) instead of o / lse.  n_splits == 1: no split.
+  int n_splits;
+  int split_pages;
+  int total_q;          // rows of all sequences (the partials' row dimension)
+  float* part_o;
+  float* part_lse;
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  int n_splits, total_q, Hq;
+  void* o;       // bf16 [total_q][Hq][d]
+  float* lse;    // optional [total_q][Hq]
 };
 
 // Both return hipSuccess or the launch error; they never synchronise.
 hipError_t launch_block_union(const UnionArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
+// combines the split-KV partials (bf16 output)
+hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s);
 // register-staged variant (V transposed through registers); serves fp32 and is kept for bf16
 // as the reference point of the direct-to-LDS bf16 kernel
 hipError_t launch_prefill_regstaged(const PrefillArgs& a, bool bf16, int d, hipStream_t s);

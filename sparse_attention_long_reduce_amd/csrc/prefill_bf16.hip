@@ -130,8 +130,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int l32 = lane & 31;
   const int hl = lane >> 5;  // lane half
 
-  int gi, rank;
-  if (!decode_tile(a, lane, gi, rank)) return;
+  int gi, rank, split;
+  if (!decode_tile(a, lane, gi, rank, split)) return;
   const int b = gi / a.Hkv;
   const int g = gi - b * a.Hkv;
   const int hsub = rank % a.hsplit;
@@ -154,8 +154,15 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 
   const int cnt = min(max(a.counts[gi], 0), a.table_cap);
   const int32_t* tab = a.tables + (size_t)gi * a.table_cap;
-  const int n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
-  const int n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
+  int n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
+  int n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
+  if (a.n_splits > 1) {   // this workgroup's range of the tile's pages
+    const int lo = split * a.split_pages;
+    const int hi = min(n_iter, lo + a.split_pages);
+    tab += lo;
+    n_vis = max(0, min(n_vis, hi) - lo);
+    n_iter = max(0, hi - lo);
+  }
 
   const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(a.k) + (size_t)g * a.head_stride;
   const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(a.v) + (size_t)g * a.head_stride;
@@ -536,6 +543,21 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   if (!row_ok) return;
   const float lt = xhalf_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (a.n_splits > 1) {   // normalised partial output and LSE of this range, fp32
+    if (q0 + row >= a.total_q) return;   // rows past total_q (inconsistent cu_q) have no slot
+    const size_t rh = (size_t)split * a.total_q * a.Hq + (size_t)(q0 + row) * a.Hq + head;
+    float* pdst = a.part_o + rh * D;
+#pragma unroll
+    for (int dt = 0; dt < GE::DT; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv, o[dt][4 * q + 2] * inv,
+                                     o[dt][4 * q + 3] * inv);
+        *reinterpret_cast<float4*>(pdst + 32 * dt + 8 * q + 4 * hl) = v;
+      }
+    if (hl == 0) a.part_lse[rh] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
+    return;
+  }
   __bf16* dst = reinterpret_cast<__bf16*>(a.o) + ((size_t)(q0 + row) * a.Hq + head) * D;
 #pragma unroll
   for (int dt = 0; dt < GE::DT; ++dt) {
@@ -551,6 +573,38 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     a.lse[(size_t)(q0 + row) * a.Hq + head] = lt > 0.f ? (m_run + __log2f(lt)) * kLn2 : -INFINITY;
 }
 
+// Split-KV merge: one wave per (row, head) combines the n_splits normalised partials by their
+// LSEs, O = sum_s e^(lse_s - LSE) O_s with LSE = log sum_s e^lse_s (empty ranges have
+// lse = -inf and weigh nothing), and writes the bf16 output and the LSE.
+template <int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(const MergeArgs m) {
+  constexpr int PL = D / 64;   // values per lane
+  const size_t rh = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const size_t n_rh = (size_t)m.total_q * m.Hq;
+  if (rh >= n_rh) return;
+  const int lane = threadIdx.x & 63;
+  float mx = -INFINITY;
+  for (int s = 0; s < m.n_splits; ++s) mx = fmaxf(mx, m.part_lse[s * n_rh + rh]);
+  float acc[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) acc[e] = 0.f;
+  float sum = 0.f;
+  if (mx > -INFINITY) {
+    for (int s = 0; s < m.n_splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f((m.part_lse[s * n_rh + rh] - mx) * 1.4426950408889634f);
+      sum += w;
+      const float* src = m.part_o + (s * n_rh + rh) * D + lane * PL;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc[e] += w * src[e];
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  __bf16* dst = reinterpret_cast<__bf16*>(m.o) + rh * D + lane * PL;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) dst[e] = (__bf16)(acc[e] * inv);
+  if (m.lse != nullptr && lane == 0) m.lse[rh] = sum > 0.f ? mx + __logf(sum) : -INFINITY;
+}
+
 template <int D>
 hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const int grid = prefill_grid(a);
@@ -560,6 +614,15 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
+  const size_t n_rh = (size_t)m.total_q * m.Hq;
+  if (n_rh == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n_rh + 3) / 4));
+  if (d == 64) hipLaunchKernelGGL((split_merge_kernel<64>), grid, dim3(256), 0, s, m);
+  else hipLaunchKernelGGL((split_merge_kernel<128>), grid, dim3(256), 0, s, m);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
   if (!bf16) return launch_prefill_regstaged(a, false, d, s);

@@ -47,36 +47,42 @@ __device__ __forceinline__ int weight_rank(const PrefillArgs& a, int xcd, int ng
   return r;
 }
 
-// Workgroup -> (KV group index gi = b*Hkv + g, tile rank).  Workgroups are dispatched
+// Workgroup -> (KV group index gi = b*Hkv + g, tile rank, split).  Workgroups are dispatched
 // round-robin over the 8 XCDs (blockIdx % 8) and, within an XCD, in blockIdx order as CUs free
 // up.  With xcd_remap every tile of one KV group lands on the same XCD, so the group's pages
 // are shared through that XCD's L2.  Work is handed out longest first: the groups of an XCD in
 // decreasing table length (a tile visits about as many pages as its group's table holds), and
-// within a group the tiles of rank 0 (the last query blocks, which see the most pages) first.
-// Beyond 64 groups per XCD the groups go in index order.  Returns false for padding.
-__device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int lane, int& gi, int& rank) {
+// within a group the tiles of rank 0 (the last query blocks, which see the most pages) first,
+// the split ranges of one tile next to each other.  Beyond 64 groups per XCD the groups go in
+// index order.  Returns false for padding.
+__device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int lane, int& gi, int& rank, int& split) {
+  const int per_group = a.tiles_per_group * a.n_splits;   // work items of one KV group
+  int w;
   if (a.xcd_remap) {
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
     const int ngx = (a.n_groups - xcd + 7) >> 3;  // groups gi with gi % 8 == xcd
-    if (slot >= ngx * a.tiles_per_group) return false;
-    int k = slot / a.tiles_per_group;
-    rank = slot - k * a.tiles_per_group;
+    if (slot >= ngx * per_group) return false;
+    int k = slot / per_group;
+    w = slot - k * per_group;
     if (ngx <= 64) {
       const uint64_t hit = __builtin_amdgcn_ballot_w64(weight_rank(a, xcd, ngx, lane) == k);
       k = __builtin_ctzll(hit);
     }
     gi = xcd + 8 * k;
   } else {
-    if ((int)blockIdx.x >= a.n_groups * a.tiles_per_group) return false;
+    if ((int)blockIdx.x >= a.n_groups * per_group) return false;
     gi = blockIdx.x % a.n_groups;
-    rank = blockIdx.x / a.n_groups;
+    w = blockIdx.x / a.n_groups;
   }
+  rank = w / a.n_splits;
+  split = w - rank * a.n_splits;
   return true;
 }
 
 inline int prefill_grid(const PrefillArgs& a) {
-  return a.xcd_remap ? 8 * ((a.n_groups + 7) / 8) * a.tiles_per_group : a.n_groups * a.tiles_per_group;
+  const int per_group = a.tiles_per_group * a.n_splits;
+  return a.xcd_remap ? 8 * ((a.n_groups + 7) / 8) * per_group : a.n_groups * per_group;
 }
 
 }  // namespace cpa

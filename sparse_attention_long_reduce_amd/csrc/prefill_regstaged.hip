@@ -89,8 +89,8 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   const int hl = lane >> 5;  // lane half
 
   // ---- tile decode ---------------------------------------------------------------------
-  int gi, rank;
-  if (!decode_tile(a, lane, gi, rank)) return;
+  int gi, rank, split;   // split-KV is not taken on this path (n_splits == 1)
+  if (!decode_tile(a, lane, gi, rank, split)) return;
   const int b = gi / a.Hkv;
   const int g = gi - b * a.Hkv;
   const int hsub = rank % a.hsplit;

@@ -27,7 +27,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"cpa_build_block_tables", "cpa_chunked_prefill", "cpa_status_string", "cpa_version"}
+    assert set(names) == {"cpa_build_block_tables", "cpa_chunked_prefill", "cpa_chunked_prefill_split",
+                          "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -92,6 +93,47 @@ def test_prefill_validation(lib):
     assert pf(lib, ts=132, hs=64 * 132, ps=8 * 64 * 132) == 3    # bf16 row of 264 B
     assert pf(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
     assert pf(lib, mcl=0, q=NULL) == 0
+
+
+def pfs(lib, dtype=1, total_q=256, split=4, ws=FAKE, ws_bytes=1 << 30, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
+             tab=FAKE, cap=16, cnt=FAKE, cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0,
+             o=FAKE, lse=NULL)
+    a.update(kw)
+    return lib.cpa_chunked_prefill_split(a["q"], dtype, a["k"], a["v"], a["ps"], a["hs"], a["ts"], a["npages"],
+                                         a["pm"], a["pms"], a["tab"], a["cap"], a["cnt"], a["cu"], a["pl"],
+                                         a["B"], a["Hq"], a["Hkv"], a["d"], a["mcl"], a["scale"], a["o"],
+                                         a["lse"], total_q, split, ws, ws_bytes, None)
+
+
+def test_split_validation(lib):
+    assert pfs(lib, split=0) == 2
+    assert pfs(lib, total_q=-1) == 2
+    assert pfs(lib, d=96) == 4                 # the checks of cpa_chunked_prefill come first
+    assert pfs(lib, q=NULL) == 1
+    assert pfs(lib, dtype=0) == 4              # fp32 has no split path (4 ranges of 4 pages)
+    assert pfs(lib, ts=1 << 25, hs=64 << 25, ps=8 * (64 << 25)) == 4   # too wide for the split path
+    assert pfs(lib, ws=NULL) == 1
+    assert pfs(lib, ws=FAKE + 4) == 3
+    need = lib.cpa_split_workspace_bytes(256, 32, 128, 16, 4)
+    assert need == 4 * 256 * 32 * 129 * 4
+    assert pfs(lib, ws_bytes=need - 1) == 5
+    assert pfs(lib, B=0, q=NULL) == 0
+    assert lib.cpa_split_workspace_bytes(256, 32, 128, 16, 16) == 0   # one range: no workspace
+    assert lib.cpa_split_workspace_bytes(0, 32, 128, 16, 4) == 0
+
+
+def test_split_planner():
+    # one KV group of a 128K context (4 query heads, 2048-row chunk): 32 tiles on 256 CUs
+    assert cpa.prefill_tiles(1, 4, 1, 2048) == 32
+    assert cpa.plan_split_pages(1, 4, 1, 2048, 2048, 256) == 256
+    # the whole layer (32 heads, 8 groups) already has a tile per CU
+    assert cpa.prefill_tiles(1, 32, 8, 2048) == 256
+    assert cpa.plan_split_pages(1, 32, 8, 2048, 2048, 256) == 0
+    # G = 1 packs 4 query blocks, G = 8 splits the heads in two
+    assert cpa.prefill_tiles(2, 8, 8, 300) == 2 * 8 * 2 * 1
+    assert cpa.prefill_tiles(1, 16, 2, 128) == 1 * 2 * 2 * 2
+    assert cpa.plan_split_pages(1, 4, 1, 64, 1, 256) == 0
 
 
 def test_python_layer_rejects_cpu_tensors():

@@ -79,8 +79,11 @@ def test_small_tables_and_prefill(name):
     fin = np.isfinite(Lr)
     assert np.array_equal(np.isfinite(lg), fin)
     if fin.any():
-        # bf16 path: the row sum adds the bf16-rounded weights (relative rounding <= 2^-9 each)
-        tol = 2 ** -8 if w.dtype == "bf16" else 1e-4
+        # bf16 path: the row sum adds the bf16-rounded weights (relative rounding <= 2^-9 each,
+        # <= 2^-9 on the LSE), and Q is rounded to bf16 after the softmax scale is folded in,
+        # which moves a score by 2^-9/sqrt(3) * scale * |q.k|_2 ~ 1.1e-3 RMS at d = 128 with
+        # N(0,1) inputs; a row dominated by one key carries that into the LSE (5 sigma 5.7e-3)
+        tol = 2 ** -7 if w.dtype == "bf16" else 1e-4
         assert np.max(np.abs(lg[fin] - Lr[fin])) < tol
     if name == "all_zero_bf16":
         assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
