@@ -5,9 +5,10 @@
 // query heads of one GQA group yields the minimal per-group KV block table that keeps every
 // selected block.  The table holds logical KV-block ids in ascending order.
 //
-// One workgroup of 256 threads per (sequence, KV group).
+// One workgroup of 1024 threads per (sequence, KV group).
 //   phase 1  OR-reduce the group's G * nqb mask rows, 16 KV blocks (one 16-byte load) per
-//            thread and row, with the causal clip kb <= prefix_blocks + qi applied per row;
+//            thread and row, four rows' loads in flight per thread, with the causal clip
+//            kb <= prefix_blocks + qi applied per row;
 //            partial ORs of threads that share a column meet in LDS; each 16-block column
 //            becomes 16 bits of a 64-bit word in LDS.
 //   phase 2  popcount per word, exclusive scan over words in LDS, then each wave expands
@@ -19,7 +20,7 @@
 namespace cpa {
 namespace {
 
-constexpr int UT = 256;               // threads per workgroup
+constexpr int UT = 1024;              // threads per workgroup
 constexpr int MAX_WORDS = 65536 / 64;  // 64-bit words for the largest supported KV extent
 
 // 0x80 in every byte of x that is nonzero
@@ -82,11 +83,12 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
       const int kb0 = c << 4;
       const int qi_lo = max(0, kb0 - qb0);  // first query block that can reach column kb0
       const int nq = nqb - qi_lo;
-      for (int t = s; t < G * nq; t += rsplit) {
+      // mask bytes of row t (head t / nq of the group, query block qi_lo + t % nq) at column
+      // kb0, causally clipped
+      auto row = [&](int t, uint32_t v[4]) __attribute__((always_inline)) {
         const int hh = t / nq;
         const int qi = qi_lo + (t - hh * nq);
         const uint8_t* rowp = gbase + ((size_t)hh * a.nqb_max + qi) * row_stride + kb0;
-        uint32_t v[4];
         if (VEC) {
           const uint4 x = *reinterpret_cast<const uint4*>(rowp);
           v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
@@ -112,8 +114,23 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
             v[w] &= m;
           }
         }
+      };
+      const int nrows = G * nq;
+      for (int t0 = s; t0 < nrows; t0 += 4 * rsplit) {
+        uint32_t v[4][4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[w] |= v[w];
+        for (int u = 0; u < 4; ++u) {
+          const int t = t0 + u * rsplit;
+          if (t < nrows) {
+            row(t, v[u]);
+          } else {
+            v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0u;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[w] |= v[u][w];
       }
     }
     red[tid] = make_uint4(acc[0], acc[1], acc[2], acc[3]);

@@ -109,7 +109,7 @@ __device__ __forceinline__ void barrier_keep_vm() {
 template <int I>
 using IC = std::integral_constant<int, I>;
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
   using GE = Geo<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 kR0[GE::PAGE];
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int32_t* tab = a.tables + (size_t)gi * a.table_cap;
   int n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
   int n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
-  if (a.n_splits > 1) {   // this workgroup's range of the tile's pages
+  if (SPLIT) {   // this workgroup's range of the tile's pages
     const int lo = split * a.split_pages;
     const int hi = min(n_iter, lo + a.split_pages);
     tab += lo;
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   if (!row_ok) return;
   const float lt = xhalf_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (a.n_splits > 1) {   // normalised partial output and LSE of this range, fp32
+  if (SPLIT) {   // normalised partial output and LSE of this range, fp32
     if (q0 + row >= a.total_q) return;   // rows past total_q (inconsistent cu_q) have no slot
     const size_t rh = (size_t)split * a.total_q * a.Hq + (size_t)(q0 + row) * a.Hq + head;
     float* pdst = a.part_o + rh * D;
@@ -609,7 +609,10 @@ template <int D>
 hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const int grid = prefill_grid(a);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3(grid), dim3(THREADS), 0, s, a);
+  if (a.n_splits > 1)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3(grid), dim3(THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3(grid), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
 
