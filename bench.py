@@ -58,15 +58,15 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_key):
+def read_traffic(workload_key, v_layout):
     """HBM bytes per prefill launch from the committed rocprofv3 counter summary, or None when
-    the summary is absent or was taken on a different kernel source."""
+    the summary is absent, covers the other V layout or was taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", f"prefill_{workload_key}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_source_hash():
+    if t.get("kernel_sha") != kernel_source_hash() or t.get("v_layout", "token") != v_layout:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -139,6 +139,8 @@ class Batch:
         self.lse = torch.empty((self.q.shape[0], w.Hq), dtype=torch.float32, device=dev)
         self.split_pages = 0
         self.workspace = None
+        self.v_layout = "token"
+        self.vp_dim = None         # dim-major copy of the V pool ([page][group][d][64])
         if split:
             n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
             self.split_pages = cpa.plan_split_pages(w.B, w.Hq, w.Hkv, w.max_chunk_len, w.nkvb_max, n_cus)
@@ -155,9 +157,10 @@ class Batch:
 
     def prefill(self, cpa, dense):
         t, c = (self.tables_dense, self.counts_dense) if dense else (self.tables, self.counts)
-        cpa.chunked_prefill(self.q, self.kp, self.vp, self.pm, t, c, self.cu, self.pl,
+        dim = self.v_layout == "dim"
+        cpa.chunked_prefill(self.q, self.kp, self.vp_dim if dim else self.vp, self.pm, t, c, self.cu, self.pl,
                             self.w.max_chunk_len, out=self.out, lse=self.lse,
-                            split_pages=self.split_pages, workspace=self.workspace)
+                            split_pages=self.split_pages, workspace=self.workspace, v_layout=self.v_layout)
 
     def flops(self, cpa, dense=False):
         w = self.w
@@ -166,19 +169,26 @@ class Batch:
                                    w.chunk_len, w.Hq, w.Hkv, w.d)
 
 
-def make_batches(key, dev):
+def make_batches(key, dev, v_layouts):
     from workloads import make_config
     from workloads.configs import chunked_sequence_chunk
     name, _ = WORKLOADS[key]
     if key != "c4":
-        return [Batch(make_config(name), dev, split=(key == "c3s"))]
-    batches = []
-    kp = vp = None
-    for k in range(64):
-        w = chunked_sequence_chunk(k)
-        bt = Batch(w, dev, kp, vp)
-        kp, vp = bt.kp, bt.vp     # one paged pool shared by all chunks of the sequence
-        batches.append(bt)
+        batches = [Batch(make_config(name), dev, split=(key == "c3s"))]
+    else:
+        batches = []
+        kp = vp = None
+        for k in range(64):
+            w = chunked_sequence_chunk(k)
+            bt = Batch(w, dev, kp, vp)
+            kp, vp = bt.kp, bt.vp     # one paged pool shared by all chunks of the sequence
+            batches.append(bt)
+    if "dim" in v_layouts:
+        vp_dim = batches[0].vp.transpose(2, 3).contiguous()   # the same values, dim-major pages
+        for bt in batches:
+            bt.vp_dim = vp_dim
+    for bt in batches:
+        bt.v_layout = v_layouts[0]
     return batches
 
 
@@ -226,6 +236,11 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--v-layout", default="dim", choices=("dim", "token"),
+                    help="V pool pages dim-major [page][group][d][64] or token-major [page][group][64][d] "
+                         "(K pages are token-major)")
+    ap.add_argument("--no-layout-ab", action="store_true",
+                    help="skip the timing of the other V layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB three times (the reference "
                          "kernel that scales the HBM byte counters)")
@@ -252,7 +267,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.perf_counter()
-    batches = make_batches(args.workload, dev)
+    other = "token" if args.v_layout == "dim" else "dim"
+    batches = make_batches(args.workload, dev, (args.v_layout,) if args.no_layout_ab else (args.v_layout, other))
     torch.cuda.synchronize()
     log(f"[bench] {name}: {len(batches)} launch pair(s) per step, inputs resident on the GPU "
         f"({time.perf_counter() - t0:.1f} s)")
@@ -280,7 +296,19 @@ def main():
             bt.split_pages = sp
         log(f"[bench] unsplit: prefill {unsplit['prefill_ms']:.3f} ms (split pages {saved[0]})")
 
+    layout_ab = None
+    if not args.no_layout_ab:
+        for bt in batches:
+            bt.v_layout = other
+        alt = timed(cpa, batches, (False,), max(5, args.steps // 2), 2)[0]
+        for bt in batches:
+            bt.v_layout = args.v_layout
+        again = timed(cpa, batches, (False,), max(5, args.steps // 2), 2)[0]
+        layout_ab = {args.v_layout: round(again["prefill_ms"], 4), other: round(alt["prefill_ms"], 4)}
+        log(f"[bench] V layout A/B prefill ms: {layout_ab}")
+
     w0 = batches[-1].w
+    bt0 = batches[0]
     step_tflops = flops / (r["step_ms"] * 1e-3) / 1e12
     pre_tflops = flops / (r["prefill_ms"] * 1e-3) / 1e12
     mask_bytes = sum(int(bt.w.masks.nbytes) for bt in batches)
@@ -301,7 +329,10 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, synthetic block masks, permuted paged KV pool)",
         "config": {"workload": desc, "sequences": int(w0.B), "chunk_len": int(w0.max_chunk_len),
                    "context": context, "Hq": w0.Hq, "Hkv": w0.Hkv, "head_dim": w0.d, "block": 64,
-                   "launch_pairs_per_step": len(batches)},
+                   "launch_pairs_per_step": len(batches),
+                   "kv_layout": "K pages token-major [page][group][64][d], V pages "
+                                + ("dim-major [page][group][d][64]" if args.v_layout == "dim"
+                                   else "token-major [page][group][64][d]")},
         "selected_flop": int(flops),
         "union_blocks": union,
         "prefill_tflops": round(pre_tflops, 2),
@@ -309,7 +340,9 @@ def main():
         "table_build_us": round(r["build_ms"] * 1e3, 2),
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": read_traffic(args.workload), "kernel": "prefill_bf16_kernel<128>"},
+                     "traffic": read_traffic(args.workload, args.v_layout),
+                     "kernel": f"prefill_bf16_kernel<128, {'true' if bt0.split_pages else 'false'}, "
+                               f"{'true' if args.v_layout == 'dim' else 'false'}>"},
         "table_build_roofline": {
             "bound": "hbm", "achieved": round((mask_bytes + tab_bytes) / (r["build_ms"] * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -321,6 +354,8 @@ def main():
                            "flop": int(dflops), "prefill_tflops": round(dflops / (d["prefill_ms"] * 1e-3) / 1e12, 2)}
         result["speedup_vs_dense"] = {"kernel": round(d["prefill_ms"] / r["prefill_ms"], 4),
                                       "end_to_end": round(d["step_ms"] / r["step_ms"], 4)}
+    if layout_ab is not None:
+        result["v_layout_prefill_ms"] = layout_ab
     if unsplit is not None:
         result["split_kv"] = {"split_pages": batches[0].split_pages,
                               "unsplit_prefill_ms": round(unsplit["prefill_ms"], 4),

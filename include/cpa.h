@@ -163,6 +163,38 @@ cpa_status cpa_chunked_prefill_split(const void* q, cpa_dtype dtype, const void*
  * that split count exceeds 1. */
 size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int split_pages);
 
+/*
+ * cpa_chunked_prefill_vt - cpa_chunked_prefill (split_pages <= 0) or cpa_chunked_prefill_split
+ * (split_pages >= 1) for a V pool whose pages are stored dim-major: within a page and group the
+ * d rows hold 64 consecutive tokens each, the layout [n_pages][Hkv][d][64] by default.  The K
+ * pool keeps the token-major layout of cpa_chunked_prefill.  The result is the same attention
+ * (CompactAttention abstract: every query head of the group over exactly its table's blocks,
+ * read in place from the paged cache).  It equals cpa_chunked_prefill's on the same values up
+ * to rounding: the keys of each 16-key MFMA step are summed in another order.
+ *
+ * Why: the PV product contracts over tokens, so its V operand is 8 consecutive tokens of one
+ * column.  Dim-major pages hold those in one 16-byte chunk, which the kernel stages in LDS in
+ * operand order and reads at full LDS width, instead of building each operand from two
+ * half-width transposed reads.  A cache writer that stores V this way pays nothing extra.
+ *
+ * Arguments as cpa_chunked_prefill_split, except that V is described by its own strides
+ * (elements): V(page, group, token, dim) at v_pages + page * v_page_stride +
+ * group * v_head_stride + dim * v_dim_stride + token.  Requires v_dim_stride >= 64,
+ * v_head_stride >= d * v_dim_stride, v_page_stride >= Hkv * v_head_stride (else CPA_ERR_SHAPE),
+ * all three 16-byte multiples (else CPA_ERR_ALIGN).  total_q, workspace and workspace_bytes are
+ * used only when split_pages >= 1 (see cpa_chunked_prefill_split; a split also needs
+ * v_dim_stride <= 2^24, else CPA_ERR_UNSUPPORTED).
+ */
+cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                                  int64_t head_stride, int64_t token_stride, const void* v_pages,
+                                  int64_t v_page_stride, int64_t v_head_stride, int64_t v_dim_stride,
+                                  int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                                  const int32_t* tables, int table_cap, const int32_t* counts,
+                                  const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv,
+                                  int d, int max_chunk_len, float sm_scale, void* o, float* lse, int total_q,
+                                  int split_pages, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (host pointer, never NULL). */
 const char* cpa_status_string(cpa_status s);
 

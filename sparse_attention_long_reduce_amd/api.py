@@ -83,16 +83,18 @@ def split_workspace_bytes(total_q, Hq, d, table_cap, split_pages):
 
 def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len,
                     sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None, split_pages=0,
-                    workspace=None):
+                    workspace=None, v_layout="token"):
     """Attention of each sequence's chunk over its group's table blocks, K/V read in place.
 
-    q [Tq][Hq][d]; k_pages / v_pages [n_pages][Hkv][64][d] (or any strided view with d
-    contiguous); page_map int32 [B][stride]; tables int32 [B][Hkv][cap]; counts int32 [B][Hkv];
-    cu_q int32 [B+1]; prefix_len int32 [B]; max_chunk_len host int.  Returns (o, lse-or-None).
+    q [Tq][Hq][d]; k_pages [n_pages][Hkv][64][d] (or any strided view with d contiguous);
+    v_pages the same (v_layout "token") or dim-major [n_pages][Hkv][d][64] (v_layout "dim", any
+    strided view with the token dimension contiguous); page_map int32 [B][stride]; tables int32
+    [B][Hkv][cap]; counts int32 [B][Hkv]; cu_q int32 [B+1]; prefix_len int32 [B]; max_chunk_len
+    host int.  Returns (o, lse-or-None).
 
     split_pages > 0 runs split-KV (cpa_chunked_prefill_split) with ranges of that many pages;
     the workspace (a CUDA uint8 tensor of split_workspace_bytes(...) bytes) is allocated here
-    when not given.
+    when not given.  v_layout "dim" calls cpa_chunked_prefill_vt.
     """
     if q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("q, k_pages and v_pages must share dtype float32 or bfloat16")
@@ -101,8 +103,15 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     Tq, Hq, d = q.shape
     if k_pages.dim() != 4 or k_pages.shape[2] != BLOCK or k_pages.shape[3] != d:
         raise ValueError("k_pages must be [n_pages][Hkv][64][d]")
-    if v_pages.shape != k_pages.shape or v_pages.stride() != k_pages.stride():
-        raise ValueError("v_pages must match k_pages in shape and strides")
+    if v_layout == "token":
+        if v_pages.shape != k_pages.shape or v_pages.stride() != k_pages.stride():
+            raise ValueError("v_pages must match k_pages in shape and strides")
+    elif v_layout == "dim":
+        n_p, h_p = k_pages.shape[0], k_pages.shape[1]
+        if v_pages.dim() != 4 or tuple(v_pages.shape) != (n_p, h_p, d, BLOCK) or v_pages.stride(3) != 1:
+            raise ValueError("dim-major v_pages must be [n_pages][Hkv][d][64] with the token dimension contiguous")
+    else:
+        raise ValueError("v_layout must be 'token' or 'dim'")
     if k_pages.stride(3) != 1:
         raise ValueError("the head dimension of the pages must be contiguous")
     n_pages, Hkv = k_pages.shape[0], k_pages.shape[1]
@@ -123,12 +132,25 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
             k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
             _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
             _ptr(lse))
-    if split_pages and split_pages > 0:
+    split = bool(split_pages and split_pages > 0)
+    if split:
         need = split_workspace_bytes(Tq, Hq, d, cap, split_pages)
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         if not workspace.is_cuda:
             raise TypeError("workspace must be a CUDA tensor")
+    if v_layout == "dim":
+        st = load().cpa_chunked_prefill_vt(
+            _ptr(q), _DTYPES[q.dtype], _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
+            _ptr(v_pages), v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map),
+            page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
+            int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq, int(split_pages) if split else 0,
+            _ptr(workspace) if split else None,
+            workspace.numel() * workspace.element_size() if split else 0, _stream(stream))
+        if st != 0:
+            raise CpaError(st, "cpa_chunked_prefill_vt")
+        return out, lse
+    if split:
         st = load().cpa_chunked_prefill_split(*args, Tq, int(split_pages), _ptr(workspace),
                                               workspace.numel() * workspace.element_size(), _stream(stream))
         if st != 0:

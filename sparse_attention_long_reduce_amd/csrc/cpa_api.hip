@@ -13,11 +13,18 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 extern "C" size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int split_pages);
 
 namespace {
+// V pool description: strides in elements; v_row_stride is the token stride of token-major
+// pages (dim contiguous) or the dim stride of dim-major pages (tokens contiguous)
+struct VLayout {
+  int64_t page_stride, head_stride, row_stride;
+  bool dmajor;
+};
+
 // Checks the arguments of a prefill call and fills the launch arguments (no HIP call).
 // *nothing: the call has no work (B == 0 or max_chunk_len == 0).
 cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
                            const void* v_pages, int64_t page_stride, int64_t head_stride,
-                           int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                           int64_t token_stride, const VLayout& vl, int64_t n_pages, const int32_t* page_map,
                            int page_map_stride, const int32_t* tables, int table_cap,
                            const int32_t* counts, const int32_t* cu_q,
                            const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
@@ -39,15 +46,22 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   if (page_map_stride < 1) return CPA_ERR_SHAPE;
   if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
     return CPA_ERR_SHAPE;
+  const int64_t v_rows = vl.dmajor ? d : 64, v_row_len = vl.dmajor ? 64 : d;
+  if (vl.row_stride < v_row_len || vl.head_stride < v_rows * vl.row_stride ||
+      vl.page_stride < (int64_t)Hkv * vl.head_stride)
+    return CPA_ERR_SHAPE;
   if (!q || !k_pages || !v_pages || !page_map || !counts || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
   if (table_cap > 0 && !tables) return CPA_ERR_NULL;
   const int eb = dtype == CPA_BF16 ? 2 : 4;
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return CPA_ERR_ALIGN;
   if ((token_stride * eb) % 16 || (head_stride * eb) % 16 || (page_stride * eb) % 16) return CPA_ERR_ALIGN;
+  if ((vl.row_stride * eb) % 16 || (vl.head_stride * eb) % 16 || (vl.page_stride * eb) % 16) return CPA_ERR_ALIGN;
 
   a = cpa::PrefillArgs{};
   a.q = q; a.k = k_pages; a.v = v_pages;
   a.page_stride = page_stride; a.head_stride = head_stride; a.token_stride = token_stride;
+  a.v_page_stride = vl.page_stride; a.v_head_stride = vl.head_stride; a.v_row_stride = vl.row_stride;
+  a.v_dmajor = vl.dmajor ? 1 : 0;
   a.n_pages = n_pages;
   a.page_map = page_map; a.page_map_stride = page_map_stride;
   a.tables = tables; a.table_cap = table_cap; a.counts = counts;
@@ -114,7 +128,8 @@ cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pag
                                hipStream_t stream) {
   cpa::PrefillArgs a;
   bool nothing;
-  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride,
+  const VLayout vl{page_stride, head_stride, token_stride, false};
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
                                         n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
                                         prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
   if (st != CPA_OK || nothing) return st;
@@ -128,26 +143,28 @@ size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int 
   return n_splits * (size_t)total_q * (size_t)Hq * (size_t)(d + 1) * sizeof(float);
 }
 
-cpa_status cpa_chunked_prefill_split(const void* q, cpa_dtype dtype, const void* k_pages,
-                                     const void* v_pages, int64_t page_stride, int64_t head_stride,
-                                     int64_t token_stride, int64_t n_pages, const int32_t* page_map,
-                                     int page_map_stride, const int32_t* tables, int table_cap,
-                                     const int32_t* counts, const int32_t* cu_q,
-                                     const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
-                                     int max_chunk_len, float sm_scale, void* o, float* lse,
-                                     int total_q, int split_pages, void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// the split-KV call for either V layout (split_pages >= 1)
+cpa_status prefill_split(const void* q, cpa_dtype dtype, const void* k_pages, const void* v_pages,
+                         int64_t page_stride, int64_t head_stride, int64_t token_stride, const VLayout& vl,
+                         int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                         const int32_t* tables, int table_cap, const int32_t* counts, const int32_t* cu_q,
+                         const int32_t* prefix_len, int B, int Hq, int Hkv, int d, int max_chunk_len,
+                         float sm_scale, void* o, float* lse, int total_q, int split_pages, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
   if (split_pages <= 0 || total_q < 0) return CPA_ERR_SHAPE;
   cpa::PrefillArgs a;
   bool nothing;
-  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride,
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
                                         n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
                                         prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
   if (st != CPA_OK || nothing) return st;
   const int n_splits = (table_cap + split_pages - 1) / split_pages;
   if (n_splits <= 1)   // one range: the plain path
     return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
-  if (dtype != CPA_BF16 || token_stride > (1 << 24)) return CPA_ERR_UNSUPPORTED;
+  if (dtype != CPA_BF16 || token_stride > (1 << 24) || vl.row_stride > (1 << 24)) return CPA_ERR_UNSUPPORTED;
   if (total_q == 0) return CPA_OK;
   const size_t need = cpa_split_workspace_bytes(total_q, Hq, d, table_cap, split_pages);
   if (workspace == nullptr) return CPA_ERR_NULL;
@@ -161,6 +178,49 @@ cpa_status cpa_chunked_prefill_split(const void* q, cpa_dtype dtype, const void*
   if (cpa::launch_prefill(a, true, d, stream) != hipSuccess) return CPA_ERR_LAUNCH;
   cpa::MergeArgs m{a.part_o, a.part_lse, n_splits, total_q, Hq, o, lse};
   return cpa::launch_split_merge(m, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" {
+
+cpa_status cpa_chunked_prefill_split(const void* q, cpa_dtype dtype, const void* k_pages,
+                                     const void* v_pages, int64_t page_stride, int64_t head_stride,
+                                     int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                                     int page_map_stride, const int32_t* tables, int table_cap,
+                                     const int32_t* counts, const int32_t* cu_q,
+                                     const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                                     int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     int total_q, int split_pages, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  const VLayout vl{page_stride, head_stride, token_stride, false};
+  return prefill_split(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl, n_pages, page_map,
+                       page_map_stride, tables, table_cap, counts, cu_q, prefix_len, B, Hq, Hkv, d, max_chunk_len,
+                       sm_scale, o, lse, total_q, split_pages, workspace, workspace_bytes, stream);
+}
+
+cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                                  int64_t head_stride, int64_t token_stride, const void* v_pages,
+                                  int64_t v_page_stride, int64_t v_head_stride, int64_t v_dim_stride,
+                                  int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                                  const int32_t* tables, int table_cap, const int32_t* counts,
+                                  const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv,
+                                  int d, int max_chunk_len, float sm_scale, void* o, float* lse, int total_q,
+                                  int split_pages, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  const VLayout vl{v_page_stride, v_head_stride, v_dim_stride, true};
+  if (split_pages > 0)
+    return prefill_split(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl, n_pages,
+                         page_map, page_map_stride, tables, table_cap, counts, cu_q, prefix_len, B, Hq, Hkv, d,
+                         max_chunk_len, sm_scale, o, lse, total_q, split_pages, workspace, workspace_bytes,
+                         stream);
+  if (total_q < 0) return CPA_ERR_SHAPE;
+  cpa::PrefillArgs a;
+  bool nothing;
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
+                                        n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
+                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
+  if (st != CPA_OK || nothing) return st;
+  return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
 }  // extern "C"

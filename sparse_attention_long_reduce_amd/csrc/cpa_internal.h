@@ -19,7 +19,12 @@ struct PrefillArgs {
   const void* q;
   const void* k;
   const void* v;
-  int64_t page_stride, head_stride, token_stride, n_pages;  // elements / pages
+  int64_t page_stride, head_stride, token_stride, n_pages;  // elements / pages (K; V unless below)
+  // V pool: element (page, group, token, dim) at page * v_page_stride + group * v_head_stride +
+  // token * v_row_stride + dim (v_dmajor == 0, token-major pages) or + dim * v_row_stride + token
+  // (v_dmajor == 1, dim-major pages)
+  int64_t v_page_stride, v_head_stride, v_row_stride;
+  int v_dmajor;
   const int32_t* page_map;
   int page_map_stride;
   const int32_t* tables;

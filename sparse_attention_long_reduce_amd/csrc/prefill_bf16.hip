@@ -18,10 +18,17 @@
 // slot.  That makes the LDS layouts free to choose:
 //   K: in MFMA operand order.  Slab (h, ks) (1 KiB) holds, at 16-byte slot l, key 32h + l % 32,
 //      chunk 2ks + l / 32: the operand of lane l for k-step ks of key half h.  Every operand
-//      load is then one contiguous, conflict-free 1 KiB read at an immediate offset;
-//   V: natural [token][d] rows with chunk c at c ^ swz_v(r); the PV operand (8 consecutive
-//      keys of one column per lane) is produced by two ds_read_b64_tr_b16 transposed reads,
-//      which the swizzle keeps free of bank conflicts.
+//      load is then one contiguous, conflict-free 1 KiB read at an immediate offset.  With
+//      dim-major V the keys of a slab are permuted (key_perm), see below;
+//   V: the PV operand of lane l is 8 consecutive keys of one output column.  A pool of
+//      token-major pages ([token][d], d contiguous) is staged as natural rows with chunk c at
+//      c ^ swz_v(r), and each operand is built by two ds_read_b64_tr_b16 transposed reads,
+//      which the swizzle keeps free of bank conflicts.  A pool of dim-major pages ([d][token],
+//      tokens contiguous) holds those 8 keys in one 16-byte chunk, so it is staged in operand
+//      order like K: slab (h, u, dt) holds, at slot l, column 32dt + l % 32, keys
+//      32h + 16u + 8(l / 32) .. +7, and each operand is one ds_read_b128.  The transposed read
+//      delivers half the bytes per LDS cycle of ds_read_b128, so the dim-major layout halves
+//      the LDS time of the V operands.
 // No staging registers and no LDS stores are needed.  Waves 0-3 copy K, waves 4-7 copy V.
 //
 // Software pipeline.  Per page (64 keys) and wave (32 query rows), in the transposed domain so
@@ -30,7 +37,7 @@
 //   SM   causal cut (only on pages that reach past the wave's first row), online softmax in
 //        fp32, log2 domain, softmax scale folded into one FMA; a row's 64 scores live in lanes
 //        l and l^32 (one permlane32 swap per row maximum); P^T rounded to bf16
-//   PV   O^T[dv][row] += V^T . P^T   A = V^T by transposed LDS reads, B = P^T
+//   PV   O^T[dv][row] += V^T . P^T   A = V^T from LDS (see V above), B = P^T
 // The pipeline works on units of 32 keys (half a page): unit u runs SM of unit u together with
 // QK of unit u+1 and PV of unit u-1.  The three are independent, so each wave's softmax VALU
 // work issues in the shadow of its own MFMAs instead of waiting for them.  Iteration i of the
@@ -77,6 +84,13 @@ struct Geo {
   static constexpr int KS = D / 16;     // k-steps of the QK product
 };
 
+// Key order of the K slabs for dim-major V.  The score accumulator of lane l holds, in
+// elements 0..7, rows 4(l/32) + 0..3 and 8 + 4(l/32) + 0..3 of each 16-row half, and those
+// elements become the lane's 8 k-values of the PV product's P operand.  Dim-major V pages give
+// lane l the 8 consecutive keys 8(l/32) + 0..7 as its V operand, so slab row m holds key
+// key_perm(m) (bits 2 and 3 swapped), which puts exactly those keys in the lane's 8 elements.
+__device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
 // chunk position of V chunk c of row r is c ^ swz_v(r)
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
@@ -109,7 +123,8 @@ __device__ __forceinline__ void barrier_keep_vm() {
 template <int I>
 using IC = std::integral_constant<int, I>;
 
-template <int D, bool SPLIT>
+// VT: the V pool is dim-major ([d][token] per page and group, row stride a.v_row_stride)
+template <int D, bool SPLIT, bool VT>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
   using GE = Geo<D>;
   __shared__ __attribute__((aligned(1024))) __bf16 kR0[GE::PAGE];
@@ -165,9 +180,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   }
 
   const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(a.k) + (size_t)g * a.head_stride;
-  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(a.v) + (size_t)g * a.head_stride;
+  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(a.v) + (size_t)g * a.v_head_stride;
   const int32_t* __restrict__ pmap = a.page_map + (size_t)b * a.page_map_stride;
-  const int ts = (int)a.token_stride;
 
   // ---- Q in registers (B operand of S^T = K Q^T) -------------------------------------------
   const int row0 = 64 * qi_w + 32 * half;   // first chunk row of this wave
@@ -191,22 +205,31 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // s = 4w' + j of its tensor (w' = w % 4), lane l the 16-byte slot l of that slab.
   const bool vrole = wave >= 4;
   const __bf16* const tg = vrole ? vg : kg;  // this wave's tensor of group g
+  const int64_t pstride = vrole ? a.v_page_stride : a.page_stride;
+  const int rs = (int)(vrole ? a.v_row_stride : a.token_stride);   // elements between rows
   uint32_t dma_off[GE::NPW];   // byte offset of the lane's source chunk within a page
-  int dma_row[GE::NPW];        // its token row
+  int dma_row[GE::NPW];        // its (first) token
 #pragma unroll
   for (int j = 0; j < GE::NPW; ++j) {
     const int sl = (wave & 3) * GE::NPW + j;
-    int r, c;
-    if (vrole) {   // natural rows, swizzled chunks
-      const int p = sl * 64 + lane;
-      r = p / GE::CPR;
-      c = (p % GE::CPR) ^ swz_v<D>(r);
-    } else {       // operand order: slab (h, ks)
-      r = 32 * (sl / GE::KS) + l32;
-      c = 2 * (sl % GE::KS) + hl;
+    if (vrole && VT) {   // operand order: slab (h, u, dt), 8 keys of column 32dt + l % 32
+      const int h = sl / (2 * GE::DT), u = (sl / GE::DT) & 1, dt = sl % GE::DT;
+      const int tok = 32 * h + 16 * u + 8 * hl;
+      dma_row[j] = tok;
+      dma_off[j] = (uint32_t)((32 * dt + l32) * rs + tok) * 2u;
+    } else {
+      int r, c;
+      if (vrole) {   // natural rows, swizzled chunks
+        const int p = sl * 64 + lane;
+        r = p / GE::CPR;
+        c = (p % GE::CPR) ^ swz_v<D>(r);
+      } else {       // operand order: slab (h, ks)
+        r = 32 * (sl / GE::KS) + (VT ? key_perm(l32) : l32);
+        c = 2 * (sl % GE::KS) + hl;
+      }
+      dma_row[j] = r;
+      dma_off[j] = (uint32_t)(r * rs + c * 8) * 2u;
     }
-    dma_row[j] = r;
-    dma_off[j] = (uint32_t)(r * ts + c * 8) * 2u;
   }
   const int dma_dst = (wave & 3) * GE::NPW * 64 * 8;  // elements; + j * 512
 
@@ -222,14 +245,22 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   auto plan = [&](bool valid, int kb, int ph, __bf16* tile) __attribute__((always_inline)) {
     if (!valid) return idle;
     const int nv_tok = min(max(L - 64 * kb, 0), 64);
-    if (ph >= 0 && nv_tok == 64) return Fill{tg + (size_t)ph * a.page_stride, tile + dma_dst};
-    const __bf16* src = tg + (size_t)(ph < 0 ? 0 : ph) * a.page_stride;
+    if (ph >= 0 && nv_tok == 64) return Fill{tg + (size_t)ph * pstride, tile + dma_dst};
+    const __bf16* src = tg + (size_t)(ph < 0 ? 0 : ph) * pstride;
     const uint32_t fv = ph < 0 ? 0x7FC07FC0u : 0u;
 #pragma unroll
     for (int j = 0; j < GE::NPW; ++j) {
       uint4 v = make_uint4(fv, fv, fv, fv);
-      if (ph >= 0 && dma_row[j] < nv_tok)
+      if (ph >= 0 && dma_row[j] < nv_tok) {
         v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) + dma_off[j]);
+        if (vrole && VT && dma_row[j] + 8 > nv_tok) {   // a chunk of 8 keys crossing the end
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (dma_row[j] + e >= nv_tok) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
       *reinterpret_cast<uint4*>(tile + dma_dst + j * 512 + lane * 8) = v;
     }
     return idle;
@@ -316,7 +347,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     if (k0 + 31 > wave_pos0) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = k0 + 8 * (j >> 2) + 4 * hl + (j & 3);
+        // accumulator row 8(j/4) + 4hl + j%4 holds that key, or its key_perm image
+        const int key = k0 + (VT ? 16 * (j >> 3) + 8 * hl + (j & 7) : 8 * (j >> 2) + 4 * hl + (j & 3));
         if (key > row_pos) s[j] = -INFINITY;
       }
     }
@@ -368,10 +400,15 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       const int krow = (32 * h + 16 * u) * D;
 #pragma unroll
       for (int dt = 0; dt < GE::DT; ++dt) {
-        const v4i16 lo = ds_read_tr(Vl + krow + v_off[dt]);
-        const v4i16 hi = ds_read_tr(Vl + krow + 8 * D + v_off[dt]);
-        const v4i16 both[2] = {lo, hi};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, both);
+        bf16x8 va;
+        if (VT) {
+          va = *reinterpret_cast<const bf16x8*>(Vl + ((2 * h + u) * GE::DT + dt) * 512 + k_lane_off);
+        } else {
+          const v4i16 lo = ds_read_tr(Vl + krow + v_off[dt]);
+          const v4i16 hi = ds_read_tr(Vl + krow + 8 * D + v_off[dt]);
+          const v4i16 both[2] = {lo, hi};
+          va = __builtin_bit_cast(bf16x8, both);
+        }
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, u == 0 ? p0 : p1, o[dt], 0, 0, 0);
       }
     }
@@ -609,10 +646,14 @@ template <int D>
 hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const int grid = prefill_grid(a);
   if (grid == 0) return hipSuccess;
-  if (a.n_splits > 1)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3(grid), dim3(THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3(grid), dim3(THREADS), 0, s, a);
+  const bool split = a.n_splits > 1;
+  if (a.v_dmajor) {
+    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
+  } else {
+    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -629,7 +670,8 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
   if (!bf16) return launch_prefill_regstaged(a, false, d, s);
-  if (a.token_stride > (1 << 24)) return launch_prefill_regstaged(a, true, d, s);  // 32-bit offsets
+  if (a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24))   // 32-bit offsets within a page
+    return launch_prefill_regstaged(a, true, d, s);
   return d == 64 ? launch_bf16<64>(a, s) : launch_bf16<128>(a, s);
 }
 

@@ -117,9 +117,19 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   const int n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
 
   const T* __restrict__ kg = reinterpret_cast<const T*>(a.k) + (size_t)g * a.head_stride;
-  const T* __restrict__ vg = reinterpret_cast<const T*>(a.v) + (size_t)g * a.head_stride;
+  const T* __restrict__ vg = reinterpret_cast<const T*>(a.v) + (size_t)g * a.v_head_stride;
   const int32_t* __restrict__ pmap = a.page_map + (size_t)b * a.page_map_stride;
   const int64_t ts = a.token_stride;
+  const int64_t vrs = a.v_row_stride;
+  // 16-byte chunk `col` of V token row r of the page at vp: one load for token-major pages, a
+  // gather of EPC elements (one per dim row) for dim-major pages
+  auto v_chunk = [&](const T* vp, int r, int col) __attribute__((always_inline)) {
+    if (!a.v_dmajor) return *reinterpret_cast<const uint4*>(vp + (size_t)r * vrs + col * C::EPC);
+    T e[C::EPC];
+#pragma unroll
+    for (int x = 0; x < C::EPC; ++x) e[x] = vp[(size_t)(col * C::EPC + x) * vrs + r];
+    return __builtin_bit_cast(uint4, e);
+  };
 
   // ---- Q in registers (B operand of S^T = K Q^T) -------------------------------------------
   const int row0 = 64 * qi_w + 32 * half;   // first chunk row of this wave
@@ -154,14 +164,13 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
     const int nv_tok = min(max(L - 64 * kb, 0), 64);
     if (ph >= 0 && nv_tok == 64) {
       if (vrole) {
-        const T* vp = vg + (size_t)ph * a.page_stride;
+        const T* vp = vg + (size_t)ph * a.v_page_stride;
 #pragma unroll
         for (int k = 0; k < C::VPT; ++k) {
           const int u = min(rtid + ROLE * k, C::VUNITS - 1);
           const int col = u % C::CPR, q4 = u / C::CPR;
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            st[4 * k + c] = *reinterpret_cast<const uint4*>(vp + (size_t)(4 * q4 + c) * ts + col * C::EPC);
+          for (int c = 0; c < 4; ++c) st[4 * k + c] = v_chunk(vp, 4 * q4 + c, col);
         }
       } else {
         const T* kp = kg + (size_t)ph * a.page_stride;
@@ -176,6 +185,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
       const uint4 fill = make_uint4(f, f, f, f);
       const size_t pofs = (size_t)(ph < 0 ? 0 : ph) * a.page_stride;
       if (vrole) {
+        const T* vp = vg + (size_t)(ph < 0 ? 0 : ph) * a.v_page_stride;
 #pragma unroll
         for (int k = 0; k < C::VPT; ++k) {
           const int u = min(rtid + ROLE * k, C::VUNITS - 1);
@@ -183,9 +193,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = 4 * q4 + c;
-            st[4 * k + c] = (ph >= 0 && r < nv_tok)
-                                ? *reinterpret_cast<const uint4*>(vg + pofs + (size_t)r * ts + col * C::EPC)
-                                : fill;
+            st[4 * k + c] = (ph >= 0 && r < nv_tok) ? v_chunk(vp, r, col) : fill;
           }
         }
       } else {

@@ -28,7 +28,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"cpa_build_block_tables", "cpa_chunked_prefill", "cpa_chunked_prefill_split",
-                          "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
+                          "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string",
+                          "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -121,6 +122,37 @@ def test_split_validation(lib):
     assert pfs(lib, B=0, q=NULL) == 0
     assert lib.cpa_split_workspace_bytes(256, 32, 128, 16, 16) == 0   # one range: no workspace
     assert lib.cpa_split_workspace_bytes(0, 32, 128, 16, 4) == 0
+
+
+def pfv(lib, dtype=1, total_q=256, split=0, ws=NULL, ws_bytes=0, vps=8 * 128 * 64, vhs=128 * 64, vds=64, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
+             tab=FAKE, cap=16, cnt=FAKE, cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0,
+             o=FAKE, lse=NULL)
+    a.update(kw)
+    return lib.cpa_chunked_prefill_vt(a["q"], dtype, a["k"], a["ps"], a["hs"], a["ts"], a["v"], vps, vhs, vds,
+                                      a["npages"], a["pm"], a["pms"], a["tab"], a["cap"], a["cnt"], a["cu"],
+                                      a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["mcl"], a["scale"], a["o"],
+                                      a["lse"], total_q, split, ws, ws_bytes, None)
+
+
+def test_vt_validation(lib):
+    assert pfv(lib, vds=63) == 2                      # a dim row must hold the page's 64 tokens
+    assert pfv(lib, vhs=127 * 64) == 2                # d dim rows per head
+    assert pfv(lib, vps=7 * 128 * 64) == 2            # Hkv heads per page
+    assert pfv(lib, vds=68, vhs=128 * 68, vps=8 * 128 * 68) == 3   # bf16 row of 136 B
+    assert pfv(lib, ts=64) == 2                       # K is still checked
+    assert pfv(lib, d=96) == 4
+    assert pfv(lib, v=NULL) == 1
+    assert pfv(lib, v=FAKE + 2) == 3
+    # d = 64: rows of 64 tokens, 64 of them per head
+    assert pfv(lib, d=64, ps=8 * 64 * 64, hs=64 * 64, ts=64, vps=8 * 64 * 64, vhs=64 * 64, vds=63) == 2
+    # the split form: the split checks apply
+    assert pfv(lib, split=4) == 1                     # no workspace
+    assert pfv(lib, split=4, ws=FAKE, ws_bytes=1 << 30, dtype=0) == 4
+    assert pfv(lib, split=4, ws=FAKE, ws_bytes=1 << 30, vds=1 << 25, vhs=128 << 25, vps=8 * (128 << 25)) == 4
+    assert pfv(lib, split=4, ws=FAKE, ws_bytes=16, total_q=256) == 5
+    assert pfv(lib, split=4, total_q=-1) == 2
+    assert pfv(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
 
 
 def test_split_planner():
