@@ -7,7 +7,7 @@ attention-layer shape (32 query heads, 8 KV heads, head dim 128), bf16, structur
 block masks (vertical stripes, slash diagonals, Bernoulli noise, sink block and a 4-block local
 window), K/V in a randomly permuted paged pool.  Other workloads: --workload c2 (32K context),
 c4 (the full chunked prefill of one 131072-token sequence: 64 chunks of 2048, one step = all 64
-chunks in order), c5a / c5b (varlen batch of four sequences, last 4096-token chunks), c3s (one KV
+chunks in order), c4b (the same 64 chunks as one varlen launch pair), c5a / c5b (varlen batch of four sequences, last 4096-token chunks), c3s (one KV
 group's share of the 128K workload, too few tiles for the GPU: run with split-KV, the unsplit
 time reported beside it).  All inputs are seeded synthetic data resident in HBM before the timed
 region.
@@ -40,6 +40,9 @@ WORKLOADS = {
             "d 128, bf16, group-shared stripes 0.1"),
     "c5b": ("c5b_varlen_independent", "varlen 4 x last 4096 of {8K,32K,64K,128K}, Hq 32 / Hkv 8 / "
             "d 128, bf16, per-head stripes 0.1"),
+    "c4b": ("c4_128k_chunked_batch", "full chunked prefill of one 131072-token sequence as one varlen "
+            "launch pair over its 64 chunks of 2048 (prefix 2048k), Hq 32 / Hkv 8 / d 128, bf16, "
+            "structured masks per chunk"),
     "c3s": ("c3s_128k_one_group", "one KV group's share of the 128K last chunk (the per-GPU share of "
             "an 8-way head split): prefix 129024 + chunk 2048, Hq 4 / Hkv 1 / d 128, bf16, "
             "structured masks, split-KV"),
@@ -171,9 +174,11 @@ class Batch:
 
 def make_batches(key, dev, v_layouts):
     from workloads import make_config
-    from workloads.configs import chunked_sequence_chunk
+    from workloads.configs import chunked_sequence_batch, chunked_sequence_chunk
     name, _ = WORKLOADS[key]
-    if key != "c4":
+    if key == "c4b":
+        batches = [Batch(chunked_sequence_batch(), dev)]
+    elif key != "c4":
         batches = [Batch(make_config(name), dev, split=(key == "c3s"))]
     else:
         batches = []
@@ -226,6 +231,40 @@ def timed(cpa, batches, modes, steps, warmup):
                     "prefill_ms": float(pre.sum(1).mean()), "prefill_ms_median": float(np.median(pre.sum(1))),
                     "prefill_launch_ms": float(pre.mean()), "launches_per_step": nb})
     return out
+
+
+def time_append(cpa, bt, steps):
+    """HIP-event time of cpa_append_kv writing the batch's chunk rows (taken from the pool itself,
+    so the pool's contents do not change) into the pool in the bench's V layout."""
+    import numpy as np
+    import torch
+    w = bt.w
+    pos = [w.prefix_len[b] + np.arange(w.chunk_len[b]) for b in range(w.B)]
+    pages = torch.from_numpy(np.concatenate([w.page_map[b, p // 64] for b, p in enumerate(pos)]).astype(np.int64))
+    slots = torch.from_numpy(np.concatenate([p % 64 for p in pos]).astype(np.int64))
+    pages, slots = pages.to(bt.q.device), slots.to(bt.q.device)
+    k_rows = bt.kp[pages, :, slots].contiguous()
+    v_rows = bt.vp[pages, :, slots].contiguous()
+    dim = bt.v_layout == "dim"
+    vpool = bt.vp_dim if dim else bt.vp
+
+    def run():
+        cpa.append_kv(k_rows, v_rows, bt.kp, vpool, bt.pm, bt.cu, bt.pl, w.max_chunk_len, v_layout=bt.v_layout)
+
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+    nbytes = 2 * 2 * k_rows.numel() * k_rows.element_size()   # K and V, read once and written once
+    return {"us": round(us, 2), "rows": int(k_rows.shape[0]),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": nbytes}}
 
 
 def main():
@@ -307,6 +346,12 @@ def main():
         layout_ab = {args.v_layout: round(again["prefill_ms"], 4), other: round(alt["prefill_ms"], 4)}
         log(f"[bench] V layout A/B prefill ms: {layout_ab}")
 
+    append = None
+    if args.workload != "c4":
+        append = time_append(cpa, batches[0], max(5, args.steps))
+        log(f"[bench] kv append: {append['us']:.1f} us for {append['rows']} rows, "
+            f"{append['roofline']['achieved']:.0f} GB/s")
+
     w0 = batches[-1].w
     bt0 = batches[0]
     step_tflops = flops / (r["step_ms"] * 1e-3) / 1e12
@@ -356,6 +401,8 @@ def main():
                                       "end_to_end": round(d["step_ms"] / r["step_ms"], 4)}
     if layout_ab is not None:
         result["v_layout_prefill_ms"] = layout_ab
+    if append is not None:
+        result["kv_append"] = append
     if unsplit is not None:
         result["split_kv"] = {"split_pages": batches[0].split_pages,
                               "unsplit_prefill_ms": round(unsplit["prefill_ms"], 4),

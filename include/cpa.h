@@ -195,6 +195,38 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
                                   int split_pages, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
+/*
+ * cpa_append_kv - write each sequence's chunk of new K and V rows into the paged cache, the step
+ * before attention in chunked prefill (CompactAttention abstract: the chunk attends over KV
+ * blocks that live in a paged cache and are read in place, so its own K/V must be there).
+ *
+ *   k_new, v_new  [Tq][Hkv][d] in `dtype`, contiguous; rows of sequence b at cu_q[b]..cu_q[b+1]
+ *                 (the layout of q with Hkv heads).
+ *   k_pages       out: the K pool, layout as in cpa_chunked_prefill (token-major).
+ *   v_pages       out: the V pool; v_dim_major = 0: token-major with (v_page_stride,
+ *                 v_head_stride, v_row_stride = token stride), dim contiguous; v_dim_major = 1:
+ *                 dim-major as in cpa_chunked_prefill_vt (v_row_stride = dim stride), tokens
+ *                 contiguous.
+ *   n_pages, page_map, page_map_stride, cu_q, prefix_len, B, Hkv, d, max_chunk_len
+ *                 as in cpa_chunked_prefill.
+ *
+ * Row r of sequence b goes to position p = prefix_len[b] + r: slot p % 64 of physical page
+ * page_map[b][p / 64], group h for head h.  Nothing else in the pools is written: slots of the
+ * last page past the chunk stay as they were.  A page whose logical block is >= page_map_stride
+ * or whose id is outside [0, n_pages) is skipped (its rows are not written).  A copy: the pool
+ * holds the input bits exactly.  Calls must not overlap with a prefill reading the same pages.
+ * Supported: CPA_BF16 and CPA_F32, d in {64, 128}.
+ * Errors: CPA_ERR_NULL, CPA_ERR_SHAPE (negative sizes, strides too small to hold a page,
+ * v_dim_major not 0 or 1, page_map_stride < 1), CPA_ERR_ALIGN (16-byte alignment of pointers
+ * and strides), CPA_ERR_UNSUPPORTED, CPA_ERR_LAUNCH.
+ */
+cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, void* k_pages,
+                         int64_t page_stride, int64_t head_stride, int64_t token_stride, void* v_pages,
+                         int v_dim_major, int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride,
+                         int64_t n_pages, const int32_t* page_map, int page_map_stride, const int32_t* cu_q,
+                         const int32_t* prefix_len, int B, int Hkv, int d, int max_chunk_len,
+                         hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (host pointer, never NULL). */
 const char* cpa_status_string(cpa_status s);
 

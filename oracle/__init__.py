@@ -17,6 +17,9 @@ Pin status (what each function is checked against besides itself):
                        closed forms (constant V, q=0, single key), LSE-merge identity,
                        page-permutation invariance
   attention_rows       pinned: equals paged_attention on every row it is given
+  append_kv            pinned: a worked example written out by hand; the appended rows read
+                       back through logical positions; every other slot unchanged
 """
 from .union import block_union_tables  # noqa: F401
 from .attention import paged_attention, attention_rows  # noqa: F401
+from .append import append_kv  # noqa: F401

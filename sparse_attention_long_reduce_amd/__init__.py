@@ -1,17 +1,21 @@
 """Block-Union KV Selection for chunked prefill on MI355X (gfx950).
 
-Two entry points, both thin wrappers over the C ABI in include/cpa.h:
+Thin wrappers over the C ABI in include/cpa.h:
 
 * build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv) -> (tables, counts)
 * chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len,
-                  max_chunk_len, split_pages=0) -> (o, lse)
-  (split_pages > 0: split-KV over page ranges with an LSE merge; plan_split_pages picks one)
+                  max_chunk_len, split_pages=0, v_layout="token") -> (o, lse)
+  (split_pages > 0: split-KV over page ranges with an LSE merge; plan_split_pages picks one;
+  v_layout "dim": V pages stored [page][group][d][64])
+* append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len,
+            v_layout="token"): the chunk's K/V rows into the paged cache
 
 The library must be built first (``python -m sparse_attention_long_reduce_amd.build``); nothing
 here falls back to another implementation.
 """
 from .api import (  # noqa: F401
     BLOCK,
+    append_kv,
     attention_flops,
     build_block_tables,
     chunked_prefill,

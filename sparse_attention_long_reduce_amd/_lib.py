@@ -5,7 +5,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpa.so")
 
-EXPORTS = ("cpa_build_block_tables", "cpa_chunked_prefill", "cpa_chunked_prefill_split",
+EXPORTS = ("cpa_append_kv", "cpa_build_block_tables", "cpa_chunked_prefill", "cpa_chunked_prefill_split",
            "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version")
 
 _lib = None
@@ -35,6 +35,9 @@ def load():
     lib.cpa_chunked_prefill_vt.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, i64, i64, i64, vp, i32, vp, i32,
                                            vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, i32, i32, vp,
                                            c.c_size_t, vp]
+    lib.cpa_append_kv.restype = i32
+    lib.cpa_append_kv.argtypes = [vp, vp, i32, vp, i64, i64, i64, vp, i32, i64, i64, i64, i64, vp, i32, vp, vp,
+                                  i32, i32, i32, i32, vp]
     lib.cpa_split_workspace_bytes.restype = c.c_size_t
     lib.cpa_split_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.cpa_status_string.restype = c.c_char_p

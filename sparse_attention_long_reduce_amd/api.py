@@ -162,6 +162,46 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     return out, lse
 
 
+def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len, v_layout="token",
+              stream=None):
+    """Write each sequence's chunk rows k_new / v_new [Tq][Hkv][d] into their slots of the paged
+    pools in place (cpa_append_kv).  k_pages [n_pages][Hkv][64][d]; v_pages the same (v_layout
+    "token") or [n_pages][Hkv][d][64] (v_layout "dim"), strided views allowed as in
+    chunked_prefill."""
+    if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype or k_pages.dtype != k_new.dtype \
+            or v_pages.dtype != k_new.dtype:
+        raise TypeError("k_new, v_new and the pools must share dtype float32 or bfloat16")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        if not (t.is_cuda and t.dim() == 3 and t.is_contiguous()):
+            raise TypeError(f"{n} must be a contiguous [Tq][Hkv][d] CUDA tensor")
+    if v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must have the same shape")
+    Tq, Hkv, d = k_new.shape
+    if k_pages.dim() != 4 or tuple(k_pages.shape[1:]) != (Hkv, BLOCK, d) or k_pages.stride(3) != 1:
+        raise ValueError("k_pages must be [n_pages][Hkv][64][d] with d contiguous")
+    if v_layout == "token":
+        vshape = (k_pages.shape[0], Hkv, BLOCK, d)
+    elif v_layout == "dim":
+        vshape = (k_pages.shape[0], Hkv, d, BLOCK)
+    else:
+        raise ValueError("v_layout must be 'token' or 'dim'")
+    if tuple(v_pages.shape) != vshape or v_pages.stride(3) != 1:
+        raise ValueError(f"v_pages must be {list(vshape)} with the last dimension contiguous")
+    _dev_i32(page_map, "page_map")
+    _dev_i32(cu_q, "cu_q")
+    _dev_i32(prefix_len, "prefix_len")
+    B = prefix_len.numel()
+    if cu_q.numel() != B + 1 or page_map.dim() != 2 or page_map.shape[0] != B:
+        raise ValueError("inconsistent B across cu_q / prefix_len / page_map")
+    st = load().cpa_append_kv(_ptr(k_new), _ptr(v_new), _DTYPES[k_new.dtype], _ptr(k_pages), k_pages.stride(0),
+                              k_pages.stride(1), k_pages.stride(2), _ptr(v_pages), 1 if v_layout == "dim" else 0,
+                              v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), k_pages.shape[0],
+                              _ptr(page_map), page_map.shape[1], _ptr(cu_q), _ptr(prefix_len), B, Hkv, d,
+                              int(max_chunk_len), _stream(stream))
+    if st != 0:
+        raise CpaError(st, "cpa_append_kv")
+
+
 def status_string(code: int) -> str:
     return load().cpa_status_string(int(code)).decode()
 

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libcpa.so")
-SOURCES = ("block_union.hip", "prefill_regstaged.hip", "prefill_bf16.hip", "cpa_api.hip")
+SOURCES = ("block_union.hip", "prefill_regstaged.hip", "prefill_bf16.hip", "kv_append.hip", "cpa_api.hip")
 ARCH = os.environ.get("CPA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

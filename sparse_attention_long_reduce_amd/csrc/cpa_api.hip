@@ -136,6 +136,41 @@ cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pag
   return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
+cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, void* k_pages,
+                         int64_t page_stride, int64_t head_stride, int64_t token_stride, void* v_pages,
+                         int v_dim_major, int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride,
+                         int64_t n_pages, const int32_t* page_map, int page_map_stride, const int32_t* cu_q,
+                         const int32_t* prefix_len, int B, int Hkv, int d, int max_chunk_len,
+                         hipStream_t stream) {
+  if (B < 0 || Hkv <= 0 || max_chunk_len < 0 || n_pages < 0) return CPA_ERR_SHAPE;
+  if (dtype != CPA_F32 && dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
+  if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
+  if (B == 0 || max_chunk_len == 0) return CPA_OK;
+  if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
+    return CPA_ERR_SHAPE;
+  const int64_t v_rows = v_dim_major ? d : 64, v_row_len = v_dim_major ? 64 : d;
+  if (v_row_stride < v_row_len || v_head_stride < v_rows * v_row_stride ||
+      v_page_stride < (int64_t)Hkv * v_head_stride)
+    return CPA_ERR_SHAPE;
+  if (!k_new || !v_new || !k_pages || !v_pages || !page_map || !cu_q || !prefix_len) return CPA_ERR_NULL;
+  const int eb = dtype == CPA_BF16 ? 2 : 4;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages)) return CPA_ERR_ALIGN;
+  if ((token_stride * eb) % 16 || (head_stride * eb) % 16 || (page_stride * eb) % 16) return CPA_ERR_ALIGN;
+  if ((v_row_stride * eb) % 16 || (v_head_stride * eb) % 16 || (v_page_stride * eb) % 16) return CPA_ERR_ALIGN;
+  if ((long long)B * ((max_chunk_len + 63) / 64) * Hkv > 0x7fffffffLL) return CPA_ERR_SHAPE;
+  cpa::AppendArgs a{};
+  a.k_new = k_new; a.v_new = v_new; a.k_pages = k_pages; a.v_pages = v_pages;
+  a.page_stride = page_stride; a.head_stride = head_stride; a.token_stride = token_stride; a.n_pages = n_pages;
+  a.v_page_stride = v_page_stride; a.v_head_stride = v_head_stride; a.v_row_stride = v_row_stride;
+  a.v_dmajor = v_dim_major;
+  a.page_map = page_map; a.page_map_stride = page_map_stride;
+  a.cu_q = cu_q; a.prefix_len = prefix_len;
+  a.B = B; a.Hkv = Hkv; a.max_chunk_len = max_chunk_len;
+  return cpa::launch_kv_append(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
 size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int split_pages) {
   if (total_q <= 0 || Hq <= 0 || d <= 0 || table_cap <= 0 || split_pages <= 0) return 0;
   const size_t n_splits = ((size_t)table_cap + split_pages - 1) / split_pages;

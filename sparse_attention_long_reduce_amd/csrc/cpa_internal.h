@@ -63,7 +63,24 @@ struct MergeArgs {
   float* lse;    // optional [total_q][Hq]
 };
 
-// Both return hipSuccess or the launch error; they never synchronise.
+// KV append: rows [Tq][Hkv][d] of k_new / v_new go to their slots of the paged pools (layouts
+// as in PrefillArgs)
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  void* k_pages;
+  void* v_pages;
+  int64_t page_stride, head_stride, token_stride, n_pages;
+  int64_t v_page_stride, v_head_stride, v_row_stride;
+  int v_dmajor;
+  const int32_t* page_map;
+  int page_map_stride;
+  const int32_t* cu_q;
+  const int32_t* prefix_len;
+  int B, Hkv, max_chunk_len;
+};
+
+// All return hipSuccess or the launch error; they never synchronise.
 hipError_t launch_block_union(const UnionArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
 // combines the split-KV partials (bf16 output)
@@ -71,5 +88,6 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s);
 // register-staged variant (V transposed through registers); serves fp32 and is kept for bf16
 // as the reference point of the direct-to-LDS bf16 kernel
 hipError_t launch_prefill_regstaged(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
+hipError_t launch_kv_append(const AppendArgs& a, bool bf16, int d, hipStream_t s);
 
 }  // namespace cpa

@@ -27,9 +27,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"cpa_build_block_tables", "cpa_chunked_prefill", "cpa_chunked_prefill_split",
-                          "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string",
-                          "cpa_version"}
+    assert set(names) == {"cpa_append_kv", "cpa_build_block_tables", "cpa_chunked_prefill",
+                          "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes",
+                          "cpa_status_string", "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -153,6 +153,34 @@ def test_vt_validation(lib):
     assert pfv(lib, split=4, ws=FAKE, ws_bytes=16, total_q=256) == 5
     assert pfv(lib, split=4, total_q=-1) == 2
     assert pfv(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
+
+
+def ap(lib, kn=FAKE, vn=FAKE, dtype=1, k=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, v=FAKE, vdm=0,
+       vps=8 * 64 * 128, vhs=64 * 128, vrs=128, npages=10, pm=FAKE, pms=16, cu=FAKE, pl=FAKE, B=1, Hkv=8, d=128,
+       mcl=256):
+    return lib.cpa_append_kv(kn, vn, dtype, k, ps, hs, ts, v, vdm, vps, vhs, vrs, npages, pm, pms, cu, pl, B, Hkv,
+                             d, mcl, None)
+
+
+def test_append_validation(lib):
+    assert ap(lib, d=96) == 4
+    assert ap(lib, dtype=5) == 4
+    assert ap(lib, Hkv=0) == 2
+    assert ap(lib, B=-1) == 2
+    assert ap(lib, vdm=2) == 2
+    assert ap(lib, ts=64) == 2
+    assert ap(lib, vrs=64) == 2                       # token-major V rows hold d = 128 values
+    assert ap(lib, vdm=1, vrs=63, vhs=128 * 64, vps=8 * 128 * 64) == 2
+    assert ap(lib, vdm=1, vrs=64, vhs=127 * 64, vps=8 * 128 * 64) == 2
+    assert ap(lib, pms=0) == 2
+    assert ap(lib, kn=NULL) == 1
+    assert ap(lib, v=NULL) == 1
+    assert ap(lib, pm=NULL) == 1
+    assert ap(lib, kn=FAKE + 4) == 3
+    assert ap(lib, ts=132, hs=64 * 132, ps=8 * 64 * 132) == 3
+    assert ap(lib, vdm=1, vrs=68, vhs=128 * 68, vps=8 * 128 * 68) == 3
+    assert ap(lib, B=0, kn=NULL, vn=NULL, k=NULL, v=NULL, pm=NULL, cu=NULL, pl=NULL) == 0
+    assert ap(lib, mcl=0, kn=NULL) == 0
 
 
 def test_split_planner():

@@ -402,3 +402,53 @@ def test_structured_mask_shape_and_density():
     assert np.all(m[:, :, 0])
     for qi in range(8):
         assert np.all(m[:, qi, 100 + qi - 3:100 + qi + 1])
+
+
+# ---- KV append ---------------------------------------------------------------------------------
+
+def test_append_kv_worked_example():
+    # two sequences, one KV head, d = 2, four pages.  Sequence 0: prefix 64, chunk of 3 rows;
+    # logical block 1 is page 0, so its rows land in page 0 slots 0..2.  Sequence 1: prefix 0,
+    # chunk of 2 rows; block 0 is page 3.
+    k_new = np.array([[[1, 2]], [[3, 4]], [[5, 6]], [[7, 8]], [[9, 10]]], dtype=np.float64)
+    v_new = -k_new
+    kp = np.zeros((4, 1, 64, 2))
+    vp = np.zeros((4, 1, 64, 2))
+    page_map = np.array([[2, 0], [3, 1]], dtype=np.int32)
+    cu = np.array([0, 3, 5], dtype=np.int32)
+    P = np.array([64, 0], dtype=np.int32)
+    k2, v2 = oracle.append_kv(k_new, v_new, kp, vp, page_map, cu, P)
+    expect = np.zeros((4, 1, 64, 2))
+    expect[0, 0, 0] = [1, 2]
+    expect[0, 0, 1] = [3, 4]
+    expect[0, 0, 2] = [5, 6]
+    expect[3, 0, 0] = [7, 8]
+    expect[3, 0, 1] = [9, 10]
+    assert np.array_equal(k2, expect) and np.array_equal(v2, -expect)
+    assert not kp.any()   # inputs untouched
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_append_kv_reads_back_and_touches_nothing_else(seed):
+    rng = np.random.default_rng(seed)
+    w = make_workload("app", [0, 128, 640], [100, 64, 200], 8, 2, 16, "f32",
+                      lambda r, *a: mask_all(r, *a, value=1), seed)
+    k_new = rng.standard_normal((w.q.shape[0], w.Hkv, w.d)).astype(w.k_pages.dtype)
+    v_new = rng.standard_normal((w.q.shape[0], w.Hkv, w.d)).astype(w.v_pages.dtype)
+    pm = w.page_map.copy()
+    pm[2, (640 + 150) // 64] = -1             # one unresolved page: its rows are dropped
+    k2, v2 = oracle.append_kv(k_new, v_new, w.k_pages, w.v_pages, pm, w.cu_q, w.prefix_len)
+    written = np.zeros(w.k_pages.shape[:1] + w.k_pages.shape[2:3], dtype=bool)   # [page][slot]
+    for b in range(w.B):
+        pos = w.prefix_len[b] + np.arange(w.chunk_len[b])
+        pages = pm[b, pos // 64]
+        ok = pages >= 0
+        rows = w.cu_q[b] + np.arange(w.chunk_len[b])
+        # read back through (page, slot) of each logical position, all heads at once
+        assert np.array_equal(k2[pages[ok], :, pos[ok] % 64], k_new[rows[ok]])
+        assert np.array_equal(v2[pages[ok], :, pos[ok] % 64], v_new[rows[ok]])
+        written[pages[ok], pos[ok] % 64] = True
+        assert (~ok).sum() == (64 if b == 2 else 0)
+    keep = ~written
+    assert np.array_equal(k2.transpose(0, 2, 1, 3)[keep], w.k_pages.transpose(0, 2, 1, 3)[keep])
+    assert np.array_equal(v2.transpose(0, 2, 1, 3)[keep], w.v_pages.transpose(0, 2, 1, 3)[keep])

@@ -276,6 +276,26 @@ def chunked_sequence_chunk(k: int, dense: bool = False, seed: int | None = None)
     return w
 
 
+def chunked_sequence_batch(dense: bool = False, seed: int | None = None, n_chunks: int = 64) -> Workload:
+    """The first n_chunks chunks of the 131072-token sequence as one varlen batch: sequence k of
+    the batch is chunk k (prefix 2048*k, chunk 2048) with the Q, mask and page map of
+    chunked_sequence_chunk(k), all over the one shared paged pool."""
+    parts = [chunked_sequence_chunk(k, dense=dense, seed=seed) for k in range(n_chunks)]
+    last = parts[-1]
+    nqb = C4_CHUNK // BLOCK
+    nkvb = max(p.nkvb_max for p in parts)
+    masks = np.zeros((n_chunks, last.Hq, nqb, nkvb), dtype=np.uint8)
+    page_map = np.full((n_chunks, nkvb), last.poison_page, dtype=np.int32)
+    for k, p in enumerate(parts):
+        masks[k, :, :, :p.nkvb_max] = p.masks[0]
+        page_map[k, :p.page_map.shape[1]] = p.page_map[0]
+    return Workload("c4_128k_chunked_batch" + ("_dense" if dense else ""), last.Hq, last.Hkv, last.d, last.dtype,
+                    np.array([p.prefix_len[0] for p in parts], dtype=np.int32),
+                    np.array([p.chunk_len[0] for p in parts], dtype=np.int32),
+                    np.concatenate([p.q for p in parts], axis=0), last.k_pages, last.v_pages, page_map, masks,
+                    last.poison_page, meta={"seed": last.meta.get("seed"), "chunks": n_chunks})
+
+
 def make_config(name: str, dense: bool = False, chunk: int = 63, seed: int | None = None) -> Workload:
     """One of the named workloads; dense=True swaps every mask for all-ones (the dense run)."""
     s = SEEDS[name] if seed is None else seed
