@@ -233,6 +233,33 @@ def timed(cpa, batches, modes, steps, warmup):
     return out
 
 
+def time_build_bits(cpa, batches, steps):
+    """HIP-event time of the table build from bit-packed masks (cpa_build_block_tables_bits) for
+    every launch pair of the workload, and whether its tables equal the byte-mask build's."""
+    import numpy as np
+    import torch
+    from workloads.configs import pack_mask_bits
+    bits = [torch.from_numpy(pack_mask_bits(bt.w.masks).view(np.int64)).to(bt.q.device) for bt in batches]
+    outs = [(torch.empty_like(bt.tables), torch.empty_like(bt.counts)) for bt in batches]
+
+    def run():
+        for bt, mb, (t, c) in zip(batches, bits, outs):
+            cpa.build_block_tables_bits(mb, bt.w.nkvb_max, bt.pb, bt.cb, bt.w.Hkv, tables=t, counts=c)
+
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+    same = all(torch.equal(t, bt.tables) and torch.equal(c, bt.counts) for bt, (t, c) in zip(batches, outs))
+    nbytes = sum(int(b.numel()) * 8 for b in bits)
+    return {"us": round(us, 2), "mask_bytes": nbytes, "tables_equal_byte_masks": bool(same)}
+
+
 def time_append(cpa, bt, steps):
     """HIP-event time of cpa_append_kv writing the batch's chunk rows (taken from the pool itself,
     so the pool's contents do not change) into the pool in the bench's V layout."""
@@ -346,6 +373,9 @@ def main():
         layout_ab = {args.v_layout: round(again["prefill_ms"], 4), other: round(alt["prefill_ms"], 4)}
         log(f"[bench] V layout A/B prefill ms: {layout_ab}")
 
+    bits = time_build_bits(cpa, batches, max(5, args.steps))
+    log(f"[bench] table build from bit-packed masks: {bits['us']:.1f} us ({bits['mask_bytes']} mask bytes), "
+        f"tables equal: {bits['tables_equal_byte_masks']}")
     append = None
     if args.workload != "c4":
         append = time_append(cpa, batches[0], max(5, args.steps))
@@ -403,6 +433,7 @@ def main():
         result["v_layout_prefill_ms"] = layout_ab
     if append is not None:
         result["kv_append"] = append
+    result["table_build_bit_masks"] = bits
     if unsplit is not None:
         result["split_kv"] = {"split_pages": batches[0].split_pages,
                               "unsplit_prefill_ms": round(unsplit["prefill_ms"], 4),

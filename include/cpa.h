@@ -77,6 +77,24 @@ cpa_status cpa_build_block_tables(const uint8_t* masks, int B, int Hq, int Hkv, 
                                   int32_t* counts, hipStream_t stream);
 
 /*
+ * cpa_build_block_tables_bits - cpa_build_block_tables for bit-packed masks: one bit per
+ * (query head, query block, KV block) instead of one byte, so the mask read is 8x smaller.
+ * The tables and counts are those cpa_build_block_tables returns for the unpacked masks (the
+ * same Q-block and intra-group union of the CompactAttention abstract, same causal clip).
+ *
+ *   mask_bits   uint64 [B][Hq][nqb_max][mask_words]: block kb of row (b, h, qi) is selected iff
+ *               bit kb % 64 of word kb / 64 is set.  8-byte aligned.
+ *   mask_words  64-bit words per row, >= ceil(nkvb_max / 64); bits at or past nkvb_max and
+ *               outside the causal region are ignored.
+ * Other arguments and errors as cpa_build_block_tables, plus CPA_ERR_SHAPE for
+ * mask_words < ceil(nkvb_max / 64) and CPA_ERR_ALIGN for a misaligned mask_bits.
+ */
+cpa_status cpa_build_block_tables_bits(const uint64_t* mask_bits, int B, int Hq, int Hkv, int nqb_max,
+                                       int nkvb_max, int mask_words, const int32_t* prefix_blocks,
+                                       const int32_t* chunk_blocks, int32_t* tables, int table_cap,
+                                       int32_t* counts, hipStream_t stream);
+
+/*
  * cpa_chunked_prefill - attention of one prefill chunk per sequence over the selected blocks.
  *
  * For every sequence b, query head h (group g = h / (Hq/Hkv)) and chunk row r (absolute

@@ -12,6 +12,8 @@ library, and it imports nothing from it.
 
 Pin status (what each function is checked against besides itself):
   block_union_tables   pinned: brute-force loops, superset/minimality, all-ones/all-zero/G=1
+  unpack_mask_bits     pinned: hand-written words (bits 0, 1, 63 of two words) and a per-bit
+                       Python-int loop
   paged_attention      pinned: dense causal attention via torch SDPA (all-ones masks),
                        per-token brute force, per-query block-sparse SDPA special case,
                        closed forms (constant V, q=0, single key), LSE-merge identity,
@@ -20,6 +22,6 @@ Pin status (what each function is checked against besides itself):
   append_kv            pinned: a worked example written out by hand; the appended rows read
                        back through logical positions; every other slot unchanged
 """
-from .union import block_union_tables  # noqa: F401
+from .union import block_union_tables, block_union_tables_bits, unpack_mask_bits  # noqa: F401
 from .attention import paged_attention, attention_rows  # noqa: F401
 from .append import append_kv  # noqa: F401

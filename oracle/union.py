@@ -42,3 +42,18 @@ def block_union_tables(masks, prefix_blocks, chunk_blocks, Hkv, table_cap):
             tables[b, g, :ids.size] = ids
             counts[b, g] = ids.size
     return tables, counts
+
+
+def unpack_mask_bits(mask_bits, nkvb_max):
+    """Bit-packed masks uint64 [B][Hq][nqb][words] -> bool [B][Hq][nqb][nkvb_max]: block kb is
+    selected iff bit kb % 64 of word kb // 64 is set (the packed input format)."""
+    bits = np.asarray(mask_bits, dtype=np.uint64)
+    kb = np.arange(nkvb_max)
+    words = bits[..., kb // 64]
+    return ((words >> (kb % 64).astype(np.uint64)) & np.uint64(1)).astype(bool)
+
+
+def block_union_tables_bits(mask_bits, nkvb_max, prefix_blocks, chunk_blocks, Hkv, table_cap=None):
+    """The tables of the bit-packed masks: those of the masks they encode."""
+    return block_union_tables(unpack_mask_bits(mask_bits, nkvb_max).astype(np.uint8), prefix_blocks,
+                              chunk_blocks, Hkv, nkvb_max if table_cap is None else table_cap)

@@ -3,6 +3,8 @@
 Thin wrappers over the C ABI in include/cpa.h:
 
 * build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv) -> (tables, counts)
+* build_block_tables_bits(mask_bits, nkvb_max, prefix_blocks, chunk_blocks, Hkv): the same from
+  bit-packed masks (one bit per block)
 * chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len,
                   max_chunk_len, split_pages=0, v_layout="token") -> (o, lse)
   (split_pages > 0: split-KV over page ranges with an LSE merge; plan_split_pages picks one;
@@ -18,6 +20,7 @@ from .api import (  # noqa: F401
     append_kv,
     attention_flops,
     build_block_tables,
+    build_block_tables_bits,
     chunked_prefill,
     plan_split_pages,
     prefill_tiles,

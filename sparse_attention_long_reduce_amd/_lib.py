@@ -5,8 +5,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpa.so")
 
-EXPORTS = ("cpa_append_kv", "cpa_build_block_tables", "cpa_chunked_prefill", "cpa_chunked_prefill_split",
-           "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version")
+EXPORTS = ("cpa_append_kv", "cpa_build_block_tables", "cpa_build_block_tables_bits", "cpa_chunked_prefill",
+           "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string",
+           "cpa_version")
 
 _lib = None
 
@@ -24,6 +25,8 @@ def load():
     vp, i32, i64, f32 = c.c_void_p, c.c_int, c.c_int64, c.c_float
     lib.cpa_build_block_tables.restype = i32
     lib.cpa_build_block_tables.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.cpa_build_block_tables_bits.restype = i32
+    lib.cpa_build_block_tables_bits.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     lib.cpa_chunked_prefill.restype = i32
     lib.cpa_chunked_prefill.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, vp,
                                         vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]

@@ -57,6 +57,33 @@ def build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv, table_cap=None, 
     return tables, counts
 
 
+def build_block_tables_bits(mask_bits, nkvb_max, prefix_blocks, chunk_blocks, Hkv, table_cap=None, tables=None,
+                            counts=None, stream=None):
+    """Bit-packed masks int64 [B][Hq][nqb_max][words] (CUDA; bit kb % 64 of word kb / 64 = block
+    kb selected, the words' bits taken as unsigned) -> (tables, counts) as build_block_tables."""
+    if not (mask_bits.is_cuda and mask_bits.dtype in (torch.int64, torch.uint64) and mask_bits.is_contiguous()
+            and mask_bits.dim() == 4):
+        raise TypeError("mask_bits must be a contiguous 4-D int64 CUDA tensor")
+    B, Hq, nqb_max, words = mask_bits.shape
+    _dev_i32(prefix_blocks, "prefix_blocks")
+    _dev_i32(chunk_blocks, "chunk_blocks")
+    cap = int(nkvb_max) if table_cap is None else int(table_cap)
+    if tables is None:
+        tables = torch.empty((B, Hkv, cap), dtype=torch.int32, device=mask_bits.device)
+    if counts is None:
+        counts = torch.empty((B, Hkv), dtype=torch.int32, device=mask_bits.device)
+    _dev_i32(tables, "tables")
+    _dev_i32(counts, "counts")
+    if tables.numel() != B * Hkv * cap or counts.numel() != B * Hkv:
+        raise ValueError("tables/counts have the wrong size")
+    st = load().cpa_build_block_tables_bits(_ptr(mask_bits), B, Hq, Hkv, nqb_max, int(nkvb_max), words,
+                                            _ptr(prefix_blocks), _ptr(chunk_blocks), _ptr(tables), cap,
+                                            _ptr(counts), _stream(stream))
+    if st != 0:
+        raise CpaError(st, "cpa_build_block_tables_bits")
+    return tables, counts
+
+
 def prefill_tiles(B, Hq, Hkv, max_chunk_len):
     """Workgroups cpa_chunked_prefill launches without split-KV (one per group and query tile):
     a tile is the group's heads (up to 4 per workgroup) times 1, 2 or 4 query blocks."""

@@ -10,7 +10,8 @@
 //            thread and row, four rows' loads in flight per thread, with the causal clip
 //            kb <= prefix_blocks + qi applied per row;
 //            partial ORs of threads that share a column meet in LDS; each 16-block column
-//            becomes 16 bits of a 64-bit word in LDS.
+//            becomes 16 bits of a 64-bit word in LDS.  Bit-packed masks (one bit per KV block,
+//            64 blocks per 8-byte word) are OR-reduced a word at a time instead.
 //   phase 2  popcount per word, exclusive scan over words in LDS, then each wave expands
 //            words: lane l of the wave owning word w writes 64w + l at (word offset +
 //            mbcnt rank) when bit l is set.  Positions count .. table_cap-1 get -1.
@@ -42,7 +43,8 @@ __device__ __forceinline__ uint32_t bytes_to_bits(const uint32_t v[4]) {
   return bits;
 }
 
-template <bool VEC>
+// VEC: byte masks read 16 bytes at a time; BITS: bit-packed masks (a.mask_bits)
+template <bool VEC, bool BITS>
 __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
   __shared__ unsigned long long words[MAX_WORDS];
   __shared__ uint4 red[UT];
@@ -67,7 +69,53 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
   __syncthreads();
 
   // ---- phase 1: OR over (head in group, query block), causal clip per row -----------------
-  const int nchunk = (nkvb + 15) >> 4;
+  if (BITS) {
+    // column c = word c (KV blocks 64c .. 64c+63); row t as in the byte path below
+    int lgw = 0;
+    while ((1 << lgw) < nwords && (1 << lgw) < UT) ++lgw;
+    const int colw = 1 << lgw;
+    const int rs = UT >> lgw;
+    const size_t wstride = (size_t)a.mask_words;
+    const unsigned long long* wbase =
+        a.mask_bits + ((size_t)b * a.Hq + (size_t)g * G) * a.nqb_max * wstride;
+    unsigned long long* redw = reinterpret_cast<unsigned long long*>(red);
+    for (int c0 = 0; c0 < nwords; c0 += colw) {
+      const int c = c0 + (tid & (colw - 1));
+      const int s = tid >> lgw;
+      unsigned long long acc = 0ull;
+      if (c < nwords) {
+        const int kb0 = c << 6;
+        const int qi_lo = max(0, kb0 - qb0);
+        const int nq = nqb - qi_lo;
+        const int nrows = G * nq;
+        auto row = [&](int t) __attribute__((always_inline)) {
+          const int hh = t / nq;
+          const int qi = qi_lo + (t - hh * nq);
+          unsigned long long v = wbase[((size_t)hh * a.nqb_max + qi) * wstride + c];
+          const int nallow = qb0 + qi - kb0 + 1;   // bits 0 .. nallow-1 are causally reachable
+          if (nallow < 64) v &= (1ull << nallow) - 1ull;   // nallow >= 1 here (qi >= qi_lo)
+          return v;
+        };
+        for (int t0 = s; t0 < nrows; t0 += 4 * rs) {
+          unsigned long long v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = t0 + u * rs;
+            v[u] = t < nrows ? row(t) : 0ull;
+          }
+          acc |= (v[0] | v[1]) | (v[2] | v[3]);
+        }
+      }
+      redw[tid] = acc;
+      __syncthreads();
+      if (s == 0 && c < nwords) {
+        for (int k = 1; k < rs; ++k) acc |= redw[tid + (k << lgw)];
+        words[c] = acc;
+      }
+      __syncthreads();
+    }
+  }
+  const int nchunk = BITS ? 0 : (nkvb + 15) >> 4;
   int lg = 0;
   while ((1 << lg) < nchunk && (1 << lg) < UT) ++lg;
   const int cols = 1 << lg;
@@ -191,12 +239,16 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
 
 hipError_t launch_block_union(const UnionArgs& a, hipStream_t s) {
   if (a.B == 0 || a.Hkv == 0) return hipSuccess;
-  const bool vec = (a.nkvb_max % 16 == 0) && ((uintptr_t)a.masks % 16 == 0);
   dim3 grid((unsigned)(a.B * a.Hkv)), block(UT);
+  if (a.use_bits) {
+    hipLaunchKernelGGL((block_union_kernel<false, true>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  const bool vec = (a.nkvb_max % 16 == 0) && ((uintptr_t)a.masks % 16 == 0);
   if (vec)
-    hipLaunchKernelGGL(block_union_kernel<true>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((block_union_kernel<true, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(block_union_kernel<false>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((block_union_kernel<false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -114,7 +114,28 @@ cpa_status cpa_build_block_tables(const uint8_t* masks, int B, int Hq, int Hkv, 
   if (!prefix_blocks || !chunk_blocks || !counts) return CPA_ERR_NULL;
   if (table_cap > 0 && !tables) return CPA_ERR_NULL;
   if (Hq > 0 && nqb_max > 0 && nkvb_max > 0 && !masks) return CPA_ERR_NULL;
-  cpa::UnionArgs a{masks, B, Hq, Hkv, nqb_max, nkvb_max, prefix_blocks, chunk_blocks, tables, table_cap, counts};
+  cpa::UnionArgs a{masks, B, Hq, Hkv, nqb_max, nkvb_max, prefix_blocks, chunk_blocks, tables, table_cap, counts,
+                   nullptr, 0, 0};
+  return cpa::launch_block_union(a, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+cpa_status cpa_build_block_tables_bits(const uint64_t* mask_bits, int B, int Hq, int Hkv, int nqb_max,
+                                       int nkvb_max, int mask_words, const int32_t* prefix_blocks,
+                                       const int32_t* chunk_blocks, int32_t* tables, int table_cap,
+                                       int32_t* counts, hipStream_t stream) {
+  if (B < 0 || Hq < 0 || Hkv <= 0 || nqb_max < 0 || nkvb_max < 0 || table_cap < 0 || mask_words < 0)
+    return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
+  if (mask_words < (nkvb_max + 63) / 64) return CPA_ERR_SHAPE;
+  if (table_cap < nkvb_max) return CPA_ERR_CAPACITY;
+  if (B == 0) return CPA_OK;
+  if (!prefix_blocks || !chunk_blocks || !counts) return CPA_ERR_NULL;
+  if (table_cap > 0 && !tables) return CPA_ERR_NULL;
+  if (Hq > 0 && nqb_max > 0 && nkvb_max > 0 && !mask_bits) return CPA_ERR_NULL;
+  if (((uintptr_t)mask_bits & 7u) != 0) return CPA_ERR_ALIGN;
+  cpa::UnionArgs a{nullptr, B, Hq, Hkv, nqb_max, nkvb_max, prefix_blocks, chunk_blocks, tables, table_cap, counts,
+                   reinterpret_cast<const unsigned long long*>(mask_bits), mask_words, 1};
   return cpa::launch_block_union(a, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 

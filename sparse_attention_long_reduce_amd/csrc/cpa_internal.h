@@ -13,6 +13,11 @@ struct UnionArgs {
   int32_t* tables;
   int table_cap;
   int32_t* counts;
+  // bit-packed masks instead of bytes (masks unused): row (b, h, qi) is mask_words 64-bit words,
+  // bit kb % 64 of word kb / 64 = block kb selected
+  const unsigned long long* mask_bits;
+  int mask_words;
+  int use_bits;   // 1: read mask_bits (may be NULL only when there is no mask row to read)
 };
 
 struct PrefillArgs {

@@ -27,9 +27,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"cpa_append_kv", "cpa_build_block_tables", "cpa_chunked_prefill",
-                          "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes",
-                          "cpa_status_string", "cpa_version"}
+    assert set(names) == {"cpa_append_kv", "cpa_build_block_tables", "cpa_build_block_tables_bits",
+                          "cpa_chunked_prefill", "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt",
+                          "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -62,6 +62,22 @@ def test_build_tables_validation(lib):
     assert bt(lib, masks=NULL) == 1
     assert bt(lib, tab=NULL) == 1
     assert bt(lib, B=0, masks=NULL, pb=NULL, cb=NULL, tab=NULL, cnt=NULL) == 0
+
+
+def btb(lib, bits=FAKE, B=1, Hq=8, Hkv=2, nqb=4, nkvb=130, words=3, pb=FAKE, cb=FAKE, tab=FAKE, cap=130, cnt=FAKE):
+    return lib.cpa_build_block_tables_bits(bits, B, Hq, Hkv, nqb, nkvb, words, pb, cb, tab, cap, cnt, None)
+
+
+def test_build_tables_bits_validation(lib):
+    assert btb(lib, words=2) == 2          # 130 blocks need 3 words per row
+    assert btb(lib, words=-1) == 2
+    assert btb(lib, Hq=6, Hkv=4) == 2
+    assert btb(lib, nkvb=65537, cap=70000, words=1025) == 2
+    assert btb(lib, cap=129) == 5
+    assert btb(lib, bits=NULL) == 1
+    assert btb(lib, cnt=NULL) == 1
+    assert btb(lib, bits=FAKE + 4) == 3
+    assert btb(lib, B=0, bits=NULL, pb=NULL, cb=NULL, tab=NULL, cnt=NULL) == 0
 
 
 def pf(lib, q=FAKE, dtype=1, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE,

@@ -452,3 +452,31 @@ def test_append_kv_reads_back_and_touches_nothing_else(seed):
     keep = ~written
     assert np.array_equal(k2.transpose(0, 2, 1, 3)[keep], w.k_pages.transpose(0, 2, 1, 3)[keep])
     assert np.array_equal(v2.transpose(0, 2, 1, 3)[keep], w.v_pages.transpose(0, 2, 1, 3)[keep])
+
+
+# ---- bit-packed masks ---------------------------------------------------------------------------
+
+def test_unpack_mask_bits_worked_example():
+    # two words: word 0 = bits 0, 1 and 63 set; word 1 = bit 5 set (block 69); 72 blocks
+    w = np.zeros((1, 1, 1, 2), dtype=np.uint64)
+    w[0, 0, 0, 0] = np.uint64((1 << 0) | (1 << 1) | (1 << 63))
+    w[0, 0, 0, 1] = np.uint64(1 << 5) | np.uint64(1 << 20)   # bit 20 = block 84: past 72, dropped
+    m = oracle.unpack_mask_bits(w, 72)
+    assert m.shape == (1, 1, 1, 72)
+    assert list(np.nonzero(m[0, 0, 0])[0]) == [0, 1, 63, 69]
+
+
+def test_unpack_mask_bits_matches_per_bit_loop():
+    from workloads.configs import pack_mask_bits
+    rng = np.random.default_rng(3)
+    masks = (rng.random((2, 3, 4, 150)) < 0.3).astype(np.uint8) * rng.integers(1, 256, (2, 3, 4, 150), dtype=np.uint8)
+    bits = pack_mask_bits(masks)
+    assert bits.shape == (2, 3, 4, 3) and bits.dtype == np.uint64
+    for idx in np.ndindex(2, 3, 4):
+        for kb in range(150):
+            word = int(bits[idx][kb // 64])
+            assert ((word >> (kb % 64)) & 1) == (masks[idx][kb] != 0)
+    assert np.array_equal(oracle.unpack_mask_bits(bits, 150), masks != 0)
+    T1, C1 = oracle.block_union_tables(masks, np.array([1, 0], np.int32), np.array([2, 4], np.int32), 3, 150)
+    T2, C2 = oracle.block_union_tables_bits(bits, 150, np.array([1, 0], np.int32), np.array([2, 4], np.int32), 3)
+    assert np.array_equal(T1, T2) and np.array_equal(C1, C2)

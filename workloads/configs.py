@@ -276,6 +276,16 @@ def chunked_sequence_chunk(k: int, dense: bool = False, seed: int | None = None)
     return w
 
 
+def pack_mask_bits(masks: np.ndarray) -> np.ndarray:
+    """Byte masks [B][Hq][nqb][nkvb] (nonzero = selected) as bit-packed uint64 words
+    [B][Hq][nqb][ceil(nkvb/64)]: block kb is bit kb % 64 of word kb // 64 (an input encoding)."""
+    B, Hq, nqb, nkvb = masks.shape
+    words = (nkvb + 63) // 64
+    padded = np.zeros((B, Hq, nqb, words * 64), dtype=np.uint8)
+    padded[..., :nkvb] = masks != 0
+    return np.packbits(padded.reshape(B, Hq, nqb, words, 64), axis=-1, bitorder="little").view(np.uint64)[..., 0]
+
+
 def chunked_sequence_batch(dense: bool = False, seed: int | None = None, n_chunks: int = 64) -> Workload:
     """The first n_chunks chunks of the 131072-token sequence as one varlen batch: sequence k of
     the batch is chunk k (prefix 2048*k, chunk 2048) with the Q, mask and page map of
