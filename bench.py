@@ -233,6 +233,43 @@ def timed(cpa, batches, modes, steps, warmup):
     return out
 
 
+def time_direct(cpa, bt, steps, warmup=3):
+    """The direct block-sparse baseline on the batch's inputs: per-(head, query block) plans
+    (cpa_build_block_plans) and the prefill over them (cpa_chunked_prefill_direct), HIP events
+    around each launch; its FLOPs are those of the plans."""
+    import numpy as np
+    import torch
+    w = bt.w
+    if bt.vp_dim is None:
+        bt.vp_dim = bt.vp.transpose(2, 3).contiguous()
+    plans = torch.empty((w.B, w.Hq, w.nqb_max, w.nkvb_max), dtype=torch.int32, device=bt.q.device)
+    counts = torch.empty((w.B, w.Hq, w.nqb_max), dtype=torch.int32, device=bt.q.device)
+    out = torch.empty_like(bt.q)
+
+    def run():
+        cpa.build_block_plans(bt.masks, bt.pb, bt.cb, plans=plans, plan_counts=counts)
+        cpa.chunked_prefill_direct(bt.q, bt.kp, bt.vp_dim, bt.pm, plans, counts, bt.cu, bt.pl, w.max_chunk_len,
+                                   out=out)
+
+    for _ in range(warmup):
+        run()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        cpa.build_block_plans(bt.masks, bt.pb, bt.cb, plans=plans, plan_counts=counts)
+        e[1].record()
+        cpa.chunked_prefill_direct(bt.q, bt.kp, bt.vp_dim, bt.pm, plans, counts, bt.cu, bt.pl, w.max_chunk_len,
+                                   out=out)
+        e[2].record()
+    torch.cuda.synchronize()
+    build = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    pre = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    flop = cpa.plan_flops(plans.cpu().numpy(), counts.cpu().numpy(), w.prefix_len, w.chunk_len, w.d)
+    return {"plan_build_us": round(build * 1e3, 2), "prefill_ms": round(pre, 4), "step_ms": round(build + pre, 4),
+            "flop": int(flop), "prefill_tflops": round(flop / (pre * 1e-3) / 1e12, 2),
+            "plan_blocks": int(counts.sum())}
+
+
 def time_build_bits(cpa, batches, steps):
     """HIP-event time of the table build from bit-packed masks (cpa_build_block_tables_bits) for
     every launch pair of the workload, and whether its tables equal the byte-mask build's."""
@@ -373,6 +410,12 @@ def main():
         layout_ab = {args.v_layout: round(again["prefill_ms"], 4), other: round(alt["prefill_ms"], 4)}
         log(f"[bench] V layout A/B prefill ms: {layout_ab}")
 
+    direct = None
+    if len(batches) == 1 and batches[0].split_pages == 0:
+        direct = time_direct(cpa, batches[0], max(5, args.steps // 2))
+        log(f"[bench] direct block-sparse baseline: plans {direct['plan_build_us']:.1f} us, prefill "
+            f"{direct['prefill_ms']:.3f} ms ({direct['prefill_tflops']:.0f} TFLOP/s on {direct['flop']:.3e} "
+            f"FLOP, {direct['plan_blocks']} plan blocks)")
     bits = time_build_bits(cpa, batches, max(5, args.steps))
     log(f"[bench] table build from bit-packed masks: {bits['us']:.1f} us ({bits['mask_bytes']} mask bytes), "
         f"tables equal: {bits['tables_equal_byte_masks']}")
@@ -434,6 +477,9 @@ def main():
     if append is not None:
         result["kv_append"] = append
     result["table_build_bit_masks"] = bits
+    if direct is not None:
+        direct["union_speedup_over_direct"] = round(direct["step_ms"] / r["step_ms"], 4)
+        result["direct_block_sparse_baseline"] = direct
     if unsplit is not None:
         result["split_kv"] = {"split_pages": batches[0].split_pages,
                               "unsplit_prefill_ms": round(unsplit["prefill_ms"], 4),

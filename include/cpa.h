@@ -245,6 +245,48 @@ cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, 
                          const int32_t* prefix_len, int B, int Hkv, int d, int max_chunk_len,
                          hipStream_t stream);
 
+/*
+ * cpa_build_block_plans - per-(head, query block) KV block plans: the direct block-sparse
+ * execution that the Q-block and intra-group unions of the CompactAttention abstract replace
+ * (the abstract's point of comparison: block-sparse kernels that run each head's mask as it is
+ * lose efficiency when the query length is bounded by the chunk size).  No union: row
+ * (b, h, qi) of the plan lists the blocks kb with masks[b][h][qi][kb] != 0 and
+ * kb <= prefix_blocks[b] + qi, ascending, then -1 up to plan_cap; rows qi >= chunk_blocks[b]
+ * are empty.
+ *
+ *   masks, B, Hq, nqb_max, nkvb_max, prefix_blocks, chunk_blocks  as cpa_build_block_tables.
+ *   plans       (out) int32 [B][Hq][nqb_max][plan_cap], plan_cap >= nkvb_max.
+ *   plan_counts (out) int32 [B][Hq][nqb_max].
+ * Errors: CPA_ERR_NULL, CPA_ERR_SHAPE, CPA_ERR_CAPACITY (plan_cap < nkvb_max), CPA_ERR_LAUNCH.
+ * Bit-exact: the plans have exactly one correct value.
+ */
+cpa_status cpa_build_block_plans(const uint8_t* masks, int B, int Hq, int nqb_max, int nkvb_max,
+                                 const int32_t* prefix_blocks, const int32_t* chunk_blocks, int32_t* plans,
+                                 int plan_cap, int32_t* plan_counts, hipStream_t stream);
+
+/*
+ * cpa_chunked_prefill_direct - chunked-prefill attention in which every (sequence, query head,
+ * query block) attends over exactly the blocks of its own plan (cpa_build_block_plans), read in
+ * place from the paged cache, with the causal cut of cpa_chunked_prefill.  It is per-query
+ * block-sparse attention with the original masks, the baseline the union tables are measured
+ * against, on the same numerics as the bf16 path of cpa_chunked_prefill.
+ *
+ * Arguments as cpa_chunked_prefill_vt (token-major K, dim-major V), with the plans in place of
+ * the tables: plans / plan_cap / plan_counts from cpa_build_block_plans and its nqb_max
+ * (>= ceil(max_chunk_len / 64)).  o, lse as cpa_chunked_prefill: a row whose plan reaches no
+ * visible key gets O = 0 and LSE = -inf; an unresolvable page id reads as NaN.
+ * Supported: CPA_BF16, d in {64, 128}, G = Hq / Hkv any divisor.
+ * Errors: CPA_ERR_NULL, CPA_ERR_SHAPE, CPA_ERR_ALIGN, CPA_ERR_UNSUPPORTED, CPA_ERR_LAUNCH.
+ */
+cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                                      int64_t head_stride, int64_t token_stride, const void* v_pages,
+                                      int64_t v_page_stride, int64_t v_head_stride, int64_t v_dim_stride,
+                                      int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                                      const int32_t* plans, int plan_cap, const int32_t* plan_counts,
+                                      int nqb_max, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq,
+                                      int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+                                      hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (host pointer, never NULL). */
 const char* cpa_status_string(cpa_status s);
 

@@ -19,9 +19,16 @@ Pin status (what each function is checked against besides itself):
                        closed forms (constant V, q=0, single key), LSE-merge identity,
                        page-permutation invariance
   attention_rows       pinned: equals paged_attention on every row it is given
+  block_plans          pinned: per-row loop over the definition; G = 1 / one query block equals
+                       the union table
+  block_sparse_attention / block_sparse_rows
+                       pinned: torch SDPA with an explicit per-(head, row) boolean mask over
+                       contiguous K/V; equals paged_attention on the union tables when every
+                       head of a group shares one mask constant over the query blocks
   append_kv            pinned: a worked example written out by hand; the appended rows read
                        back through logical positions; every other slot unchanged
 """
 from .union import block_union_tables, block_union_tables_bits, unpack_mask_bits  # noqa: F401
 from .attention import paged_attention, attention_rows  # noqa: F401
 from .append import append_kv  # noqa: F401
+from .direct import block_plans, block_sparse_attention, block_sparse_rows  # noqa: F401

@@ -9,6 +9,8 @@ Thin wrappers over the C ABI in include/cpa.h:
                   max_chunk_len, split_pages=0, v_layout="token") -> (o, lse)
   (split_pages > 0: split-KV over page ranges with an LSE merge; plan_split_pages picks one;
   v_layout "dim": V pages stored [page][group][d][64])
+* build_block_plans(masks, prefix_blocks, chunk_blocks) and chunked_prefill_direct(...): the
+  direct block-sparse baseline, every (head, query block) over its own mask row
 * append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len,
             v_layout="token"): the chunk's K/V rows into the paged cache
 
@@ -19,9 +21,12 @@ from .api import (  # noqa: F401
     BLOCK,
     append_kv,
     attention_flops,
+    build_block_plans,
     build_block_tables,
     build_block_tables_bits,
     chunked_prefill,
+    chunked_prefill_direct,
+    plan_flops,
     plan_split_pages,
     prefill_tiles,
     split_workspace_bytes,

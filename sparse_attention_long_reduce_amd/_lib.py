@@ -5,9 +5,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpa.so")
 
-EXPORTS = ("cpa_append_kv", "cpa_build_block_tables", "cpa_build_block_tables_bits", "cpa_chunked_prefill",
-           "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string",
-           "cpa_version")
+EXPORTS = ("cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables", "cpa_build_block_tables_bits",
+           "cpa_chunked_prefill", "cpa_chunked_prefill_direct", "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt",
+           "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version")
 
 _lib = None
 
@@ -27,6 +27,11 @@ def load():
     lib.cpa_build_block_tables.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
     lib.cpa_build_block_tables_bits.restype = i32
     lib.cpa_build_block_tables_bits.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.cpa_build_block_plans.restype = i32
+    lib.cpa_build_block_plans.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp]
+    lib.cpa_chunked_prefill_direct.restype = i32
+    lib.cpa_chunked_prefill_direct.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, i64, i64, i64, vp, i32, vp, i32,
+                                               vp, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
     lib.cpa_chunked_prefill.restype = i32
     lib.cpa_chunked_prefill.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, vp,
                                         vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]

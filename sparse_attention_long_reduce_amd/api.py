@@ -84,6 +84,87 @@ def build_block_tables_bits(mask_bits, nkvb_max, prefix_blocks, chunk_blocks, Hk
     return tables, counts
 
 
+def build_block_plans(masks, prefix_blocks, chunk_blocks, plan_cap=None, plans=None, plan_counts=None,
+                      stream=None):
+    """masks uint8 [B][Hq][nqb_max][nkvb_max] (CUDA) -> per-(head, query block) plans of the
+    direct block-sparse baseline: (plans int32 [B][Hq][nqb_max][cap], counts int32 [B][Hq][nqb_max])."""
+    if not (masks.is_cuda and masks.dtype == torch.uint8 and masks.is_contiguous() and masks.dim() == 4):
+        raise TypeError("masks must be a contiguous 4-D uint8 CUDA tensor")
+    B, Hq, nqb_max, nkvb_max = masks.shape
+    _dev_i32(prefix_blocks, "prefix_blocks")
+    _dev_i32(chunk_blocks, "chunk_blocks")
+    cap = nkvb_max if plan_cap is None else int(plan_cap)
+    if plans is None:
+        plans = torch.empty((B, Hq, nqb_max, cap), dtype=torch.int32, device=masks.device)
+    if plan_counts is None:
+        plan_counts = torch.empty((B, Hq, nqb_max), dtype=torch.int32, device=masks.device)
+    _dev_i32(plans, "plans")
+    _dev_i32(plan_counts, "plan_counts")
+    if plans.numel() != B * Hq * nqb_max * cap or plan_counts.numel() != B * Hq * nqb_max:
+        raise ValueError("plans/plan_counts have the wrong size")
+    st = load().cpa_build_block_plans(_ptr(masks), B, Hq, nqb_max, nkvb_max, _ptr(prefix_blocks),
+                                      _ptr(chunk_blocks), _ptr(plans), cap, _ptr(plan_counts), _stream(stream))
+    if st != 0:
+        raise CpaError(st, "cpa_build_block_plans")
+    return plans, plan_counts
+
+
+def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu_q, prefix_len, max_chunk_len,
+                           sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None):
+    """Direct block-sparse baseline: each (head, query block) over its own plan.  q bf16
+    [Tq][Hq][d]; k_pages [n_pages][Hkv][64][d]; v_pages dim-major [n_pages][Hkv][d][64] (strided
+    views allowed as in chunked_prefill); plans / plan_counts from build_block_plans."""
+    if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("the direct baseline runs bf16 q, k_pages and v_pages")
+    if q.dim() != 3 or not q.is_contiguous():
+        raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
+    Tq, Hq, d = q.shape
+    if k_pages.dim() != 4 or k_pages.shape[2] != BLOCK or k_pages.shape[3] != d or k_pages.stride(3) != 1:
+        raise ValueError("k_pages must be [n_pages][Hkv][64][d] with d contiguous")
+    n_pages, Hkv = k_pages.shape[0], k_pages.shape[1]
+    if v_pages.dim() != 4 or tuple(v_pages.shape) != (n_pages, Hkv, d, BLOCK) or v_pages.stride(3) != 1:
+        raise ValueError("v_pages must be dim-major [n_pages][Hkv][d][64] with the token dimension contiguous")
+    for t, nm in ((page_map, "page_map"), (plans, "plans"), (plan_counts, "plan_counts"), (cu_q, "cu_q"),
+                  (prefix_len, "prefix_len")):
+        _dev_i32(t, nm)
+    B = prefix_len.numel()
+    if plans.dim() != 4 or plans.shape[0] != B or plans.shape[1] != Hq:
+        raise ValueError("plans must be [B][Hq][nqb_max][cap]")
+    nqb_max, cap = plans.shape[2], plans.shape[3]
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
+    st = load().cpa_chunked_prefill_direct(
+        _ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
+        v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1],
+        _ptr(plans), cap, _ptr(plan_counts), nqb_max, _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
+        int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), _stream(stream))
+    if st != 0:
+        raise CpaError(st, "cpa_chunked_prefill_direct")
+    return out, lse
+
+
+def plan_flops(plans, plan_counts, prefix_len, chunk_len, d):
+    """FLOPs of the direct baseline, 4*d per causally visible (query, key) pair of every
+    (head, query block) plan, from host copies (numpy) of the plans."""
+    import numpy as np
+    total = 0
+    B, Hq, nqb_max, _ = plans.shape
+    for b in range(B):
+        P, C = int(prefix_len[b]), int(chunk_len[b])
+        for qi in range((C + BLOCK - 1) // BLOCK):
+            r = np.arange(BLOCK * qi, min(C, BLOCK * qi + BLOCK), dtype=np.int64)
+            for h in range(Hq):
+                ids = np.asarray(plans[b, h, qi, :plan_counts[b, h, qi]], dtype=np.int64)
+                full = ids[ids * BLOCK + BLOCK - 1 <= P + BLOCK * qi]   # blocks wholly before the query block
+                pairs = int(full.size) * BLOCK * r.size
+                for kb in ids[ids * BLOCK + BLOCK - 1 > P + BLOCK * qi]:
+                    pairs += int(np.clip(P + r - kb * BLOCK + 1, 0, BLOCK).sum())
+                total += pairs
+    return 4 * d * total
+
+
 def prefill_tiles(B, Hq, Hkv, max_chunk_len):
     """Workgroups cpa_chunked_prefill launches without split-KV (one per group and query tile):
     a tile is the group's heads (up to 4 per workgroup) times 1, 2 or 4 query blocks."""

@@ -9,7 +9,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libcpa.so")
-SOURCES = ("block_union.hip", "prefill_regstaged.hip", "prefill_bf16.hip", "kv_append.hip", "cpa_api.hip")
+SOURCES = ("block_union.hip", "block_plans.hip", "prefill_regstaged.hip", "prefill_bf16.hip", "prefill_direct.hip",
+           "kv_append.hip", "cpa_api.hip")
 ARCH = os.environ.get("CPA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -22,7 +23,7 @@ FLAGS = [
 
 
 # per-source extra flags
-EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefill_direct.hip": ["-fno-honor-nans"]}
 
 
 def _run(cmd):

@@ -192,6 +192,61 @@ cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, 
   return cpa::launch_kv_append(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
+cpa_status cpa_build_block_plans(const uint8_t* masks, int B, int Hq, int nqb_max, int nkvb_max,
+                                 const int32_t* prefix_blocks, const int32_t* chunk_blocks, int32_t* plans,
+                                 int plan_cap, int32_t* plan_counts, hipStream_t stream) {
+  if (B < 0 || Hq < 0 || nqb_max < 0 || nkvb_max < 0 || plan_cap < 0) return CPA_ERR_SHAPE;
+  if (nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
+  if (plan_cap < nkvb_max) return CPA_ERR_CAPACITY;
+  if ((long long)B * Hq * nqb_max == 0) return CPA_OK;
+  if (!prefix_blocks || !chunk_blocks || !plan_counts) return CPA_ERR_NULL;
+  if (plan_cap > 0 && !plans) return CPA_ERR_NULL;
+  if (nkvb_max > 0 && !masks) return CPA_ERR_NULL;
+  cpa::PlanArgs a{masks, B, Hq, nqb_max, nkvb_max, prefix_blocks, chunk_blocks, plans, plan_cap, plan_counts};
+  return cpa::launch_block_plans(a, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                                      int64_t head_stride, int64_t token_stride, const void* v_pages,
+                                      int64_t v_page_stride, int64_t v_head_stride, int64_t v_dim_stride,
+                                      int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                                      const int32_t* plans, int plan_cap, const int32_t* plan_counts,
+                                      int nqb_max, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq,
+                                      int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+                                      hipStream_t stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || plan_cap < 0 || n_pages < 0 || nqb_max < 0)
+    return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (!(sm_scale >= 0.f) || std::isinf(sm_scale)) return CPA_ERR_SHAPE;
+  if (dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
+  if (nqb_max < (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK) return CPA_ERR_SHAPE;
+  if (B == 0 || max_chunk_len == 0) return CPA_OK;
+  if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
+    return CPA_ERR_SHAPE;
+  if (v_dim_stride < 64 || v_head_stride < (int64_t)d * v_dim_stride || v_page_stride < (int64_t)Hkv * v_head_stride)
+    return CPA_ERR_SHAPE;
+  if (!q || !k_pages || !v_pages || !page_map || !plan_counts || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
+  if (plan_cap > 0 && !plans) return CPA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return CPA_ERR_ALIGN;
+  if ((token_stride * 2) % 16 || (head_stride * 2) % 16 || (page_stride * 2) % 16) return CPA_ERR_ALIGN;
+  if ((v_dim_stride * 2) % 16 || (v_head_stride * 2) % 16 || (v_page_stride * 2) % 16) return CPA_ERR_ALIGN;
+  cpa::DirectArgs a{};
+  a.q = q; a.k = k_pages; a.v = v_pages;
+  a.page_stride = page_stride; a.head_stride = head_stride; a.token_stride = token_stride;
+  a.v_page_stride = v_page_stride; a.v_head_stride = v_head_stride; a.v_dim_stride = v_dim_stride;
+  a.n_pages = n_pages; a.page_map = page_map; a.page_map_stride = page_map_stride;
+  a.plans = plans; a.plan_cap = plan_cap; a.plan_counts = plan_counts;
+  a.cu_q = cu_q; a.prefix_len = prefix_len;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_chunk_len = max_chunk_len; a.nqb_max = nqb_max;
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt((float)d);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o = o; a.lse = lse;
+  a.xcd_remap = B * Hkv >= 8 ? 1 : 0;
+  return cpa::launch_prefill_direct(a, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
 size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int split_pages) {
   if (total_q <= 0 || Hq <= 0 || d <= 0 || table_cap <= 0 || split_pages <= 0) return 0;
   const size_t n_splits = ((size_t)table_cap + split_pages - 1) / split_pages;

@@ -85,6 +85,40 @@ struct AppendArgs {
   int B, Hkv, max_chunk_len;
 };
 
+// per-(head, query block) plans of the direct block-sparse baseline
+struct PlanArgs {
+  const uint8_t* masks;   // [B][Hq][nqb_max][nkvb_max]
+  int B, Hq, nqb_max, nkvb_max;
+  const int32_t* prefix_blocks;
+  const int32_t* chunk_blocks;
+  int32_t* plans;         // [B][Hq][nqb_max][plan_cap]
+  int plan_cap;
+  int32_t* plan_counts;   // [B][Hq][nqb_max]
+};
+
+// direct block-sparse prefill (bf16, dim-major V): every wave runs one (head, query block, half)
+// over its own plan, operands loaded from memory straight into registers
+struct DirectArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t page_stride, head_stride, token_stride;          // K, token-major
+  int64_t v_page_stride, v_head_stride, v_dim_stride;      // V, dim-major
+  int64_t n_pages;
+  const int32_t* page_map;
+  int page_map_stride;
+  const int32_t* plans;
+  int plan_cap;
+  const int32_t* plan_counts;
+  const int32_t* cu_q;
+  const int32_t* prefix_len;
+  int B, Hq, Hkv, max_chunk_len, nqb_max;
+  float scale_log2;
+  void* o;
+  float* lse;
+  int xcd_remap;
+};
+
 // All return hipSuccess or the launch error; they never synchronise.
 hipError_t launch_block_union(const UnionArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
@@ -94,5 +128,7 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s);
 // as the reference point of the direct-to-LDS bf16 kernel
 hipError_t launch_prefill_regstaged(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs& a, bool bf16, int d, hipStream_t s);
+hipError_t launch_block_plans(const PlanArgs& a, hipStream_t s);
+hipError_t launch_prefill_direct(const DirectArgs& a, int d, hipStream_t s);
 
 }  // namespace cpa

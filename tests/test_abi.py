@@ -27,9 +27,10 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"cpa_append_kv", "cpa_build_block_tables", "cpa_build_block_tables_bits",
-                          "cpa_chunked_prefill", "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt",
-                          "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
+    assert set(names) == {"cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables",
+                          "cpa_build_block_tables_bits", "cpa_chunked_prefill", "cpa_chunked_prefill_direct",
+                          "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes",
+                          "cpa_status_string", "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -199,6 +200,44 @@ def test_append_validation(lib):
     assert ap(lib, mcl=0, kn=NULL) == 0
 
 
+def bp(lib, masks=FAKE, B=1, Hq=8, nqb=4, nkvb=16, pb=FAKE, cb=FAKE, plans=FAKE, cap=16, cnt=FAKE):
+    return lib.cpa_build_block_plans(masks, B, Hq, nqb, nkvb, pb, cb, plans, cap, cnt, None)
+
+
+def test_build_plans_validation(lib):
+    assert bp(lib, B=-1) == 2
+    assert bp(lib, nkvb=65537, cap=70000) == 2
+    assert bp(lib, cap=15) == 5
+    assert bp(lib, masks=NULL) == 1
+    assert bp(lib, plans=NULL) == 1
+    assert bp(lib, cnt=NULL) == 1
+    assert bp(lib, B=0, masks=NULL, pb=NULL, cb=NULL, plans=NULL, cnt=NULL) == 0
+
+
+def pd(lib, q=FAKE, dtype=1, k=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, v=FAKE, vps=8 * 128 * 64, vhs=128 * 64,
+       vds=64, npages=10, pm=FAKE, pms=16, plans=FAKE, cap=16, cnt=FAKE, nqb=4, cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8,
+       d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL):
+    return lib.cpa_chunked_prefill_direct(q, dtype, k, ps, hs, ts, v, vps, vhs, vds, npages, pm, pms, plans, cap,
+                                          cnt, nqb, cu, pl, B, Hq, Hkv, d, mcl, scale, o, lse, None)
+
+
+def test_direct_validation(lib):
+    assert pd(lib, dtype=0) == 4               # bf16 only
+    assert pd(lib, d=96) == 4
+    assert pd(lib, Hq=30) == 2
+    assert pd(lib, nqb=3) == 2                 # plans must cover ceil(256 / 64) query blocks
+    assert pd(lib, vds=63) == 2
+    assert pd(lib, vhs=127 * 64) == 2
+    assert pd(lib, ts=64) == 2
+    assert pd(lib, scale=-1.0) == 2
+    assert pd(lib, q=NULL) == 1
+    assert pd(lib, plans=NULL) == 1
+    assert pd(lib, cnt=NULL) == 1
+    assert pd(lib, v=FAKE + 2) == 3
+    assert pd(lib, vds=68, vhs=128 * 68, vps=8 * 128 * 68) == 3
+    assert pd(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, plans=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
+
+
 def test_split_planner():
     # one KV group of a 128K context (4 query heads, 2048-row chunk): 32 tiles on 256 CUs
     assert cpa.prefill_tiles(1, 4, 1, 2048) == 32
@@ -230,3 +269,21 @@ def test_attention_flops_matches_oracle_visible_counts():
     _, _, NV = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q,
                                       w.prefix_len, w.Hkv, return_nvis=True)
     assert cpa.attention_flops(T, C, w.prefix_len, w.chunk_len, w.Hq, w.Hkv, w.d) == 4 * w.d * int(NV.sum())
+
+
+def test_plan_flops_matches_oracle_visible_counts():
+    import numpy as np
+    import oracle
+    from workloads import make_workload
+    from workloads.configs import mask_bernoulli
+    w = make_workload("pf", [128, 320, 0], [128, 100, 64], 8, 2, 8, "f32",
+                      lambda rng, *a: mask_bernoulli(rng, *a, p=0.3, local=1), 4)
+    P, C = oracle.block_plans(w.masks, w.prefix_blocks, w.chunk_blocks, w.nkvb_max)
+    pairs = 0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            for r in range(int(w.chunk_len[b])):
+                qi = r // 64
+                for kb in P[b, h, qi, :C[b, h, qi]].tolist():
+                    pairs += sum(1 for t in range(64 * kb, 64 * kb + 64) if t <= int(w.prefix_len[b]) + r)
+    assert cpa.plan_flops(P, C, w.prefix_len, w.chunk_len, w.d) == 4 * w.d * pairs

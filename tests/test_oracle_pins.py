@@ -480,3 +480,68 @@ def test_unpack_mask_bits_matches_per_bit_loop():
     T1, C1 = oracle.block_union_tables(masks, np.array([1, 0], np.int32), np.array([2, 4], np.int32), 3, 150)
     T2, C2 = oracle.block_union_tables_bits(bits, 150, np.array([1, 0], np.int32), np.array([2, 4], np.int32), 3)
     assert np.array_equal(T1, T2) and np.array_equal(C1, C2)
+
+
+# ---- direct block-sparse baseline ----------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,noise", [(21, 0.0), (22, 0.4)])
+def test_block_plans_equal_loop_definition(seed, noise):
+    w = small(seed, G=2, Hkv=2, d=8, prefix=(128, 0, 640), chunk=(192, 37, 100), p=0.3, noise=noise, values=True)
+    plans, counts = oracle.block_plans(w.masks, w.prefix_blocks, w.chunk_blocks, w.nkvb_max + 3)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            for qi in range(w.nqb_max):
+                expect = []
+                if qi < w.chunk_blocks[b]:
+                    for kb in range(w.nkvb_max):
+                        if w.masks[b, h, qi, kb] != 0 and kb <= w.prefix_blocks[b] + qi:
+                            expect.append(kb)
+                assert counts[b, h, qi] == len(expect)
+                assert plans[b, h, qi].tolist() == expect + [-1] * (w.nkvb_max + 3 - len(expect))
+
+
+def test_block_plans_one_head_one_block_is_the_union_table():
+    # G = 1 and a one-block chunk: nothing to union, the plan is the group's table
+    w = small(23, G=1, Hkv=3, d=8, prefix=(256, 64), chunk=(64, 50), p=0.3)
+    plans, counts = oracle.block_plans(w.masks, w.prefix_blocks, w.chunk_blocks, w.nkvb_max)
+    T, C = tables_of(w)
+    assert np.array_equal(plans[:, :, 0], T) and np.array_equal(counts[:, :, 0], C)
+
+
+@pytest.mark.parametrize("chunk", [(192, 64), (150, 37)])
+def test_block_sparse_attention_is_sdpa_with_the_block_mask(chunk):
+    w = small(24, G=2, Hkv=2, d=16, prefix=(128, 320), chunk=chunk, p=0.25)
+    plans, counts = oracle.block_plans(w.masks, w.prefix_blocks, w.chunk_blocks, w.nkvb_max)
+    O, L = oracle.block_sparse_attention(w.q, w.k_pages, w.v_pages, w.page_map, plans, counts, w.cu_q,
+                                         w.prefix_len, w.Hkv)
+
+    def token_mask(b, h):   # each row's own mask row, written out per token
+        P, Cn = int(w.prefix_len[b]), int(w.chunk_len[b])
+        m = np.zeros((Cn, P + Cn), dtype=bool)
+        for r in range(Cn):
+            for kb in range((P + Cn + BLOCK - 1) // BLOCK):
+                if w.masks[b, h, r // BLOCK, kb]:
+                    m[r, kb * BLOCK:(kb + 1) * BLOCK] = True
+        return m
+    Os, Ls = sdpa_dense(w, token_mask)
+    assert np.max(np.abs(O - Os)) < 1e-12
+    assert np.max(np.abs(L - Ls)) < 1e-12
+    S = np.array([(b, h, r) for b in range(w.B) for h in range(w.Hq) for r in range(0, int(w.chunk_len[b]), 7)])
+    Or, Lr = oracle.block_sparse_rows(w.q, w.k_pages, w.v_pages, w.page_map, plans, counts, w.cu_q,
+                                      w.prefix_len, w.Hkv, S)
+    # one row at a time against blocks of 64 rows: the same definition up to BLAS summation order
+    assert np.max(np.abs(Or - O[w.cu_q[S[:, 0]] + S[:, 2], S[:, 1]])) < 1e-13
+    assert np.max(np.abs(Lr - L[S[:, 1], w.cu_q[S[:, 0]] + S[:, 2]])) < 1e-13
+
+
+def test_block_sparse_equals_union_when_masks_are_shared_and_constant():
+    def fn(rng, Hq, Hkv, qb0, nqb, nkvb):
+        s = rng.random((Hkv, nkvb)) < 0.3
+        s[:, 0] = True
+        return np.broadcast_to(np.repeat(s, Hq // Hkv, axis=0)[:, None, :], (Hq, nqb, nkvb)).copy()
+    w = small(25, G=4, Hkv=2, d=16, prefix=(256, 512), chunk=(128, 192), fn=fn)
+    plans, counts = oracle.block_plans(w.masks, w.prefix_blocks, w.chunk_blocks, w.nkvb_max)
+    O, L = oracle.block_sparse_attention(w.q, w.k_pages, w.v_pages, w.page_map, plans, counts, w.cu_q,
+                                         w.prefix_len, w.Hkv)
+    Ou, Lu = run_oracle(w)
+    assert np.max(np.abs(O - Ou)) < 1e-12 and np.max(np.abs(L - Lu)) < 1e-12
