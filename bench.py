@@ -270,6 +270,34 @@ def time_direct(cpa, bt, steps, warmup=3):
             "plan_blocks": int(counts.sum())}
 
 
+def time_fp8kv(cpa, bt, steps, warmup=3):
+    """The batch's prefill over an fp8 (e4m3) copy of its KV cache, per-tensor scale 1/4
+    (cpa_chunked_prefill_fp8kv, token-major V), HIP events around each launch."""
+    import numpy as np
+    import torch
+    w = bt.w
+    f8 = torch.float8_e4m3fn
+    kp8 = (torch.from_numpy(w.k_pages) * 4.0).to(f8).to(bt.q.device)
+    vp8 = (torch.from_numpy(w.v_pages) * 4.0).to(f8).to(bt.q.device)
+    out = torch.empty_like(bt.q)
+
+    def run():
+        cpa.chunked_prefill(bt.q, kp8, vp8, bt.pm, bt.tables, bt.counts, bt.cu, bt.pl, w.max_chunk_len, out=out,
+                            k_scale=0.25, v_scale=0.25)
+
+    for _ in range(warmup):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    return {"prefill_ms": round(ms, 4), "kv_bytes": int(kp8.numel() + vp8.numel()),
+            "kv_bytes_bf16": int(2 * (kp8.numel() + vp8.numel()))}
+
+
 def time_build_bits(cpa, batches, steps):
     """HIP-event time of the table build from bit-packed masks (cpa_build_block_tables_bits) for
     every launch pair of the workload, and whether its tables equal the byte-mask build's."""
@@ -416,6 +444,12 @@ def main():
         log(f"[bench] direct block-sparse baseline: plans {direct['plan_build_us']:.1f} us, prefill "
             f"{direct['prefill_ms']:.3f} ms ({direct['prefill_tflops']:.0f} TFLOP/s on {direct['flop']:.3e} "
             f"FLOP, {direct['plan_blocks']} plan blocks)")
+    fp8kv = None
+    if len(batches) == 1 and batches[0].split_pages == 0:
+        fp8kv = time_fp8kv(cpa, batches[0], max(5, args.steps // 2))
+        fp8kv["prefill_tflops"] = round(flops / (fp8kv["prefill_ms"] * 1e-3) / 1e12, 2)
+        log(f"[bench] fp8 KV cache: prefill {fp8kv['prefill_ms']:.3f} ms ({fp8kv['prefill_tflops']:.0f} TFLOP/s), "
+            f"cache {fp8kv['kv_bytes'] / 2**20:.0f} MiB vs {fp8kv['kv_bytes_bf16'] / 2**20:.0f} MiB bf16")
     bits = time_build_bits(cpa, batches, max(5, args.steps))
     log(f"[bench] table build from bit-packed masks: {bits['us']:.1f} us ({bits['mask_bytes']} mask bytes), "
         f"tables equal: {bits['tables_equal_byte_masks']}")
@@ -477,6 +511,8 @@ def main():
     if append is not None:
         result["kv_append"] = append
     result["table_build_bit_masks"] = bits
+    if fp8kv is not None:
+        result["fp8_kv"] = fp8kv
     if direct is not None:
         direct["union_speedup_over_direct"] = round(direct["step_ms"] / r["step_ms"], 4)
         result["direct_block_sparse_baseline"] = direct

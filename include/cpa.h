@@ -46,7 +46,11 @@ typedef enum {
   CPA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch                      */
 } cpa_status;
 
-typedef enum { CPA_F32 = 0, CPA_BF16 = 1 } cpa_dtype;
+typedef enum {
+  CPA_F32 = 0,
+  CPA_BF16 = 1,
+  CPA_FP8_E4M3 = 2 /* OCP e4m3 (bias 7, no infinities); KV pools only (cpa_chunked_prefill_fp8kv, cpa_append_kv) */
+} cpa_dtype;
 
 /*
  * cpa_build_block_tables - masks -> minimal GQA-aware per-group KV block tables + counts.
@@ -233,7 +237,7 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
  * last page past the chunk stay as they were.  A page whose logical block is >= page_map_stride
  * or whose id is outside [0, n_pages) is skipped (its rows are not written).  A copy: the pool
  * holds the input bits exactly.  Calls must not overlap with a prefill reading the same pages.
- * Supported: CPA_BF16 and CPA_F32, d in {64, 128}.
+ * Supported: CPA_BF16, CPA_F32 and CPA_FP8_E4M3 (all three tensors in that dtype), d in {64, 128}.
  * Errors: CPA_ERR_NULL, CPA_ERR_SHAPE (negative sizes, strides too small to hold a page,
  * v_dim_major not 0 or 1, page_map_stride < 1), CPA_ERR_ALIGN (16-byte alignment of pointers
  * and strides), CPA_ERR_UNSUPPORTED, CPA_ERR_LAUNCH.
@@ -286,6 +290,29 @@ cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void
                                       int nqb_max, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq,
                                       int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
                                       hipStream_t stream);
+
+/*
+ * cpa_chunked_prefill_fp8kv - cpa_chunked_prefill with bf16 q / o and a KV cache of fp8 pages
+ * (OCP e4m3, one byte per element): the same attention over the same tables (CompactAttention
+ * abstract), over the dequantized keys and values bf16(fp32(k) * k_scale) and
+ * bf16(fp32(v) * v_scale).  Pages are dequantized on their way into LDS; the attention is the
+ * bf16 path's (bf16 MFMA, fp32 softmax, bf16 P).  The cache takes half the memory of bf16.
+ *
+ *   k_pages     e4m3 pool, token-major, strides (page, head, token) in elements = bytes.
+ *   v_pages     e4m3 pool, token-major (v_dim_major = 0, v_row_stride = token stride) or
+ *               dim-major (v_dim_major = 1, v_row_stride = dim stride), strides in bytes.
+ *   k_scale, v_scale  finite, > 0 (else CPA_ERR_SHAPE): the per-tensor dequantization scales.
+ * Other arguments and errors as cpa_chunked_prefill (dtype bf16 for q and o; strides 16-byte
+ * multiples).  This path stages pages through registers: no split-KV form.
+ */
+cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const void* v_pages, int64_t page_stride,
+                                     int64_t head_stride, int64_t token_stride, int v_dim_major,
+                                     int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride,
+                                     float k_scale, float v_scale, int64_t n_pages, const int32_t* page_map,
+                                     int page_map_stride, const int32_t* tables, int table_cap,
+                                     const int32_t* counts, const int32_t* cu_q, const int32_t* prefix_len, int B,
+                                     int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (host pointer, never NULL). */
 const char* cpa_status_string(cpa_status s);

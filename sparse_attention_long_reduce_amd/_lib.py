@@ -6,8 +6,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpa.so")
 
 EXPORTS = ("cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables", "cpa_build_block_tables_bits",
-           "cpa_chunked_prefill", "cpa_chunked_prefill_direct", "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt",
-           "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version")
+           "cpa_chunked_prefill", "cpa_chunked_prefill_direct", "cpa_chunked_prefill_fp8kv",
+           "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string",
+           "cpa_version")
 
 _lib = None
 
@@ -32,6 +33,9 @@ def load():
     lib.cpa_chunked_prefill_direct.restype = i32
     lib.cpa_chunked_prefill_direct.argtypes = [vp, i32, vp, i64, i64, i64, vp, i64, i64, i64, i64, vp, i32, vp, i32,
                                                vp, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
+    lib.cpa_chunked_prefill_fp8kv.restype = i32
+    lib.cpa_chunked_prefill_fp8kv.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i64, i64, f32, f32, i64, vp, i32,
+                                              vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
     lib.cpa_chunked_prefill.restype = i32
     lib.cpa_chunked_prefill.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, vp,
                                         vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]

@@ -10,8 +10,9 @@ import torch
 from ._lib import CpaError, load
 
 BLOCK = 64
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+_KV_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
 
 def _stream(stream):
@@ -191,7 +192,7 @@ def split_workspace_bytes(total_q, Hq, d, table_cap, split_pages):
 
 def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len,
                     sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None, split_pages=0,
-                    workspace=None, v_layout="token"):
+                    workspace=None, v_layout="token", k_scale=1.0, v_scale=1.0):
     """Attention of each sequence's chunk over its group's table blocks, K/V read in place.
 
     q [Tq][Hq][d]; k_pages [n_pages][Hkv][64][d] (or any strided view with d contiguous);
@@ -202,9 +203,16 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
 
     split_pages > 0 runs split-KV (cpa_chunked_prefill_split) with ranges of that many pages;
     the workspace (a CUDA uint8 tensor of split_workspace_bytes(...) bytes) is allocated here
-    when not given.  v_layout "dim" calls cpa_chunked_prefill_vt.
+    when not given.  v_layout "dim" calls cpa_chunked_prefill_vt.  float8_e4m3fn pools with a
+    bf16 q call cpa_chunked_prefill_fp8kv with the dequantization scales k_scale / v_scale.
     """
-    if q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+    fp8 = k_pages.dtype == torch.float8_e4m3fn
+    if fp8:
+        if q.dtype != torch.bfloat16 or v_pages.dtype != k_pages.dtype:
+            raise TypeError("fp8 pools need float8_e4m3fn k_pages and v_pages and a bfloat16 q")
+        if split_pages:
+            raise ValueError("the fp8 KV path has no split-KV form")
+    elif q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("q, k_pages and v_pages must share dtype float32 or bfloat16")
     if q.dim() != 3 or not q.is_contiguous():
         raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
@@ -240,6 +248,16 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
             k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
             _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
             _ptr(lse))
+    if fp8:
+        st = load().cpa_chunked_prefill_fp8kv(
+            _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
+            1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), float(k_scale),
+            float(v_scale), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
+            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse),
+            _stream(stream))
+        if st != 0:
+            raise CpaError(st, "cpa_chunked_prefill_fp8kv")
+        return out, lse
     split = bool(split_pages and split_pages > 0)
     if split:
         need = split_workspace_bytes(Tq, Hq, d, cap, split_pages)
@@ -276,9 +294,9 @@ def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_ch
     pools in place (cpa_append_kv).  k_pages [n_pages][Hkv][64][d]; v_pages the same (v_layout
     "token") or [n_pages][Hkv][d][64] (v_layout "dim"), strided views allowed as in
     chunked_prefill."""
-    if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype or k_pages.dtype != k_new.dtype \
+    if k_new.dtype not in _KV_DTYPES or v_new.dtype != k_new.dtype or k_pages.dtype != k_new.dtype \
             or v_pages.dtype != k_new.dtype:
-        raise TypeError("k_new, v_new and the pools must share dtype float32 or bfloat16")
+        raise TypeError("k_new, v_new and the pools must share dtype float32, bfloat16 or float8_e4m3fn")
     for t, n in ((k_new, "k_new"), (v_new, "v_new")):
         if not (t.is_cuda and t.dim() == 3 and t.is_contiguous()):
             raise TypeError(f"{n} must be a contiguous [Tq][Hkv][d] CUDA tensor")
@@ -301,7 +319,7 @@ def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_ch
     B = prefix_len.numel()
     if cu_q.numel() != B + 1 or page_map.dim() != 2 or page_map.shape[0] != B:
         raise ValueError("inconsistent B across cu_q / prefix_len / page_map")
-    st = load().cpa_append_kv(_ptr(k_new), _ptr(v_new), _DTYPES[k_new.dtype], _ptr(k_pages), k_pages.stride(0),
+    st = load().cpa_append_kv(_ptr(k_new), _ptr(v_new), _KV_DTYPES[k_new.dtype], _ptr(k_pages), k_pages.stride(0),
                               k_pages.stride(1), k_pages.stride(2), _ptr(v_pages), 1 if v_layout == "dim" else 0,
                               v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), k_pages.shape[0],
                               _ptr(page_map), page_map.shape[1], _ptr(cu_q), _ptr(prefix_len), B, Hkv, d,

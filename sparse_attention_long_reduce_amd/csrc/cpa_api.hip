@@ -164,7 +164,7 @@ cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, 
                          const int32_t* prefix_len, int B, int Hkv, int d, int max_chunk_len,
                          hipStream_t stream) {
   if (B < 0 || Hkv <= 0 || max_chunk_len < 0 || n_pages < 0) return CPA_ERR_SHAPE;
-  if (dtype != CPA_F32 && dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
+  if (dtype != CPA_F32 && dtype != CPA_BF16 && dtype != CPA_FP8_E4M3) return CPA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
   if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
   if (B == 0 || max_chunk_len == 0) return CPA_OK;
@@ -176,7 +176,7 @@ cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, 
       v_page_stride < (int64_t)Hkv * v_head_stride)
     return CPA_ERR_SHAPE;
   if (!k_new || !v_new || !k_pages || !v_pages || !page_map || !cu_q || !prefix_len) return CPA_ERR_NULL;
-  const int eb = dtype == CPA_BF16 ? 2 : 4;
+  const int eb = dtype == CPA_BF16 ? 2 : dtype == CPA_FP8_E4M3 ? 1 : 4;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages)) return CPA_ERR_ALIGN;
   if ((token_stride * eb) % 16 || (head_stride * eb) % 16 || (page_stride * eb) % 16) return CPA_ERR_ALIGN;
   if ((v_row_stride * eb) % 16 || (v_head_stride * eb) % 16 || (v_page_stride * eb) % 16) return CPA_ERR_ALIGN;
@@ -189,7 +189,30 @@ cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, 
   a.page_map = page_map; a.page_map_stride = page_map_stride;
   a.cu_q = cu_q; a.prefix_len = prefix_len;
   a.B = B; a.Hkv = Hkv; a.max_chunk_len = max_chunk_len;
-  return cpa::launch_kv_append(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+  return cpa::launch_kv_append(a, eb, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const void* v_pages, int64_t page_stride,
+                                     int64_t head_stride, int64_t token_stride, int v_dim_major,
+                                     int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride,
+                                     float k_scale, float v_scale, int64_t n_pages, const int32_t* page_map,
+                                     int page_map_stride, const int32_t* tables, int table_cap,
+                                     const int32_t* counts, const int32_t* cu_q, const int32_t* prefix_len, int B,
+                                     int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     hipStream_t stream) {
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale)) return CPA_ERR_SHAPE;
+  if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
+  cpa::PrefillArgs a;
+  bool nothing;
+  const VLayout vl{v_page_stride, v_head_stride, v_row_stride, v_dim_major == 1};
+  const cpa_status st = prepare_prefill(q, CPA_BF16, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
+                                        n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
+                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
+  if (st != CPA_OK || nothing) return st;
+  a.kv_fp8 = 1;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return cpa::launch_prefill_regstaged(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
 cpa_status cpa_build_block_plans(const uint8_t* masks, int B, int Hq, int nqb_max, int nkvb_max,

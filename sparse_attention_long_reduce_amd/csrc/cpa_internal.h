@@ -30,6 +30,10 @@ struct PrefillArgs {
   // (v_dmajor == 1, dim-major pages)
   int64_t v_page_stride, v_head_stride, v_row_stride;
   int v_dmajor;
+  // fp8 KV: the pools hold OCP e4m3 bytes (strides in elements = bytes), dequantized as
+  // bf16(fp32(x) * k_scale) and bf16(fp32(x) * v_scale); q and o are bf16
+  int kv_fp8;
+  float k_scale, v_scale;
   const int32_t* page_map;
   int page_map_stride;
   const int32_t* tables;
@@ -127,7 +131,7 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s);
 // register-staged variant (V transposed through registers); serves fp32 and is kept for bf16
 // as the reference point of the direct-to-LDS bf16 kernel
 hipError_t launch_prefill_regstaged(const PrefillArgs& a, bool bf16, int d, hipStream_t s);
-hipError_t launch_kv_append(const AppendArgs& a, bool bf16, int d, hipStream_t s);
+hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int d, hipStream_t s);
 hipError_t launch_block_plans(const PlanArgs& a, hipStream_t s);
 hipError_t launch_prefill_direct(const DirectArgs& a, int d, hipStream_t s);
 

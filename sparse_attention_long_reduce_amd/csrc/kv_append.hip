@@ -10,7 +10,7 @@
 // The chunk starts on a page boundary (prefix_len is a multiple of 64), so a chunk page maps to
 // one cache page.  K (and token-major V) rows are copied 16 bytes per thread, reads and writes
 // both contiguous along d.  Dim-major V goes through LDS: the 64 x d tile is read row by row
-// and written as d rows of 64 tokens, 16 bytes (8 bf16 or 4 fp32 tokens) per thread.  Slots
+// and written as d rows of 64 tokens, 16 bytes (16 fp8, 8 bf16 or 4 fp32 tokens) per thread.  Slots
 // past the chunk's end are left untouched; a page that cannot be resolved (logical block past
 // page_map_stride, id outside [0, n_pages)) is skipped.  A copy: bit-exact by construction.
 #include "cpa_internal.h"
@@ -28,7 +28,8 @@ __global__ __launch_bounds__(AT) void kv_append_kernel(const AppendArgs a) {
   constexpr int CPR = D / EPC;     // chunks per token row
   constexpr int LS = D + EPC;      // LDS row stride (elements), +16 bytes against bank conflicts
   typedef uint4 chunk_t;
-  typedef typename std::conditional<EB == 2, uint16_t, uint32_t>::type E;
+  typedef typename std::conditional<EB == 1, uint8_t,
+                                    typename std::conditional<EB == 2, uint16_t, uint32_t>::type>::type E;
   __shared__ __attribute__((aligned(16))) unsigned char tile_raw[64 * LS * EB];
 
   const int n_cp = a.max_chunk_len > 0 ? (a.max_chunk_len + 63) / 64 : 0;
@@ -100,8 +101,9 @@ hipError_t launch_t(const AppendArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_kv_append(const AppendArgs& a, bool bf16, int d, hipStream_t s) {
-  if (bf16) return d == 64 ? launch_t<2, 64>(a, s) : launch_t<2, 128>(a, s);
+hipError_t launch_kv_append(const AppendArgs& a, int elem_bytes, int d, hipStream_t s) {
+  if (elem_bytes == 1) return d == 64 ? launch_t<1, 64>(a, s) : launch_t<1, 128>(a, s);
+  if (elem_bytes == 2) return d == 64 ? launch_t<2, 64>(a, s) : launch_t<2, 128>(a, s);
   return d == 64 ? launch_t<4, 64>(a, s) : launch_t<4, 128>(a, s);
 }
 

@@ -28,6 +28,9 @@
 //                                      score accumulators (no LDS round trip)
 // bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 before the PV product.
 // fp32: v_mfma_f32_32x32x2f32 end to end.
+// fp8 KV (KV8, with bf16 Q): the pages hold OCP e4m3 values; each is dequantized on its way
+// into LDS as bf16(fp32(value) * scale), with one scale for K and one for V, and everything
+// after the staging is the bf16 path.
 //
 // V is written to LDS transposed ([dv][key]); in the bf16 path the key order inside each
 // 32-key half is permuted (bits 2 and 3 of the key index swapped) so that the 8 keys a lane
@@ -74,10 +77,24 @@ struct Cfg {
   static constexpr int DT = D / 32;                 // 32-wide output column tiles
 };
 
-template <bool BF, int D>
+// 8 e4m3 values (OCP fp8) -> 8 bf16 values bf16(fp32(x) * scale), as one 16-byte chunk
+__device__ __forceinline__ uint4 dequant8(uint2 x, float scale) {
+  // v_cvt_pk_f32_fp8 converts the two values of the low (false) or high (true) 16 bits
+  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, false);
+  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true);
+  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false);
+  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true);
+  const __bf16 h[8] = {(__bf16)(f0[0] * scale), (__bf16)(f0[1] * scale), (__bf16)(f1[0] * scale),
+                       (__bf16)(f1[1] * scale), (__bf16)(f2[0] * scale), (__bf16)(f2[1] * scale),
+                       (__bf16)(f3[0] * scale), (__bf16)(f3[1] * scale)};
+  return __builtin_bit_cast(uint4, h);
+}
+
+template <bool BF, int D, bool KV8>
 __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   using C = Cfg<BF, D>;
   using T = typename C::T;
+  using KT = typename std::conditional<KV8, uint8_t, T>::type;   // pool element
   __shared__ __attribute__((aligned(16))) T smem[2 * C::STAGE];
   __shared__ int win_kb[WIN];
   __shared__ int win_ph[WIN];
@@ -116,19 +133,25 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   const int n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
   const int n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
 
-  const T* __restrict__ kg = reinterpret_cast<const T*>(a.k) + (size_t)g * a.head_stride;
-  const T* __restrict__ vg = reinterpret_cast<const T*>(a.v) + (size_t)g * a.v_head_stride;
+  const KT* __restrict__ kg = reinterpret_cast<const KT*>(a.k) + (size_t)g * a.head_stride;
+  const KT* __restrict__ vg = reinterpret_cast<const KT*>(a.v) + (size_t)g * a.v_head_stride;
+  // the 16-byte chunk of EPC elements (in the compute type) that starts at p
+  auto chunk_at = [&](const KT* p, float scale) __attribute__((always_inline)) {
+    if constexpr (KV8) return dequant8(*reinterpret_cast<const uint2*>(p), scale);
+    else return *reinterpret_cast<const uint4*>(p);
+  };
   const int32_t* __restrict__ pmap = a.page_map + (size_t)b * a.page_map_stride;
   const int64_t ts = a.token_stride;
   const int64_t vrs = a.v_row_stride;
   // 16-byte chunk `col` of V token row r of the page at vp: one load for token-major pages, a
   // gather of EPC elements (one per dim row) for dim-major pages
-  auto v_chunk = [&](const T* vp, int r, int col) __attribute__((always_inline)) {
-    if (!a.v_dmajor) return *reinterpret_cast<const uint4*>(vp + (size_t)r * vrs + col * C::EPC);
-    T e[C::EPC];
+  auto v_chunk = [&](const KT* vp, int r, int col) __attribute__((always_inline)) {
+    if (!a.v_dmajor) return chunk_at(vp + (size_t)r * vrs + col * C::EPC, a.v_scale);
+    KT e[C::EPC];
 #pragma unroll
     for (int x = 0; x < C::EPC; ++x) e[x] = vp[(size_t)(col * C::EPC + x) * vrs + r];
-    return __builtin_bit_cast(uint4, e);
+    if constexpr (KV8) return dequant8(__builtin_bit_cast(uint2, e), a.v_scale);
+    else return __builtin_bit_cast(uint4, e);
   };
 
   // ---- Q in registers (B operand of S^T = K Q^T) -------------------------------------------
@@ -164,7 +187,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
     const int nv_tok = min(max(L - 64 * kb, 0), 64);
     if (ph >= 0 && nv_tok == 64) {
       if (vrole) {
-        const T* vp = vg + (size_t)ph * a.v_page_stride;
+        const KT* vp = vg + (size_t)ph * a.v_page_stride;
 #pragma unroll
         for (int k = 0; k < C::VPT; ++k) {
           const int u = min(rtid + ROLE * k, C::VUNITS - 1);
@@ -173,11 +196,11 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
           for (int c = 0; c < 4; ++c) st[4 * k + c] = v_chunk(vp, 4 * q4 + c, col);
         }
       } else {
-        const T* kp = kg + (size_t)ph * a.page_stride;
+        const KT* kp = kg + (size_t)ph * a.page_stride;
 #pragma unroll
         for (int k = 0; k < C::KCH; ++k) {
           const int ch = rtid + ROLE * k;
-          st[k] = *reinterpret_cast<const uint4*>(kp + (size_t)(ch / C::CPR) * ts + (ch % C::CPR) * C::EPC);
+          st[k] = chunk_at(kp + (size_t)(ch / C::CPR) * ts + (ch % C::CPR) * C::EPC, a.k_scale);
         }
       }
     } else {
@@ -185,7 +208,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
       const uint4 fill = make_uint4(f, f, f, f);
       const size_t pofs = (size_t)(ph < 0 ? 0 : ph) * a.page_stride;
       if (vrole) {
-        const T* vp = vg + (size_t)(ph < 0 ? 0 : ph) * a.v_page_stride;
+        const KT* vp = vg + (size_t)(ph < 0 ? 0 : ph) * a.v_page_stride;
 #pragma unroll
         for (int k = 0; k < C::VPT; ++k) {
           const int u = min(rtid + ROLE * k, C::VUNITS - 1);
@@ -201,9 +224,8 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
         for (int k = 0; k < C::KCH; ++k) {
           const int ch = rtid + ROLE * k;
           const int r = ch / C::CPR;
-          st[k] = (ph >= 0 && r < nv_tok)
-                      ? *reinterpret_cast<const uint4*>(kg + pofs + (size_t)r * ts + (ch % C::CPR) * C::EPC)
-                      : fill;
+          st[k] = (ph >= 0 && r < nv_tok) ? chunk_at(kg + pofs + (size_t)r * ts + (ch % C::CPR) * C::EPC, a.k_scale)
+                                          : fill;
         }
       }
     }
@@ -423,17 +445,18 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
     a.lse[(size_t)(q0 + row) * a.Hq + head] = lt > 0.f ? (m_run + __log2f(lt)) * LN2 : -INFINITY;
 }
 
-template <bool BF, int D>
+template <bool BF, int D, bool KV8 = false>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   const int grid = prefill_grid(a);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<BF, D>), dim3(grid), dim3(THREADS), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<BF, D, KV8>), dim3(grid), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_regstaged(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
+  if (a.kv_fp8) return d == 64 ? launch_t<true, 64, true>(a, s) : launch_t<true, 128, true>(a, s);
   if (bf16) return d == 64 ? launch_t<true, 64>(a, s) : launch_t<true, 128>(a, s);
   return d == 64 ? launch_t<false, 64>(a, s) : launch_t<false, 128>(a, s);
 }

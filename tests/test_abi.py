@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cpa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(cpa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -29,8 +29,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables",
                           "cpa_build_block_tables_bits", "cpa_chunked_prefill", "cpa_chunked_prefill_direct",
-                          "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes",
-                          "cpa_status_string", "cpa_version"}
+                          "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt",
+                          "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -182,6 +182,7 @@ def ap(lib, kn=FAKE, vn=FAKE, dtype=1, k=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=
 def test_append_validation(lib):
     assert ap(lib, d=96) == 4
     assert ap(lib, dtype=5) == 4
+    assert ap(lib, dtype=2, ts=8, hs=64 * 8, ps=8 * 64 * 8) == 2   # fp8 rows still hold d values
     assert ap(lib, Hkv=0) == 2
     assert ap(lib, B=-1) == 2
     assert ap(lib, vdm=2) == 2
@@ -236,6 +237,27 @@ def test_direct_validation(lib):
     assert pd(lib, v=FAKE + 2) == 3
     assert pd(lib, vds=68, vhs=128 * 68, vps=8 * 128 * 68) == 3
     assert pd(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, plans=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
+
+
+def pf8(lib, q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, vdm=0, vps=8 * 64 * 128, vhs=64 * 128,
+        vrs=128, ks=1.0, vs=1.0, npages=10, pm=FAKE, pms=16, tab=FAKE, cap=16, cnt=FAKE, cu=FAKE, pl=FAKE, B=1, Hq=32,
+        Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL):
+    return lib.cpa_chunked_prefill_fp8kv(q, k, v, ps, hs, ts, vdm, vps, vhs, vrs, ks, vs, npages, pm, pms, tab, cap,
+                                         cnt, cu, pl, B, Hq, Hkv, d, mcl, scale, o, lse, None)
+
+
+def test_fp8kv_validation(lib):
+    assert pf8(lib, ks=0.0) == 2
+    assert pf8(lib, vs=-1.0) == 2
+    assert pf8(lib, ks=float("inf")) == 2
+    assert pf8(lib, vs=float("nan")) == 2
+    assert pf8(lib, vdm=3) == 2
+    assert pf8(lib, d=96) == 4
+    assert pf8(lib, ts=64) == 2
+    assert pf8(lib, q=NULL) == 1
+    assert pf8(lib, k=FAKE + 8) == 3
+    assert pf8(lib, vdm=1, vrs=63, vhs=128 * 64, vps=8 * 128 * 64) == 2
+    assert pf8(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
 
 
 def test_split_planner():

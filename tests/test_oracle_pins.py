@@ -545,3 +545,35 @@ def test_block_sparse_equals_union_when_masks_are_shared_and_constant():
                                          w.prefix_len, w.Hkv)
     Ou, Lu = run_oracle(w)
     assert np.max(np.abs(O - Ou)) < 1e-12 and np.max(np.abs(L - Lu)) < 1e-12
+
+
+# ---- fp8 KV dequantization -------------------------------------------------------------------------
+
+def test_decode_e4m3_worked_values():
+    dec = oracle.decode_e4m3(np.array([0x38, 0x40, 0x7E, 0x01, 0x08, 0x80, 0x00, 0x7F, 0xFF, 0xB8, 0x3C], np.uint8))
+    assert dec[0] == 1.0 and dec[1] == 2.0 and dec[2] == 448.0
+    assert dec[3] == 2.0 ** -9 and dec[4] == 2.0 ** -6
+    assert dec[5] == 0.0 and np.signbit(dec[5]) and dec[6] == 0.0 and not np.signbit(dec[6])
+    assert np.isnan(dec[7]) and np.isnan(dec[8])
+    assert dec[9] == -1.0 and dec[10] == 1.5
+
+
+def test_decode_e4m3_every_code_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    dec = oracle.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(dec), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(dec[ok], ref[ok]) and np.array_equal(np.signbit(dec[ok]), np.signbit(ref[ok]))
+
+
+def test_round_bf16_ties_and_random():
+    # 1 + 2^-8 lies halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even gives 1;
+    # 1 + 3 * 2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: the even one is 1 + 2^-6
+    t = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -(1 + 2 ** -8)], np.float32)
+    assert oracle.round_bf16(t).tolist() == [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0]
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 100
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(oracle.round_bf16(x), ref)
+    y = oracle.dequant_e4m3(np.array([0x38, 0x3C], np.uint8), 0.3)
+    assert y.tolist() == oracle.round_bf16(np.array([0.3, 1.5 * np.float32(0.3)], np.float32)).tolist()
