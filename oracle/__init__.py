@@ -25,10 +25,9 @@ Pin status (what each function is checked against besides itself):
                        pinned: torch SDPA with an explicit per-(head, row) boolean mask over
                        contiguous K/V; equals paged_attention on the union tables when every
                        head of a group shares one mask constant over the query blocks
-  decode_e4m3 / round_bf16 / dequant_e4m3
+  decode_e4m3 / dequant_e4m3
                        pinned: code values worked by hand (1, 2, 448, the smallest subnormal,
-                       -0, NaN), every code against torch's float8_e4m3fn, rounding ties and
-                       every bf16 rounding of random floats against torch
+                       -0, NaN), every code against torch's float8_e4m3fn
   append_kv            pinned: a worked example written out by hand; the appended rows read
                        back through logical positions; every other slot unchanged
 """
@@ -36,4 +35,4 @@ from .union import block_union_tables, block_union_tables_bits, unpack_mask_bits
 from .attention import paged_attention, attention_rows  # noqa: F401
 from .append import append_kv  # noqa: F401
 from .direct import block_plans, block_sparse_attention, block_sparse_rows  # noqa: F401
-from .fp8 import decode_e4m3, dequant_e4m3, round_bf16  # noqa: F401
+from .fp8 import decode_e4m3, dequant_e4m3  # noqa: F401

@@ -1,15 +1,15 @@
 """fp8 KV dequantization written out (test infrastructure; see package header).
 
 Source: "CompactAttention: Accelerating Chunked Prefill with Block-Union KV Selection", abstract
-(KV blocks read in place from a paged cache).  With an fp8 cache the values attention sees are
-the stored e4m3 codes dequantized: v = bf16(fp32(decode(x)) * fp32(scale)).
+(KV blocks read in place from a paged cache).  With an fp8 cache the keys and values attention
+sees are the stored e4m3 codes decoded and multiplied by the tensor's scale: v = decode(x) * scale,
+taken exactly (float64).
 
 decode(x) for the OCP e4m3 format (8 bits: sign s, 4 exponent bits e, 3 mantissa bits m,
 exponent bias 7, no infinities):
   e == 15 and m == 7:  NaN
   e == 0:              (-1)^s * 2^-6 * m / 8        (subnormal; m == 0 gives a signed zero)
   otherwise:           (-1)^s * 2^(e - 7) * (1 + m / 8)
-bf16(y) rounds a float32 to the nearest bfloat16, ties to even (NaN stays NaN).
 """
 import numpy as np
 
@@ -26,17 +26,6 @@ def decode_e4m3(codes):
     return np.where((e == 15) & (m == 7), np.nan, out)
 
 
-def round_bf16(x):
-    """float32 values -> the nearest bfloat16 values (ties to even), returned as float32."""
-    f = np.asarray(x, dtype=np.float32)
-    bits = f.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
-    out = rounded.astype(np.uint32).view(np.float32)
-    return np.where(np.isnan(f), np.float32(np.nan), out)
-
-
 def dequant_e4m3(codes, scale):
-    """The values an fp8 page holds for attention: bf16(fp32(decode(x)) * fp32(scale))."""
-    y = decode_e4m3(codes).astype(np.float32) * np.float32(scale)
-    return round_bf16(y)
+    """The values an fp8 page holds for attention: decode(x) * scale, in float64."""
+    return decode_e4m3(codes) * float(np.float32(scale))

@@ -69,6 +69,7 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_chunk_len = max_chunk_len;
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt((float)d);
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_scale = 1.0f;
   a.o = o; a.lse = lse;
   a.G = G;
   a.hpw = G >= 4 ? 4 : G;
@@ -210,8 +211,8 @@ cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const v
                                         prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
   if (st != CPA_OK || nothing) return st;
   a.kv_fp8 = 1;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
+  a.scale_log2 *= k_scale;   // scores of the stored values times the K scale
+  a.out_scale = v_scale;     // the output is linear in V
   return cpa::launch_prefill_regstaged(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 

@@ -30,10 +30,10 @@ struct PrefillArgs {
   // (v_dmajor == 1, dim-major pages)
   int64_t v_page_stride, v_head_stride, v_row_stride;
   int v_dmajor;
-  // fp8 KV: the pools hold OCP e4m3 bytes (strides in elements = bytes), dequantized as
-  // bf16(fp32(x) * k_scale) and bf16(fp32(x) * v_scale); q and o are bf16
+  // fp8 KV: the pools hold OCP e4m3 bytes (strides in elements = bytes) of values x * k_scale and
+  // x * v_scale; the K scale is folded into scale_log2 and the V scale is out_scale
   int kv_fp8;
-  float k_scale, v_scale;
+  float out_scale;      // multiplies the normalised output (1 unless fp8 KV)
   const int32_t* page_map;
   int page_map_stride;
   const int32_t* tables;

@@ -28,9 +28,10 @@
 //                                      score accumulators (no LDS round trip)
 // bf16: v_mfma_f32_32x32x16_bf16, P rounded to bf16 before the PV product.
 // fp32: v_mfma_f32_32x32x2f32 end to end.
-// fp8 KV (KV8, with bf16 Q): the pages hold OCP e4m3 values; each is dequantized on its way
-// into LDS as bf16(fp32(value) * scale), with one scale for K and one for V, and everything
-// after the staging is the bf16 path.
+// fp8 KV (KV8, with bf16 Q): the pages hold OCP e4m3 codes, converted on their way into LDS to
+// bf16, which holds every e4m3 value exactly; the per-tensor scales are applied outside the
+// products (the K scale joins the softmax scale, the V scale the final normalisation), and
+// everything after the staging is the bf16 path.
 //
 // V is written to LDS transposed ([dv][key]); in the bf16 path the key order inside each
 // 32-key half is permuted (bits 2 and 3 of the key index swapped) so that the 8 keys a lane
@@ -77,16 +78,14 @@ struct Cfg {
   static constexpr int DT = D / 32;                 // 32-wide output column tiles
 };
 
-// 8 e4m3 values (OCP fp8) -> 8 bf16 values bf16(fp32(x) * scale), as one 16-byte chunk
-__device__ __forceinline__ uint4 dequant8(uint2 x, float scale) {
-  // v_cvt_pk_f32_fp8 converts the two values of the low (false) or high (true) 16 bits
-  const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, false);
-  const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true);
-  const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false);
-  const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true);
-  const __bf16 h[8] = {(__bf16)(f0[0] * scale), (__bf16)(f0[1] * scale), (__bf16)(f1[0] * scale),
-                       (__bf16)(f1[1] * scale), (__bf16)(f2[0] * scale), (__bf16)(f2[1] * scale),
-                       (__bf16)(f3[0] * scale), (__bf16)(f3[1] * scale)};
+// 8 e4m3 codes (OCP fp8) -> their 8 values in bf16 (exact), as one 16-byte chunk; each
+// instruction converts the two codes of the low (false) or high (true) 16 bits, scale 1
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 x) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true)};
   return __builtin_bit_cast(uint4, h);
 }
 
@@ -136,8 +135,8 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   const KT* __restrict__ kg = reinterpret_cast<const KT*>(a.k) + (size_t)g * a.head_stride;
   const KT* __restrict__ vg = reinterpret_cast<const KT*>(a.v) + (size_t)g * a.v_head_stride;
   // the 16-byte chunk of EPC elements (in the compute type) that starts at p
-  auto chunk_at = [&](const KT* p, float scale) __attribute__((always_inline)) {
-    if constexpr (KV8) return dequant8(*reinterpret_cast<const uint2*>(p), scale);
+  auto chunk_at = [&](const KT* p) __attribute__((always_inline)) {
+    if constexpr (KV8) return fp8x8_to_bf16(*reinterpret_cast<const uint2*>(p));
     else return *reinterpret_cast<const uint4*>(p);
   };
   const int32_t* __restrict__ pmap = a.page_map + (size_t)b * a.page_map_stride;
@@ -146,11 +145,11 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   // 16-byte chunk `col` of V token row r of the page at vp: one load for token-major pages, a
   // gather of EPC elements (one per dim row) for dim-major pages
   auto v_chunk = [&](const KT* vp, int r, int col) __attribute__((always_inline)) {
-    if (!a.v_dmajor) return chunk_at(vp + (size_t)r * vrs + col * C::EPC, a.v_scale);
+    if (!a.v_dmajor) return chunk_at(vp + (size_t)r * vrs + col * C::EPC);
     KT e[C::EPC];
 #pragma unroll
     for (int x = 0; x < C::EPC; ++x) e[x] = vp[(size_t)(col * C::EPC + x) * vrs + r];
-    if constexpr (KV8) return dequant8(__builtin_bit_cast(uint2, e), a.v_scale);
+    if constexpr (KV8) return fp8x8_to_bf16(__builtin_bit_cast(uint2, e));
     else return __builtin_bit_cast(uint4, e);
   };
 
@@ -200,7 +199,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int k = 0; k < C::KCH; ++k) {
           const int ch = rtid + ROLE * k;
-          st[k] = chunk_at(kp + (size_t)(ch / C::CPR) * ts + (ch % C::CPR) * C::EPC, a.k_scale);
+          st[k] = chunk_at(kp + (size_t)(ch / C::CPR) * ts + (ch % C::CPR) * C::EPC);
         }
       }
     } else {
@@ -224,8 +223,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
         for (int k = 0; k < C::KCH; ++k) {
           const int ch = rtid + ROLE * k;
           const int r = ch / C::CPR;
-          st[k] = (ph >= 0 && r < nv_tok) ? chunk_at(kg + pofs + (size_t)r * ts + (ch % C::CPR) * C::EPC, a.k_scale)
-                                          : fill;
+          st[k] = (ph >= 0 && r < nv_tok) ? chunk_at(kg + pofs + (size_t)r * ts + (ch % C::CPR) * C::EPC) : fill;
         }
       }
     }
@@ -421,7 +419,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   // ---- epilogue ----------------------------------------------------------------------------
   if (!row_ok) return;
   const float lt = xhalf_sum(l_run);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = lt > 0.f ? a.out_scale / lt : 0.f;
   T* dst = reinterpret_cast<T*>(a.o) + ((size_t)(q0 + row) * a.Hq + head) * D;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) {
@@ -442,7 +440,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
     }
   }
   if (a.lse != nullptr && hl == 0)
-    a.lse[(size_t)(q0 + row) * a.Hq + head] = lt > 0.f ? (m_run + __log2f(lt)) * LN2 : -INFINITY;
+    a.lse[(size_t)(q0 + row) * a.Hq + head] = lt > 0.f ? (m_run + __log2f(lt)) * LN2 : -INFINITY;   // scores include the K scale
 }
 
 template <bool BF, int D, bool KV8 = false>

@@ -1,7 +1,7 @@
 """GPU parity of the fp8 KV path (cpa_chunked_prefill_fp8kv) against the fp64 oracle.
 
 The pools hold OCP e4m3 codes; the oracle attends over its own dequantization of the same codes,
-bf16(fp32(decode(x)) * scale), so the bars are those of the bf16 path.  The append of fp8 rows
+decode(x) * scale, so the bars are those of the bf16 path.  The append of fp8 rows
 is checked bit for bit.
 """
 import numpy as np
