@@ -19,7 +19,7 @@
 //   K: in MFMA operand order.  Slab (h, ks) (1 KiB) holds, at 16-byte slot l, key 32h + l % 32,
 //      chunk 2ks + l / 32: the operand of lane l for k-step ks of key half h.  Every operand
 //      load is then one contiguous, conflict-free 1 KiB read at an immediate offset.  With
-//      dim-major V the keys of a slab are permuted (key_perm), see below;
+//      dim-major V the keys of a slab are permuted (key_perm in prefill_common.h), see V below;
 //   V: the PV operand of lane l is 8 consecutive keys of one output column.  A pool of
 //      token-major pages ([token][d], d contiguous) is staged as natural rows with chunk c at
 //      c ^ swz_v(r), and each operand is built by two ds_read_b64_tr_b16 transposed reads,
@@ -66,8 +66,6 @@ namespace cpa {
 namespace {
 
 constexpr int THREADS = 512;
-// a lane's 16 weights of one unit may sum to this before the reference must move (2^30)
-constexpr float kSumLimit = 1073741824.0f;
 constexpr int WIN = 1024;  // circular window of resolved page ids
 constexpr int CH = 512;    // ids resolved at a time
 
@@ -83,13 +81,6 @@ struct Geo {
   static constexpr int DT = D / 32;     // 32-wide output column tiles
   static constexpr int KS = D / 16;     // k-steps of the QK product
 };
-
-// Key order of the K slabs for dim-major V.  The score accumulator of lane l holds, in
-// elements 0..7, rows 4(l/32) + 0..3 and 8 + 4(l/32) + 0..3 of each 16-row half, and those
-// elements become the lane's 8 k-values of the PV product's P operand.  Dim-major V pages give
-// lane l the 8 consecutive keys 8(l/32) + 0..7 as its V operand, so slab row m holds key
-// key_perm(m) (bits 2 and 3 swapped), which puts exactly those keys in the lane's 8 elements.
-__device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 // chunk position of V chunk c of row r is c ^ swz_v(r)
 template <int D>
@@ -375,7 +366,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   };
   // SM, weights of scores s (left as they are) against the reference, rounded to bf16 as the PV
   // operands; returns this lane's sum of them.
-  //   key of operand u (0, 1), element e, lane half hl: 16*u + 8*(e / 4) + 4*hl + e % 4
+  //   key of operand u (0, 1), element e, lane half hl: 16*u + 8*(e / 4) + 4*hl + e % 4, or with
+  //   dim-major V (key_perm) 16*u + 8*hl + e
   auto weights = [&](const f32x16& s, bf16x8& p0, bf16x8& p1) __attribute__((always_inline)) {
     float w[16];
 #pragma unroll

@@ -13,6 +13,16 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // log2 headroom before the output accumulators must be rescaled to a new row maximum
 constexpr float kRescaleThreshold = 8.0f;
 
+// a lane's 16 weights of one unit may sum to this before the row reference must move (2^30)
+constexpr float kSumLimit = 1073741824.0f;
+
+// Key order of K operand rows when V operands are 8 consecutive keys (dim-major V).  The score
+// accumulator of lane l holds, in elements 0..7, rows 4(l/32) + 0..3 and 8 + 4(l/32) + 0..3 of
+// each 16-row half, and those elements become the lane's 8 k-values of the PV product's P
+// operand.  Loading K row m from key key_perm(m) (bits 2 and 3 swapped) puts exactly the keys
+// 8(l/32) + 0..7 in those elements, matching the V operand.
+__device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
 // max / sum of x over lanes l and l^32 (the two lanes that share a query row)
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

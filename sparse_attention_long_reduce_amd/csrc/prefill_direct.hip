@@ -23,11 +23,8 @@ namespace cpa {
 namespace {
 
 constexpr int DTH = 128;   // threads per workgroup
-constexpr float kSumLimitD = 1073741824.0f;   // 2^30: lane weight sum before the reference moves
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ int key_perm_d(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 template <int D>
 __global__ __launch_bounds__(DTH, 2) void prefill_direct_kernel(const DirectArgs a) {
@@ -89,7 +86,7 @@ __global__ __launch_bounds__(DTH, 2) void prefill_direct_kernel(const DirectArgs
 
   // operand loads of unit u = (plan entry u / 2, key half u % 2)
   const bf16x8 nan8 = __builtin_bit_cast(bf16x8, make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u));
-  const int krow_lane = key_perm_d(l32);
+  const int krow_lane = key_perm(l32);
   auto page_of = [&](int i, int& kb, int& ph) __attribute__((always_inline)) {
     kb = plan[i];
     ph = -1;
@@ -208,7 +205,7 @@ __global__ __launch_bounds__(DTH, 2) void prefill_direct_kernel(const DirectArgs
     }
     bf16x8 p0, p1;
     float lu = weights(s, p0, p1);
-    if (__builtin_amdgcn_ballot_w64(!(lu < kSumLimitD))) {   // move the reference (rare)
+    if (__builtin_amdgcn_ballot_w64(!(lu < kSumLimit))) {   // move the reference (rare)
       const float mx = rowmax(s);
       const float d = mx > kRescaleThreshold ? mx : 0.f;
 #pragma unroll
