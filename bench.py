@@ -265,9 +265,15 @@ def time_direct(cpa, bt, steps, warmup=3):
     build = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     pre = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     flop = cpa.plan_flops(plans.cpu().numpy(), counts.cpu().numpy(), w.prefix_len, w.chunk_len, w.d)
+    n_blk = int(counts.sum())
+    # each plan block's K and V (64 tokens x d, bf16) reach the registers of its tile once
+    opb = n_blk * 2 * 64 * w.d * 2
     return {"plan_build_us": round(build * 1e3, 2), "prefill_ms": round(pre, 4), "step_ms": round(build + pre, 4),
-            "flop": int(flop), "prefill_tflops": round(flop / (pre * 1e-3) / 1e12, 2),
-            "plan_blocks": int(counts.sum())}
+            "flop": int(flop), "prefill_tflops": round(flop / (pre * 1e-3) / 1e12, 2), "plan_blocks": n_blk,
+            "roofline": {"bound": "hbm", "achieved": round(opb / (pre * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(opb / (pre * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": opb,
+                         "note": "K/V operand bytes of the plans, one read per (head, query block) tile"}}
 
 
 def time_fp8kv(cpa, bt, steps, warmup=3):
@@ -322,7 +328,11 @@ def time_build_bits(cpa, batches, steps):
     us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
     same = all(torch.equal(t, bt.tables) and torch.equal(c, bt.counts) for bt, (t, c) in zip(batches, outs))
     nbytes = sum(int(b.numel()) * 8 for b in bits)
-    return {"us": round(us, 2), "mask_bytes": nbytes, "tables_equal_byte_masks": bool(same)}
+    tbytes = sum(int(bt.tables.numel() * 4 + bt.counts.numel() * 4) for bt in batches)
+    gbs = (nbytes + tbytes) / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "mask_bytes": nbytes, "tables_equal_byte_masks": bool(same),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 5), "algorithmic_bytes": nbytes + tbytes}}
 
 
 def time_append(cpa, bt, steps):
@@ -448,6 +458,8 @@ def main():
     if len(batches) == 1 and batches[0].split_pages == 0:
         fp8kv = time_fp8kv(cpa, batches[0], max(5, args.steps // 2))
         fp8kv["prefill_tflops"] = round(flops / (fp8kv["prefill_ms"] * 1e-3) / 1e12, 2)
+        fp8kv["roofline"] = {"bound": "mfma", "achieved": fp8kv["prefill_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(fp8kv["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(f"[bench] fp8 KV cache: prefill {fp8kv['prefill_ms']:.3f} ms ({fp8kv['prefill_tflops']:.0f} TFLOP/s), "
             f"cache {fp8kv['kv_bytes'] / 2**20:.0f} MiB vs {fp8kv['kv_bytes_bf16'] / 2**20:.0f} MiB bf16")
     bits = time_build_bits(cpa, batches, max(5, args.steps))
