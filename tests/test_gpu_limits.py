@@ -1,0 +1,78 @@
+"""GPU parity at the limits: the largest KV extent the table build takes (65536 blocks, a
+4M-token context) and the largest query groups (G = 16, 32), against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_long_reduce_amd as cpa
+from workloads import make_workload
+from workloads.configs import mask_bernoulli, mask_stripes
+
+from _gpu import compare, gpu_tables, sample_rows, upload
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+MAX_BLOCKS = 65536
+
+
+@pytest.fixture(scope="module")
+def longest():
+    # one sequence whose last 128-token chunk ends at block 65535: 4,194,304 tokens of context
+    P = (MAX_BLOCKS - 2) * 64
+    return make_workload("max_context", [P], [128], 4, 1, 64, "bf16",
+                         lambda rng, *a: mask_stripes(rng, *a, p=0.05, shared_per_group=False), 71)
+
+
+def test_max_context_tables(longest):
+    w = longest
+    assert w.nkvb_max == MAX_BLOCKS
+    dv = upload(w)
+    t, c = gpu_tables(dv, w)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    assert np.array_equal(t.cpu().numpy(), T) and np.array_equal(c.cpu().numpy(), C)
+    assert C[0, 0] > 10000   # thousands of pages: the page-id window is reloaded many times
+
+
+@pytest.mark.parametrize("mode", ["token", "dim", "split"])
+def test_max_context_prefill(longest, mode):
+    print(f"\n[case] max context {mode}", flush=True)
+    w = longest
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    if mode == "split":
+        o, lse = cpa.chunked_prefill(dv["q"], dv["kp"], dv["vp"], dv["pm"], tables, counts, dv["cu"], dv["pl"],
+                                     w.max_chunk_len, return_lse=True, split_pages=4096)
+    else:
+        vp = dv["vp"].transpose(2, 3).contiguous() if mode == "dim" else dv["vp"]
+        o, lse = cpa.chunked_prefill(dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"],
+                                     w.max_chunk_len, return_lse=True, v_layout=mode)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    S = sample_rows(w, 48, seed=2)
+    Os, Ls = oracle.attention_rows(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv, S)
+    r = torch.from_numpy(w.cu_q[S[:, 0]] + S[:, 2]).cuda()
+    h = torch.from_numpy(S[:, 1]).cuda()
+    compare(w, o[r, h].float().cpu().numpy(), Os, f"max context {mode}")
+    assert np.max(np.abs(lse[r, h].cpu().numpy() - Ls)) < 2e-2
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(32, 1, 128), (32, 2, 64), (16, 1, 64)])
+def test_large_groups(Hq, Hkv, d):
+    print(f"\n[case] G = {Hq // Hkv}, d = {d}", flush=True)
+    w = make_workload(f"g{Hq // Hkv}", [512, 1024], [192, 77], Hq, Hkv, d, "bf16",
+                      lambda rng, *a: mask_bernoulli(rng, *a, p=0.1, local=1), 72)
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    assert np.array_equal(tables.cpu().numpy(), T)
+    O, L = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
+    for v_layout in ("token", "dim"):
+        vp = dv["vp"].transpose(2, 3).contiguous() if v_layout == "dim" else dv["vp"]
+        o, lse = cpa.chunked_prefill(dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"],
+                                     w.max_chunk_len, return_lse=True, v_layout=v_layout)
+        torch.cuda.synchronize()
+        compare(w, o, O, f"G={Hq // Hkv} {v_layout}")
+        assert np.max(np.abs(lse.cpu().numpy() - L.T)) < 2 ** -7
