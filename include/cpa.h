@@ -146,9 +146,9 @@ cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pag
                                hipStream_t stream);
 
 /*
- * cpa_chunked_prefill_split - cpa_chunked_prefill with each (group, query tile) cut along its
- * table into ranges of split_pages pages (split-KV), for calls with too few tiles to fill the
- * GPU or with tables of very different lengths.
+ * cpa_chunked_prefill_split - cpa_chunked_prefill with the pages each (group, query tile)
+ * visits cut into n_splits near-equal ranges (split-KV), for calls with too few tiles to fill
+ * the GPU or with tables of very different lengths.
  *
  * Each range is run by its own workgroup, which writes the normalised partial output of its
  * rows and their LSE over that range into `workspace`.  A second kernel then combines the
@@ -159,8 +159,10 @@ cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pag
  *
  * Arguments as cpa_chunked_prefill, plus:
  *   total_q     rows of all sequences (Tq = cu_q[B]); sizes the workspace rows.
- *   split_pages pages per range, >= 1.  n_splits = ceil(table_cap / split_pages) ranges per tile;
- *               with n_splits == 1 this is cpa_chunked_prefill and the workspace is unused.
+ *   split_pages >= 1; sets n_splits = ceil(table_cap / split_pages) ranges per tile.  A tile
+ *               that visits n pages gives each range ceil(n / n_splits) of them (the last ones
+ *               fewer), at most split_pages.  With n_splits == 1 this is cpa_chunked_prefill and
+ *               the workspace is unused.
  *   workspace   device memory owned by the caller, 16-byte aligned, at least
  *               cpa_split_workspace_bytes(total_q, Hq, d, table_cap, split_pages) bytes; its
  *               contents on entry do not matter and on return are unspecified.  Calls that use

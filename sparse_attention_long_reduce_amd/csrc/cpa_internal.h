@@ -54,9 +54,10 @@ struct PrefillArgs {
   int tiles_per_group;  // n_qtiles * hsplit
   int n_groups;         // B * Hkv
   int xcd_remap;        // 1: keep each KV group's tiles on one XCD (see the prefill kernel)
-  // split-KV: each tile's table is cut into n_splits ranges of split_pages pages; range s of a
-  // tile writes its rows' normalised partial output (fp32 part_o[s][row][head][d]) and LSE
-  // (part_lse[s][row][head], natural log) instead of o / lse.  n_splits == 1: no split.
+  // split-KV: the pages each tile visits are cut into n_splits near-equal ranges (at most
+  // split_pages each); range s of a tile writes its rows' normalised partial output (fp32
+  // part_o[s][row][head][d]) and LSE (part_lse[s][row][head], natural log) instead of o / lse.
+  // n_splits == 1: no split.
   int n_splits;
   int split_pages;
   int total_q;          // rows of all sequences (the partials' row dimension)

@@ -162,9 +162,10 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int32_t* tab = a.tables + (size_t)gi * a.table_cap;
   int n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
   int n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
-  if (SPLIT) {   // this workgroup's range of the tile's pages
-    const int lo = split * a.split_pages;
-    const int hi = min(n_iter, lo + a.split_pages);
+  if (SPLIT) {   // this workgroup's range: the tile's pages cut into n_splits near-equal ranges
+    const int len = (n_iter + a.n_splits - 1) / a.n_splits;
+    const int lo = min(n_iter, split * len);
+    const int hi = min(n_iter, lo + len);
     tab += lo;
     n_vis = max(0, min(n_vis, hi) - lo);
     n_iter = max(0, hi - lo);
