@@ -276,6 +276,37 @@ def time_direct(cpa, bt, steps, warmup=3):
                          "note": "K/V operand bytes of the plans, one read per (head, query block) tile"}}
 
 
+def time_graph(cpa, batches, steps):
+    """The workload's launch pairs (sparse masks) captured into one HIP graph and replayed; HIP
+    events around each replay.  Returns the mean replay time."""
+    import numpy as np
+    import torch
+
+    def step():
+        for bt in batches:
+            bt.build(cpa, False)
+            bt.prefill(cpa, False)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(2):
+        g.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
 def time_fp8kv(cpa, bt, steps, warmup=3):
     """The batch's prefill over an fp8 (e4m3) copy of its KV cache, per-tensor scale 1/4
     (cpa_chunked_prefill_fp8kv, token-major V), HIP events around each launch."""
@@ -465,6 +496,13 @@ def main():
     bits = time_build_bits(cpa, batches, max(5, args.steps))
     log(f"[bench] table build from bit-packed masks: {bits['us']:.1f} us ({bits['mask_bytes']} mask bytes), "
         f"tables equal: {bits['tables_equal_byte_masks']}")
+    graph = None
+    if args.workload == "c4":
+        gms = time_graph(cpa, batches, max(5, args.steps // 2))
+        graph = {"step_ms": round(gms, 4), "eager_step_ms": round(r["step_ms"], 4),
+                 "speedup_over_eager": round(r["step_ms"] / gms, 4),
+                 "note": "the 64 launch pairs of a step captured into one HIP graph and replayed"}
+        log(f"[bench] one HIP graph of the step's {2 * len(batches)} launches: {gms:.3f} ms per replay")
     append = None
     if args.workload != "c4":
         append = time_append(cpa, batches[0], max(5, args.steps))
@@ -523,6 +561,8 @@ def main():
     if append is not None:
         result["kv_append"] = append
     result["table_build_bit_masks"] = bits
+    if graph is not None:
+        result["graph_replay"] = graph
     if fp8kv is not None:
         result["fp8_kv"] = fp8kv
     if direct is not None:
