@@ -34,9 +34,9 @@
 // Software pipeline.  Per page (64 keys) and wave (32 query rows), in the transposed domain so
 // that each lane owns whole query rows:
 //   QK   S^T[key][row] = K . Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS, B = Q^T in VGPRs
-//   SM   causal cut (only on pages that reach past the wave's first row), online softmax in
-//        fp32, log2 domain, softmax scale folded into one FMA; a row's 64 scores live in lanes
-//        l and l^32 (one permlane32 swap per row maximum); P^T rounded to bf16
+//   SM   causal cut (only on units that reach past the wave's first row), weights exp2 of the
+//        scores (already in log2 units and relative to the row's reference, see below), P^T
+//        rounded to bf16; a row's 32 scores of a unit live in lanes l and l^32
 //   PV   O^T[dv][row] += V^T . P^T   A = V^T from LDS (see V above), B = P^T
 // The pipeline works on units of 32 keys (half a page): unit u runs SM of unit u together with
 // QK of unit u+1 and PV of unit u-1.  The three are independent, so each wave's softmax VALU
@@ -51,13 +51,21 @@
 // instead) sends its copy instructions to a scratch LDS tile, so every wave issues the same
 // number of copies per iteration.
 //
-// Rescaling is lazy: the output accumulators are rescaled only when a row maximum grows by more
-// than 2^8 over the reference it was accumulated with, after PV of the previous unit has added
-// the weights taken against the old reference.  The row sum adds the bf16-rounded weights that
-// enter the PV product (v_dot2_f32_bf16 with ones, two weights per instruction), so the result
-// is normalised by exactly the weights used.  This file is compiled without NaN semantics so
-// that maxima need no operand quieting; NaN inputs still propagate through the exponentials and
-// the MFMAs to the output.
+// Softmax.  Q is taken multiplied by scale * log2(e) (rounded to bf16), so the MFMA returns
+// scores in log2 units, and the first QK MFMA of a unit starts its accumulator at -m, the row's
+// reference, so a weight is a bare exp2.  The reference is the row maximum of the first unit and
+// is not checked against every unit's maximum: a unit whose weights in some lane sum to 2^30 or
+// more (or to inf / NaN) takes a rare branch that moves the reference to the unit's row maximum,
+// rescales the output accumulators (after PV of the previous unit has added the weights taken
+// against the old reference) and takes the weights again.  The row sum adds the bf16-rounded
+// weights that enter the PV product (v_dot2_f32_bf16 with ones, two weights per instruction), so
+// the result is normalised by exactly the weights used.  This file is compiled without NaN
+// semantics so that maxima need no operand quieting; NaN inputs still propagate through the
+// exponentials and the MFMAs to the output.
+//
+// Split-KV (SPLIT): a workgroup runs one of n_splits near-equal ranges of its tile's pages and
+// writes that range's normalised output (fp32) and LSE into the caller's workspace;
+// split_merge_kernel combines the ranges of each row by their LSEs.
 #include "prefill_common.h"
 
 #include <type_traits>
