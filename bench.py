@@ -316,23 +316,29 @@ def time_fp8kv(cpa, bt, steps, warmup=3):
     f8 = torch.float8_e4m3fn
     kp8 = (torch.from_numpy(w.k_pages) * 4.0).to(f8).to(bt.q.device)
     vp8 = (torch.from_numpy(w.v_pages) * 4.0).to(f8).to(bt.q.device)
+    vp8d = vp8.view(torch.uint8).transpose(2, 3).contiguous().view(f8)   # dim-major copy
     out = torch.empty_like(bt.q)
 
-    def run():
-        cpa.chunked_prefill(bt.q, kp8, vp8, bt.pm, bt.tables, bt.counts, bt.cu, bt.pl, w.max_chunk_len, out=out,
-                            k_scale=0.25, v_scale=0.25)
+    def timed_ms(vp, layout):
+        def run():
+            cpa.chunked_prefill(bt.q, kp8, vp, bt.pm, bt.tables, bt.counts, bt.cu, bt.pl, w.max_chunk_len,
+                                out=out, k_scale=0.25, v_scale=0.25, v_layout=layout)
+        for _ in range(warmup):
+            run()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record()
+            run()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
 
-    for _ in range(warmup):
-        run()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for e0, e1 in ev:
-        e0.record()
-        run()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
-    return {"prefill_ms": round(ms, 4), "kv_bytes": int(kp8.numel() + vp8.numel()),
-            "kv_bytes_bf16": int(2 * (kp8.numel() + vp8.numel()))}
+    ms_dim = timed_ms(vp8d, "dim")
+    ms_tok = timed_ms(vp8, "token")
+    return {"prefill_ms": round(ms_dim, 4), "prefill_ms_token_major_v": round(ms_tok, 4),
+            "kv_bytes": int(kp8.numel() + vp8.numel()), "kv_bytes_bf16": int(2 * (kp8.numel() + vp8.numel())),
+            "note": "dim-major V: codes staged in LDS and converted at operand read; token-major V: "
+                    "register-staged conversion"}
 
 
 def time_build_bits(cpa, batches, steps):

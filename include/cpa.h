@@ -307,7 +307,8 @@ cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void
  *               dim-major (v_dim_major = 1, v_row_stride = dim stride), strides in bytes.
  *   k_scale, v_scale  finite, > 0 (else CPA_ERR_SHAPE): the per-tensor dequantization scales.
  * Other arguments and errors as cpa_chunked_prefill (dtype bf16 for q and o; strides 16-byte
- * multiples).  This path stages pages through registers: no split-KV form.
+ * multiples).  With dim-major V the pages are staged in LDS as codes and converted at operand
+ * read; with token-major V they are converted on their way into LDS.  No split-KV form.
  */
 cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const void* v_pages, int64_t page_stride,
                                      int64_t head_stride, int64_t token_stride, int v_dim_major,

@@ -213,7 +213,9 @@ cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const v
   a.kv_fp8 = 1;
   a.scale_log2 *= k_scale;   // scores of the stored values times the K scale
   a.out_scale = v_scale;     // the output is linear in V
-  return cpa::launch_prefill_regstaged(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+  // dim-major V: the direct-to-LDS kernel converts at operand read; token-major V: the
+  // register-staged kernel converts on the way into LDS
+  return cpa::launch_prefill(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
 cpa_status cpa_build_block_plans(const uint8_t* masks, int B, int Hq, int nqb_max, int nkvb_max,

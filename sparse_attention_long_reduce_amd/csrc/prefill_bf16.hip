@@ -96,8 +96,8 @@ __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 
 
 // 16-byte direct-to-LDS copy: each lane's chunk at byte offset `off` from the wave-uniform
 // `base` lands at ldst + 16 * lane (a 32-bit offset keeps the base in scalar registers)
-__device__ __forceinline__ void lds_dma16(const __bf16* base, uint32_t off, __bf16* ldst) {
-  const char* g = reinterpret_cast<const char*>(base) + off;
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, __bf16* ldst) {
+  const char* g = base + off;
   __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)ldst, 16, 0, 0);
 }
@@ -122,10 +122,18 @@ __device__ __forceinline__ void barrier_keep_vm() {
 template <int I>
 using IC = std::integral_constant<int, I>;
 
-// VT: the V pool is dim-major ([d][token] per page and group, row stride a.v_row_stride)
-template <int D, bool SPLIT, bool VT>
+// VT: the V pool is dim-major ([d][token] per page and group, row stride a.v_row_stride).
+// F8 (with VT): the pools hold OCP e4m3 codes.  A page is copied into LDS as codes, in operand
+// order at 16 codes per 16-byte slot (K: 16 dims of one key, V: 16 keys of one dim row), so its
+// copy moves half the bytes; each lane reads its 8 codes of an operand with one ds_read_b64 and
+// converts them to bf16 exactly (every e4m3 value is a bf16 value).  The K scale is folded into
+// the softmax scale and the V scale into the output (a.out_scale).
+template <int D, bool SPLIT, bool VT, bool F8>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
   using GE = Geo<D>;
+  static_assert(!F8 || VT, "fp8 pages need dim-major V");
+  constexpr int NPW = F8 ? (GE::NPW / 2 > 0 ? GE::NPW / 2 : 1) : GE::NPW;   // copies per wave and page
+  constexpr int EB = F8 ? 1 : 2;                                            // bytes per pool element
   __shared__ __attribute__((aligned(1024))) __bf16 kR0[GE::PAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 kR1[GE::PAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 kR2[GE::PAGE];
@@ -134,7 +142,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   __shared__ __attribute__((aligned(1024))) __bf16 vR1[GE::PAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 vR2[GE::PAGE];
   __shared__ __attribute__((aligned(1024))) __bf16 vR3[GE::PAGE];
-  __shared__ __attribute__((aligned(1024))) __bf16 sink[GE::NPW * 512];  // target of idle copies
+  __shared__ __attribute__((aligned(1024))) __bf16 sink[NPW * 512];  // target of idle copies
   __shared__ int win_kb[WIN];
   __shared__ int win_ph[WIN];
 
@@ -179,8 +187,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     n_iter = max(0, hi - lo);
   }
 
-  const __bf16* __restrict__ kg = reinterpret_cast<const __bf16*>(a.k) + (size_t)g * a.head_stride;
-  const __bf16* __restrict__ vg = reinterpret_cast<const __bf16*>(a.v) + (size_t)g * a.v_head_stride;
+  const char* __restrict__ kg = reinterpret_cast<const char*>(a.k) + (size_t)g * a.head_stride * EB;
+  const char* __restrict__ vg = reinterpret_cast<const char*>(a.v) + (size_t)g * a.v_head_stride * EB;
   const int32_t* __restrict__ pmap = a.page_map + (size_t)b * a.page_map_stride;
 
   // ---- Q in registers (B operand of S^T = K Q^T) -------------------------------------------
@@ -204,15 +212,27 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // waves 0-3 move K, waves 4-7 move V; wave w's instruction j fills the 1 KiB slab
   // s = 4w' + j of its tensor (w' = w % 4), lane l the 16-byte slot l of that slab.
   const bool vrole = wave >= 4;
-  const __bf16* const tg = vrole ? vg : kg;  // this wave's tensor of group g
-  const int64_t pstride = vrole ? a.v_page_stride : a.page_stride;
+  const char* const tg = vrole ? vg : kg;  // this wave's tensor of group g
+  const int64_t pstride = (vrole ? a.v_page_stride : a.page_stride) * EB;   // bytes
   const int rs = (int)(vrole ? a.v_row_stride : a.token_stride);   // elements between rows
-  uint32_t dma_off[GE::NPW];   // byte offset of the lane's source chunk within a page
-  int dma_row[GE::NPW];        // its (first) token
+  uint32_t dma_off[NPW];   // byte offset of the lane's source chunk within a page
+  int dma_row[NPW];        // its (first) token
 #pragma unroll
-  for (int j = 0; j < GE::NPW; ++j) {
-    const int sl = (wave & 3) * GE::NPW + j;
-    if (vrole && VT) {   // operand order: slab (h, u, dt), 8 keys of column 32dt + l % 32
+  for (int j = 0; j < NPW; ++j) {
+    const int sl = (wave & 3) * NPW + j;
+    if (F8) {   // codes in operand order, 16 per slot
+      if (vrole) {   // slab (h, dt): dim row 32dt + l % 32, keys 32h + 16(l / 32) .. +15
+        const int h = sl / GE::DT, dt = sl % GE::DT;
+        const int tok = 32 * h + 16 * hl;
+        dma_row[j] = tok;
+        dma_off[j] = (uint32_t)((32 * dt + l32) * rs + tok);
+      } else {       // slab (h, ks2): key 32h + key_perm(l % 32), dims 32ks2 + 16(l / 32) .. +15
+        const int h = sl / (GE::KS / 2), ks2 = sl % (GE::KS / 2);
+        const int r = 32 * h + key_perm(l32);
+        dma_row[j] = r;
+        dma_off[j] = (uint32_t)(r * rs + 32 * ks2 + 16 * hl);
+      }
+    } else if (vrole && VT) {   // operand order: slab (h, u, dt), 8 keys of column 32dt + l % 32
       const int h = sl / (2 * GE::DT), u = (sl / GE::DT) & 1, dt = sl % GE::DT;
       const int tok = 32 * h + 16 * u + 8 * hl;
       dma_row[j] = tok;
@@ -231,34 +251,38 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       dma_off[j] = (uint32_t)(r * rs + c * 8) * 2u;
     }
   }
-  const int dma_dst = (wave & 3) * GE::NPW * 64 * 8;  // elements; + j * 512
+  const int dma_dst = (wave & 3) * NPW * 64 * 8;  // elements; + j * 512
 
   // A copy is planned at the top of an iteration and issued one direct-to-LDS instruction at a
   // time in between the iteration's MFMAs.  Pages that are unresolved (NaN) or end inside the
   // sequence (rows past the end read as 0) are written through registers at once; their copy
   // instructions, like those of an idle wave, read page 0 of the pool into the sink tile.
   struct Fill {
-    const __bf16* src;   // this wave's tensor (K or V) of the page
-    __bf16* dst;         // this wave's part of the destination tile
+    const char* src;   // this wave's tensor (K or V) of the page
+    __bf16* dst;       // this wave's part of the destination tile
   };
   const Fill idle{tg, sink};
   auto plan = [&](bool valid, int kb, int ph, __bf16* tile) __attribute__((always_inline)) {
     if (!valid) return idle;
     const int nv_tok = min(max(L - 64 * kb, 0), 64);
     if (ph >= 0 && nv_tok == 64) return Fill{tg + (size_t)ph * pstride, tile + dma_dst};
-    const __bf16* src = tg + (size_t)(ph < 0 ? 0 : ph) * pstride;
-    const uint32_t fv = ph < 0 ? 0x7FC07FC0u : 0u;
+    const char* src = tg + (size_t)(ph < 0 ? 0 : ph) * pstride;
+    const uint32_t fv = ph < 0 ? (F8 ? 0x7F7F7F7Fu : 0x7FC07FC0u) : 0u;
+    constexpr int KPC = 16 / EB;   // keys in a dim-major chunk
 #pragma unroll
-    for (int j = 0; j < GE::NPW; ++j) {
+    for (int j = 0; j < NPW; ++j) {
       uint4 v = make_uint4(fv, fv, fv, fv);
       if (ph >= 0 && dma_row[j] < nv_tok) {
-        v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) + dma_off[j]);
-        if (vrole && VT && dma_row[j] + 8 > nv_tok) {   // a chunk of 8 keys crossing the end
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        v = *reinterpret_cast<const uint4*>(src + dma_off[j]);
+        if (vrole && VT && dma_row[j] + KPC > nv_tok) {   // a chunk of keys crossing the end
+          unsigned char by[16];
+          *reinterpret_cast<uint4*>(by) = v;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (dma_row[j] + e >= nv_tok) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          v = make_uint4(w[0], w[1], w[2], w[3]);
+          for (int e = 0; e < KPC; ++e)
+            if (dma_row[j] + e >= nv_tok)
+#pragma unroll
+              for (int y = 0; y < EB; ++y) by[e * EB + y] = 0;
+          v = *reinterpret_cast<const uint4*>(by);
         }
       }
       *reinterpret_cast<uint4*>(tile + dma_dst + j * 512 + lane * 8) = v;
@@ -270,7 +294,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   };
   auto fill_all = [&](const Fill& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < GE::NPW; ++j) fill_one(f, j);
+    for (int j = 0; j < NPW; ++j) fill_one(f, j);
   };
 
   // resolve table entries [base, base + CH) into window slots (base + j) % WIN
@@ -330,15 +354,23 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // ---- the three stages, on units of 32 keys (page half h) ----------------------------------
   // QK: S^T = K Q^T for half h of the page in LDS tile Kl; copy instructions j0 .. j0+NJ-1 of f
   // go out in between
-  constexpr int NJ = GE::NPW / 2 > 0 ? GE::NPW / 2 : 1;   // copy instructions per unit
+  constexpr int NJ = NPW / 2 > 0 ? NPW / 2 : 1;   // copy instructions per unit
+  // F8: the lane's 8 codes of an operand, converted to bf16
+  auto read8 = [&](const __bf16* slab, int slot) __attribute__((always_inline)) {
+    const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(slab) + 16 * slot + 8 * hl);
+    return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(x));
+  };
   auto qk = [&](const __bf16* Kl, int h, f32x16& s, const f32x16& c0, const Fill& f, int j0)
       __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < GE::KS; ++ks) {
-      const int off = k_lane_off + (h * GE::KS + ks) * 512;
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kl + off);
+      bf16x8 ka;
+      if (F8)   // slab (h, ks / 2), slot (ks % 2) * 32 + l % 32
+        ka = read8(Kl + (h * (GE::KS / 2) + ks / 2) * 512, 32 * (ks & 1) + l32);
+      else
+        ka = *reinterpret_cast<const bf16x8*>(Kl + k_lane_off + (h * GE::KS + ks) * 512);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], ks == 0 ? c0 : s, 0, 0, 0);
-      if (ks % (GE::KS / NJ) == 0 && j0 + ks / (GE::KS / NJ) < GE::NPW) fill_one(f, j0 + ks / (GE::KS / NJ));
+      if (ks % (GE::KS / NJ) == 0 && j0 + ks / (GE::KS / NJ) < NPW) fill_one(f, j0 + ks / (GE::KS / NJ));
     }
   };
   // SM, causal cut of half h of page kb: key position must not exceed the row position
@@ -402,7 +434,9 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 #pragma unroll
       for (int dt = 0; dt < GE::DT; ++dt) {
         bf16x8 va;
-        if (VT) {
+        if (F8) {   // slab (h, dt), slot u * 32 + l % 32
+          va = read8(Vl + (h * GE::DT + dt) * 512, 32 * u + l32);
+        } else if (VT) {
           va = *reinterpret_cast<const bf16x8*>(Vl + ((2 * h + u) * GE::DT + dt) * 512 + k_lane_off);
         } else {
           const v4i16 lo = ds_read_tr(Vl + krow + v_off[dt]);
@@ -528,14 +562,14 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       const Fill f = plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) % 4) : kr(r));
       unit(sy, kb_c0, 1, py0, py1, kr((r + 1) % 4), 0, sx, vr(r), 0, px0, px1, f, 0);
       unit(sx, kb_c1, 0, px0, px1, kr((r + 1) % 4), 1, sy, vr(r), 1, py0, py1, f, NJ);
-      barrier_keep_vm<2 * GE::NPW>();
+      barrier_keep_vm<2 * NPW>();
       advance(i);
     };
     // copies and barrier only (the wave has no page i)
     auto idle_step = [&](const int i) __attribute__((always_inline)) {
       const int r = i & 3;
       fill_all(plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r)));
-      barrier_keep_vm<2 * GE::NPW>();
+      barrier_keep_vm<2 * NPW>();
       advance(i);
     };
 
@@ -569,7 +603,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       pv(vr(r), 0, px0, px1);
       if (moved) rescale(alpha);
       pv(vr(r), 1, py0, py1);
-      barrier_keep_vm<2 * GE::NPW>();
+      barrier_keep_vm<2 * NPW>();
       advance(i);
       ++i;
     }
@@ -580,7 +614,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // ---- epilogue ----------------------------------------------------------------------------
   if (!row_ok) return;
   const float lt = xhalf_sum(l_run);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float inv = lt > 0.f ? a.out_scale / lt : 0.f;   // out_scale: the fp8 V scale, else 1
   if (SPLIT) {   // normalised partial output and LSE of this range, fp32
     if (q0 + row >= a.total_q) return;   // rows past total_q (inconsistent cu_q) have no slot
     const size_t rh = (size_t)split * a.total_q * a.Hq + (size_t)(q0 + row) * a.Hq + head;
@@ -648,12 +682,16 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const int grid = prefill_grid(a);
   if (grid == 0) return hipSuccess;
   const bool split = a.n_splits > 1;
+  if (a.kv_fp8) {   // fp8 pages, dim-major V, no split
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.v_dmajor) {
-    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
   } else {
-    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -670,6 +708,8 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
+  if (a.kv_fp8 && (!a.v_dmajor || a.n_splits > 1 || a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
+    return launch_prefill_regstaged(a, true, d, s);   // fp8 forms the direct-to-LDS kernel does not take
   if (!bf16) return launch_prefill_regstaged(a, false, d, s);
   if (a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24))   // 32-bit offsets within a page
     return launch_prefill_regstaged(a, true, d, s);

@@ -23,6 +23,17 @@ constexpr float kSumLimit = 1073741824.0f;
 // 8(l/32) + 0..7 in those elements, matching the V operand.
 __device__ __forceinline__ int key_perm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+// 8 e4m3 codes (OCP fp8) -> their 8 values in bf16 (exact), as one 16-byte chunk; each
+// instruction converts the two codes of the low (false) or high (true) 16 bits, scale 1
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 x) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false),
+                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true)};
+  return __builtin_bit_cast(uint4, h);
+}
+
 // max / sum of x over lanes l and l^32 (the two lanes that share a query row)
 __device__ __forceinline__ float xhalf_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -78,17 +78,6 @@ struct Cfg {
   static constexpr int DT = D / 32;                 // 32-wide output column tiles
 };
 
-// 8 e4m3 codes (OCP fp8) -> their 8 values in bf16 (exact), as one 16-byte chunk; each
-// instruction converts the two codes of the low (false) or high (true) 16 bits, scale 1
-__device__ __forceinline__ uint4 fp8x8_to_bf16(uint2 x) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t h[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false),
-                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true),
-                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false),
-                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true)};
-  return __builtin_bit_cast(uint4, h);
-}
-
 template <bool BF, int D, bool KV8>
 __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   using C = Cfg<BF, D>;

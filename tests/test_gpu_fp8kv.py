@@ -1,7 +1,8 @@
 """GPU parity of the fp8 KV path (cpa_chunked_prefill_fp8kv) against the fp64 oracle.
 
 The pools hold OCP e4m3 codes; the oracle attends over its own dequantization of the same codes,
-decode(x) * scale, so the bars are those of the bf16 path.  The append of fp8 rows
+decode(x) * scale, so the bars are those of the bf16 path.  Dim-major V runs the direct-to-LDS
+kernel (codes in LDS, converted at operand read), token-major V the register-staged one.  The append of fp8 rows
 is checked bit for bit.
 """
 import numpy as np
@@ -78,12 +79,13 @@ def test_fp8kv_small(name, v_layout):
         assert np.max(np.abs(lg[fin] - L.T[fin])) < 2 ** -7
 
 
-def test_fp8kv_poison_unselected_pages_and_tail_tokens():
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_fp8kv_poison_unselected_pages_and_tail_tokens(v_layout):
     w = make_workload("p", [0, 192, 4096], [37, 130, 255], 8, 2, 128, "bf16", bern(0.05), 62)
     kc, vc, _, _ = fp8_setup(w)
     dv = upload(w)
     tables, counts = gpu_tables(dv, w)
-    o1, l1 = run(dv, w, tables, counts, kc, vc, "token")
+    o1, l1 = run(dv, w, tables, counts, kc, vc, v_layout)
     T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
     keep = np.zeros(w.n_pages, dtype=bool)
     for b in range(w.B):
@@ -97,17 +99,18 @@ def test_fp8kv_poison_unselected_pages_and_tail_tokens():
         if L % 64:
             kp[w.page_map[b, L // 64], :, L % 64:] = 0x7F
             vp[w.page_map[b, L // 64], :, L % 64:] = 0x7F
-    o2, l2 = run(dv, w, tables, counts, kp, vp, "token")
+    o2, l2 = run(dv, w, tables, counts, kp, vp, v_layout)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_fp8kv_full_size_128k():
-    print("\n[case] fp8 kv full c3", flush=True)
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_fp8kv_full_size_128k(v_layout):
+    print(f"\n[case] fp8 kv full c3 {v_layout}", flush=True)
     w = make_config("c3_128k_last_chunk")
     kc, vc, kdq, vdq = fp8_setup(w)
     dv = upload(w)
     tables, counts = gpu_tables(dv, w)
-    o, lse = run(dv, w, tables, counts, kc, vc, "token")
+    o, lse = run(dv, w, tables, counts, kc, vc, v_layout)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
@@ -115,7 +118,7 @@ def test_fp8kv_full_size_128k():
     Os, Ls = oracle.attention_rows(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv, S)
     r = torch.from_numpy(w.cu_q[S[:, 0]] + S[:, 2]).cuda()
     h = torch.from_numpy(S[:, 1]).cuda()
-    compare(w, o[r, h].float().cpu().numpy(), Os, "fp8 c3")
+    compare(w, o[r, h].float().cpu().numpy(), Os, f"fp8 c3 {v_layout}")
     assert np.max(np.abs(lse[r, h].cpu().numpy() - Ls)) < 2e-2
 
 
