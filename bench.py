@@ -550,7 +550,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": read_traffic(args.workload, args.v_layout),
                      "kernel": f"prefill_bf16_kernel<128, {'true' if bt0.split_pages else 'false'}, "
-                               f"{'true' if args.v_layout == 'dim' else 'false'}>"},
+                               f"{'true' if args.v_layout == 'dim' else 'false'}, false>"},
         "table_build_roofline": {
             "bound": "hbm", "achieved": round((mask_bytes + tab_bytes) / (r["build_ms"] * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
