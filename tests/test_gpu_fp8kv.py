@@ -143,3 +143,32 @@ def test_fp8_append_bit_exact(v_layout):
     got_v = got_v.transpose(2, 3) if v_layout == "dim" else got_v
     assert np.array_equal(kp.view(torch.uint8).cpu().numpy(), K)
     assert np.array_equal(got_v.cpu().numpy(), V)
+
+
+@pytest.mark.parametrize("kv", ["bf16-dim", "fp8-token", "fp8-dim"])
+def test_out_of_range_page_id_reads_as_nan(kv):
+    # a block that only group 1 selects gets a page id outside the pool: group 1's heads turn NaN
+    # exactly on the rows that reach the block, group 0 is unaffected
+    w = make_workload("oor", [768], [256], 8, 2, 64, "bf16", bern(0.05), 64)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    only1 = sorted(set(T[0, 1, :C[0, 1]].tolist()) - set(T[0, 0, :C[0, 0]].tolist()))
+    assert only1, "need a block selected by group 1 only"
+    kb = only1[0]
+    pm = w.page_map.copy()
+    pm[0, kb] = w.n_pages + 5
+    dv = upload(w, page_map=pm)
+    tables, counts = gpu_tables(dv, w)
+    dtype, layout = kv.split("-")
+    if dtype == "fp8":
+        kc, vc, kdq, vdq = fp8_setup(w)
+        o, _ = run(dv, w, tables, counts, kc, vc, layout)
+    else:
+        kdq, vdq = w.k_pages, w.v_pages
+        o, _ = cpa.chunked_prefill(dv["q"], dv["kp"], dv["vp"].transpose(2, 3).contiguous(), dv["pm"], tables, counts,
+                                   dv["cu"], dv["pl"], w.max_chunk_len, return_lse=True, v_layout="dim")
+    torch.cuda.synchronize()
+    on = o.float().cpu().numpy()
+    seeing = np.arange(int(w.chunk_len[0])) + int(w.prefix_len[0]) >= 64 * kb
+    assert np.all(np.isnan(on[seeing][:, 4:8])) and not np.any(np.isnan(on[~seeing][:, 4:8]))
+    O, _ = oracle.paged_attention(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
+    compare(w, o[:, :4], O[:, :4], f"{kv}: group 0 unaffected")
