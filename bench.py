@@ -424,8 +424,9 @@ def main():
                          "kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the path is measured on one GPU's share "
-              "(see the sharding notes in DESIGN.md); --gpus must be 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: every figure it reports is one GPU's (the path shards "
+              "along KV groups or the sequence with no change to the kernels); --gpus must be 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
