@@ -309,7 +309,8 @@ def time_graph(cpa, batches, steps):
 
 def time_fp8kv(cpa, bt, steps, warmup=3):
     """The batch's prefill over an fp8 (e4m3) copy of its KV cache, per-tensor scale 1/4
-    (cpa_chunked_prefill_fp8kv, token-major V), HIP events around each launch."""
+    (cpa_chunked_prefill_fp8kv), with dim-major and with token-major V, HIP events around each
+    launch."""
     import numpy as np
     import torch
     w = bt.w
@@ -337,7 +338,7 @@ def time_fp8kv(cpa, bt, steps, warmup=3):
     ms_tok = timed_ms(vp8, "token")
     return {"prefill_ms": round(ms_dim, 4), "prefill_ms_token_major_v": round(ms_tok, 4),
             "kv_bytes": int(kp8.numel() + vp8.numel()), "kv_bytes_bf16": int(2 * (kp8.numel() + vp8.numel())),
-            "note": "dim-major V: codes staged in LDS and converted at operand read; token-major V: "
+            "note": "dim-major V: codes staged in LDS, converted to bf16 once per workgroup; token-major V: "
                     "register-staged conversion"}
 
 

@@ -29,7 +29,8 @@
 //      32h + 16u + 8(l / 32) .. +7, and each operand is one ds_read_b128.  The transposed read
 //      delivers half the bytes per LDS cycle of ds_read_b128, so the dim-major layout halves
 //      the LDS time of the V operands.
-// No staging registers and no LDS stores are needed.  Waves 0-3 copy K, waves 4-7 copy V.
+// For bf16 pages no staging registers and no LDS stores are needed.  Waves 0-3 copy K, waves
+// 4-7 copy V.
 //
 // Software pipeline.  Per page (64 keys) and wave (32 query rows), in the transposed domain so
 // that each lane owns whole query rows:
@@ -123,10 +124,16 @@ template <int I>
 using IC = std::integral_constant<int, I>;
 
 // VT: the V pool is dim-major ([d][token] per page and group, row stride a.v_row_stride).
-// F8 (with VT): the pools hold OCP e4m3 codes.  A page is copied into LDS as codes, in operand
-// order at 16 codes per 16-byte slot (K: 16 dims of one key, V: 16 keys of one dim row), so its
-// copy moves half the bytes; each lane reads its 8 codes of an operand with one ds_read_b64 and
-// converts them to bf16 exactly (every e4m3 value is a bf16 value).  The K scale is folded into
+// F8 (with VT): the pools hold OCP e4m3 codes.  A page is copied into an LDS staging tile as
+// codes, 16 per 16-byte slot: staging slot 32s + m holds the codes that become slots m and
+// m + 32 of slab s of the bf16 operand-order tile (K: 16 dims of one key, V: 16 keys of one dim
+// row).  Once the codes have landed, the whole workgroup converts the page to bf16 exactly
+// (every e4m3 value is a bf16 value), each thread one staging slot per tensor and page, and
+// from then on the page is read as in the bf16 dim-major case.  Converting once per workgroup
+// instead of once per reading wave costs 1/8 of the conversions.  The pipeline runs one page
+// further ahead: iteration i copies K codes of page i+5 and V codes of page i+4, converts K of
+// page i+2 and V of page i+1 (copied in iteration i-3), and reads K of page i+1 and V of page
+// i, so the staging rings hold four pages and the bf16 rings two.  The K scale is folded into
 // the softmax scale and the V scale into the output (a.out_scale).
 template <int D, bool SPLIT, bool VT, bool F8>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
@@ -220,17 +227,16 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
     const int sl = (wave & 3) * NPW + j;
-    if (F8) {   // codes in operand order, 16 per slot
-      if (vrole) {   // slab (h, dt): dim row 32dt + l % 32, keys 32h + 16(l / 32) .. +15
-        const int h = sl / GE::DT, dt = sl % GE::DT;
-        const int tok = 32 * h + 16 * hl;
+    if (F8) {   // staging slot 64 sl + l: slots l % 32 and l % 32 + 32 of bf16 slab sb = 2 sl + l / 32
+      const int sb = 2 * sl + hl;
+      if (vrole) {   // slab ((2h + u) DT + dt): dim row 32dt + l % 32, keys 32h + 16u .. +15
+        const int tok = 16 * (sb / GE::DT), dt = sb % GE::DT;
         dma_row[j] = tok;
         dma_off[j] = (uint32_t)((32 * dt + l32) * rs + tok);
-      } else {       // slab (h, ks2): key 32h + key_perm(l % 32), dims 32ks2 + 16(l / 32) .. +15
-        const int h = sl / (GE::KS / 2), ks2 = sl % (GE::KS / 2);
-        const int r = 32 * h + key_perm(l32);
+      } else {       // slab (h, ks): key 32h + key_perm(l % 32), dims 16ks .. +15
+        const int r = 32 * (sb / GE::KS) + key_perm(l32), ks = sb % GE::KS;
         dma_row[j] = r;
-        dma_off[j] = (uint32_t)(r * rs + 32 * ks2 + 16 * hl);
+        dma_off[j] = (uint32_t)(r * rs + 16 * ks);
       }
     } else if (vrole && VT) {   // operand order: slab (h, u, dt), 8 keys of column 32dt + l % 32
       const int h = sl / (2 * GE::DT), u = (sl / GE::DT) & 1, dt = sl % GE::DT;
@@ -355,20 +361,28 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // QK: S^T = K Q^T for half h of the page in LDS tile Kl; copy instructions j0 .. j0+NJ-1 of f
   // go out in between
   constexpr int NJ = NPW / 2 > 0 ? NPW / 2 : 1;   // copy instructions per unit
-  // F8: the lane's 8 codes of an operand, converted to bf16
-  auto read8 = [&](const __bf16* slab, int slot) __attribute__((always_inline)) {
-    const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(slab) + 16 * slot + 8 * hl);
-    return __builtin_bit_cast(bf16x8, fp8x8_to_bf16(x));
+  // F8: staging slot t of a page (src, codes) to slots t % 32 and t % 32 + 32 of bf16 slab t / 32
+  // (dst)
+  constexpr int NS = GE::PAGE / 16;   // staging slots of one tensor's page
+  auto convert_slot = [&](const __bf16* src, __bf16* dst, int t) __attribute__((always_inline)) {
+    const uint4 c = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) + 16 * t);
+    __bf16* d = dst + (t >> 5) * 512 + (t & 31) * 8;
+    *reinterpret_cast<uint4*>(d) = fp8x8_to_bf16(make_uint2(c.x, c.y));
+    *reinterpret_cast<uint4*>(d + 256) = fp8x8_to_bf16(make_uint2(c.z, c.w));
+  };
+  // F8: conversion item `it` of this thread in an iteration: item x = tid + 512 it is staging slot
+  // x of the K page (x < NS) or slot x - NS of the V page (wave-uniform choice)
+  auto convert_item = [&](int it, const __bf16* ksrc, __bf16* kdst, const __bf16* vsrc, __bf16* vdst)
+      __attribute__((always_inline)) {
+    const int x = tid + THREADS * it;
+    const bool isv = x >= NS;
+    if (x < 2 * NS) convert_slot(isv ? vsrc : ksrc, isv ? vdst : kdst, isv ? x - NS : x);
   };
   auto qk = [&](const __bf16* Kl, int h, f32x16& s, const f32x16& c0, const Fill& f, int j0)
       __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < GE::KS; ++ks) {
-      bf16x8 ka;
-      if (F8)   // slab (h, ks / 2), slot (ks % 2) * 32 + l % 32
-        ka = read8(Kl + (h * (GE::KS / 2) + ks / 2) * 512, 32 * (ks & 1) + l32);
-      else
-        ka = *reinterpret_cast<const bf16x8*>(Kl + k_lane_off + (h * GE::KS + ks) * 512);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kl + k_lane_off + (h * GE::KS + ks) * 512);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], ks == 0 ? c0 : s, 0, 0, 0);
       if (ks % (GE::KS / NJ) == 0 && j0 + ks / (GE::KS / NJ) < NPW) fill_one(f, j0 + ks / (GE::KS / NJ));
     }
@@ -434,9 +448,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 #pragma unroll
       for (int dt = 0; dt < GE::DT; ++dt) {
         bf16x8 va;
-        if (F8) {   // slab (h, dt), slot u * 32 + l % 32
-          va = read8(Vl + (h * GE::DT + dt) * 512, 32 * u + l32);
-        } else if (VT) {
+        if (VT) {
           va = *reinterpret_cast<const bf16x8*>(Vl + ((2 * h + u) * GE::DT + dt) * 512 + k_lane_off);
         } else {
           const v4i16 lo = ds_read_tr(Vl + krow + v_off[dt]);
@@ -498,17 +510,60 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     auto ph_at = [&](int j) __attribute__((always_inline)) { return win_ph[j % WIN]; };
     auto kr = [&](int t) __attribute__((always_inline)) { return t == 0 ? kR0 : t == 1 ? kR1 : t == 2 ? kR2 : kR3; };
     auto vr = [&](int t) __attribute__((always_inline)) { return t == 0 ? vR0 : t == 1 ? vR1 : t == 2 ? vR2 : vR3; };
-    // prologue copies: K of pages 0, 1 and V of page 0 resident; K of pages 2, 3 and V of pages
-    // 1, 2 in flight (the copies of iterations -2 and -1)
-    if (!vrole) {
-      fill_all(plan(true, kb_at(0), ph_at(0), kR0));
-      fill_all(plan(n_iter > 1, kb_at(1), ph_at(1), kR1));
+    // F8: bf16 pages in tiles 0 and 1, the four staging pages of codes in tiles 2 and 3
+    auto kst = [&](int s) __attribute__((always_inline)) { return (s < 2 ? kR2 : kR3) + (s & 1) * (GE::PAGE / 2); };
+    auto vst = [&](int s) __attribute__((always_inline)) { return (s < 2 ? vR2 : vR3) + (s & 1) * (GE::PAGE / 2); };
+    // tiles of iteration i, r = i mod 4: K read by QK (page i+1), V read by PV (page i), and the
+    // destination of this wave's copy (K of page i + fo, V of page i + fo, below)
+    auto k_tile = [&](int r) __attribute__((always_inline)) { return F8 ? kr((r + 1) & 1) : kr((r + 1) & 3); };
+    auto v_tile = [&](int r) __attribute__((always_inline)) { return F8 ? vr(r & 1) : vr(r & 3); };
+    auto copy_tile = [&](int r) __attribute__((always_inline)) {
+      if (F8) return vrole ? vst(r & 3) : kst((r + 1) & 3);
+      return vrole ? vr((r + 3) & 3) : kr(r & 3);
+    };
+    // F8, iteration i: item `it` of the conversion of K page i+2 (staging (i+2) mod 4 -> bf16
+    // (i+2) mod 2) and V page i+1 (staging (i+1) mod 4 -> bf16 (i+1) mod 2).  Pages past the
+    // table convert stale codes into tiles nobody reads.
+    constexpr int NIT = F8 ? (2 * NS + THREADS - 1) / THREADS : 0;   // items per thread and iteration
+    auto convert_all = [&](int r) __attribute__((always_inline)) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) convert_item(it, kst((r + 2) & 3), kr(r & 1), vst((r + 1) & 3), vr((r + 1) & 1));
+    };
+    Fill fm1;
+    if (F8) {
+      // prologue: codes of K pages 0-2 and V pages 0-1 (iterations -5 .. -3 of the copy schedule)
+      // land; those of K page 3 and V page 2 go out; K pages 0, 1 and V page 0 are converted;
+      // the copies of K page 4 and V page 3 go out during the prologue's QK
+      if (!vrole) {
+        fill_all(plan(true, kb_at(0), ph_at(0), kst(0)));
+        fill_all(plan(n_iter > 1, kb_at(1), ph_at(1), kst(1)));
+        fill_all(plan(n_iter > 2, kb_at(2), ph_at(2), kst(2)));
+      } else {
+        fill_all(plan(true, kb_at(0), ph_at(0), vst(0)));
+        fill_all(plan(n_iter > 1, kb_at(1), ph_at(1), vst(1)));
+      }
+      barrier_keep_vm<0>();
+      fill_all(vrole ? plan(n_iter > 2, kb_at(2), ph_at(2), vst(2)) : plan(n_iter > 3, kb_at(3), ph_at(3), kst(3)));
+      for (int t = tid; t < NS; t += THREADS) {
+        convert_slot(kst(0), kR0, t);
+        convert_slot(kst(1), kR1, t);
+        convert_slot(vst(0), vR0, t);
+      }
+      barrier_keep_vm<NPW>();
+      fm1 = vrole ? plan(n_iter > 3, kb_at(3), ph_at(3), vst(3)) : plan(n_iter > 4, kb_at(4), ph_at(4), kst(0));
     } else {
-      fill_all(plan(true, kb_at(0), ph_at(0), vR0));
+      // prologue copies: K of pages 0, 1 and V of page 0 resident; K of pages 2, 3 and V of pages
+      // 1, 2 in flight (the copies of iterations -2 and -1)
+      if (!vrole) {
+        fill_all(plan(true, kb_at(0), ph_at(0), kR0));
+        fill_all(plan(n_iter > 1, kb_at(1), ph_at(1), kR1));
+      } else {
+        fill_all(plan(true, kb_at(0), ph_at(0), vR0));
+      }
+      barrier_keep_vm<0>();
+      fill_all(vrole ? plan(n_iter > 1, kb_at(1), ph_at(1), vR1) : plan(n_iter > 2, kb_at(2), ph_at(2), kR2));
+      fm1 = vrole ? plan(n_iter > 2, kb_at(2), ph_at(2), vR2) : plan(n_iter > 3, kb_at(3), ph_at(3), kR3);
     }
-    barrier_keep_vm<0>();
-    fill_all(vrole ? plan(n_iter > 1, kb_at(1), ph_at(1), vR1) : plan(n_iter > 2, kb_at(2), ph_at(2), kR2));
-    const Fill fm1 = vrole ? plan(n_iter > 2, kb_at(2), ph_at(2), vR2) : plan(n_iter > 3, kb_at(3), ph_at(3), kR3);
     if (n_vis > 0) {
       qk(kR0, 0, sx, cm, fm1, 0);   // cm = 0: raw scores
       causal(sx, kb_at(0), 0);
@@ -531,16 +586,17 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     // copies.  Those of iteration i+2 are read from the window during iteration i and held in
     // registers, so the reads' latency is covered by the iteration's work.  Slots past the table
     // hold stale ids; they are read but never used (every use is guarded by the page's range).
-    const int fo = vrole ? 3 : 4;   // iteration i copies page i + fo
+    constexpr int FOK = F8 ? 5 : 4;   // iteration i copies K of page i + FOK, V of page i + FOK - 1
+    const int fo = vrole ? FOK - 1 : FOK;
     int vzero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
     int kb_c0 = kb_at(0), kb_c1 = kb_at(1), kb_c1n = kb_at(2);
     int kb_f = kb_at(fo), ph_f = ph_at(fo), kb_fn = kb_at(fo + 1), ph_fn = ph_at(fo + 1);
-    // end of iteration i: resolve the next chunk of the window when entry i+6 (the furthest
-    // read below) starts one, read the ids of iteration i+2, shift the queue
+    // end of iteration i: resolve the next chunk of the window when entry i + 2 + FOK (the
+    // furthest read below) starts one, read the ids of iteration i+2, shift the queue
     auto advance = [&](const int i) __attribute__((always_inline)) {
-      if ((i + 6) % CH == 0 && i + 6 < n_iter) {
-        load_chunk(i + 6);
+      if ((i + 2 + FOK) % CH == 0 && i + 2 + FOK < n_iter) {
+        load_chunk(i + 2 + FOK);
         __syncthreads();
       }
       // the fresh ids stay in vector registers (the opaque zero in the slot index keeps the
@@ -555,20 +611,24 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       kb_fn = l_kbf;
       ph_fn = l_phf;
     };
-    // iteration i (R = i mod 4): units 2i+1 and 2i+2; K of page i+1 in tile (R+1)%4, V of page
-    // i in tile R; copies of K of page i+4 into tile R and of V of page i+3 into tile (R+3)%4
+    // iteration i (R = i mod 4): units 2i+1 and 2i+2 on K of page i+1 and V of page i; this
+    // wave's copy of page i + fo; with F8 the conversions of the iteration, last, where a wave
+    // would otherwise wait at the barrier for the others (measured faster than placing them
+    // before or between the units, or inside the units' blocks)
     auto step = [&](auto Rc, const int i) __attribute__((always_inline)) {
       constexpr int r = decltype(Rc)::value;
-      const Fill f = plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) % 4) : kr(r));
-      unit(sy, kb_c0, 1, py0, py1, kr((r + 1) % 4), 0, sx, vr(r), 0, px0, px1, f, 0);
-      unit(sx, kb_c1, 0, px0, px1, kr((r + 1) % 4), 1, sy, vr(r), 1, py0, py1, f, NJ);
+      const Fill f = plan(i + fo < n_iter, kb_f, ph_f, copy_tile(r));
+      unit(sy, kb_c0, 1, py0, py1, k_tile(r), 0, sx, v_tile(r), 0, px0, px1, f, 0);
+      unit(sx, kb_c1, 0, px0, px1, k_tile(r), 1, sy, v_tile(r), 1, py0, py1, f, NJ);
+      convert_all(r);
       barrier_keep_vm<2 * NPW>();
       advance(i);
     };
-    // copies and barrier only (the wave has no page i)
+    // copies (and conversions) and barrier only (the wave has no page i)
     auto idle_step = [&](const int i) __attribute__((always_inline)) {
       const int r = i & 3;
-      fill_all(plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r)));
+      fill_all(plan(i + fo < n_iter, kb_f, ph_f, copy_tile(r)));
+      convert_all(r);
       barrier_keep_vm<2 * NPW>();
       advance(i);
     };
@@ -590,7 +650,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     if (n_vis > 0) {
       // drain (iteration n_vis - 1): SM of its last unit, PV of its last two units
       const int r = i & 3;
-      fill_all(plan(i + fo < n_iter, kb_f, ph_f, vrole ? vr((r + 3) & 3) : kr(r)));
+      fill_all(plan(i + fo < n_iter, kb_f, ph_f, copy_tile(r)));
+      convert_all(r);
       causal(sy, kb_c0, 1);
       float lu = weights(sy, py0, py1);
       const bool moved = __builtin_amdgcn_ballot_w64(!(lu < kSumLimit)) != 0;
@@ -600,9 +661,9 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
         lu = weights(sy, py0, py1);
       }
       l_run += lu;
-      pv(vr(r), 0, px0, px1);
+      pv(v_tile(r), 0, px0, px1);
       if (moved) rescale(alpha);
-      pv(vr(r), 1, py0, py1);
+      pv(v_tile(r), 1, py0, py1);
       barrier_keep_vm<2 * NPW>();
       advance(i);
       ++i;
