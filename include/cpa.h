@@ -297,7 +297,8 @@ cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void
  * cpa_chunked_prefill_fp8kv - cpa_chunked_prefill with bf16 q / o and a KV cache of fp8 pages
  * (OCP e4m3, one byte per element): the same attention over the same tables (CompactAttention
  * abstract), over the keys decode(k) * k_scale and values decode(v) * v_scale.  Pages are
- * converted to bf16 on their way into LDS (exact: bf16 holds every e4m3 value); the K scale
+ * converted to bf16 once per workgroup, in LDS (dim-major V) or on their way into LDS
+ * (token-major V); the conversion is exact, as bf16 holds every e4m3 value.  The K scale
  * joins the softmax scale and the V scale multiplies the normalised output, both in fp32.  The
  * attention is the bf16 path's (bf16 MFMA, fp32 softmax, bf16 P).  The cache takes half the
  * memory of bf16.
