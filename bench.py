@@ -46,6 +46,9 @@ WORKLOADS = {
     "c3s": ("c3s_128k_one_group", "one KV group's share of the 128K last chunk (the per-GPU share of "
             "an 8-way head split): prefix 129024 + chunk 2048, Hq 4 / Hkv 1 / d 128, bf16, "
             "structured masks, split-KV"),
+    "c3d": ("c3d_128k_no_noise", "diagnostic: the 128K last chunk (prefix 129024 + chunk 2048, Hq 32 / "
+            "Hkv 8 / d 128, bf16) with the headline's stripes, slashes, sink and local window but "
+            "without its Bernoulli(0.02) noise term, so the group unions stay sparse"),
 }
 
 

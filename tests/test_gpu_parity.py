@@ -125,7 +125,8 @@ def test_config1_full():
 
 BIG = [("c2_32k_bf16", {}), ("c3_128k_last_chunk", {}), ("c4_128k_chunked", {"chunk": 0}),
        ("c4_128k_chunked", {"chunk": 17}), ("c4_128k_chunked", {"chunk": 63}),
-       ("c5a_varlen_shared", {}), ("c5b_varlen_independent", {}), ("c3_128k_last_chunk", {"dense": True})]
+       ("c5a_varlen_shared", {}), ("c5b_varlen_independent", {}), ("c3_128k_last_chunk", {"dense": True}),
+       ("c3d_128k_no_noise", {})]
 
 
 @pytest.mark.parametrize("name,kw", BIG, ids=[f"{n}{kw}" for n, kw in BIG])

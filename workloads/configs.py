@@ -239,11 +239,17 @@ CONFIG_NAMES = (
 
 SEEDS = {"c1_tiny_f32": 1001, "c2_32k_bf16": 1002, "c3_128k_last_chunk": 1003,
          "c4_128k_chunked": 1004, "c5a_varlen_shared": 1005, "c5b_varlen_independent": 1006,
-         "c3s_128k_one_group": 1007}
+         "c3s_128k_one_group": 1007, "c3d_128k_no_noise": 1003}
 
 # One KV group's share of the 128K last-chunk workload: what each of 8 GPUs would hold if the
 # layer's 8 KV groups were split across them (4 query heads, 1 KV head); 32 query tiles.
 SHARD_NAMES = ("c3s_128k_one_group",)
+
+# A diagnostic, never a replacement for the headline workload: the 128K last chunk with the same
+# seed and generator but without the per-entry Bernoulli(0.02) term, so its stripes, slashes, sink
+# and local window are exactly the headline's and the group unions stay sparse (about a quarter
+# of the blocks) instead of near-dense.
+DIAG_NAMES = ("c3d_128k_no_noise",)
 
 C4_SEQ = 131072
 C4_CHUNK = 2048
@@ -321,6 +327,9 @@ def make_config(name: str, dense: bool = False, chunk: int = 63, seed: int | Non
         return make_workload(name, [129024], [2048], 32, 8, 128, "bf16", fn, s)
     if name == "c4_128k_chunked":
         return chunked_sequence_chunk(chunk, dense=dense, seed=seed)
+    if name == "c3d_128k_no_noise":
+        fn = ones if dense else (lambda rng, *a: mask_structured(rng, *a, bern_p=0.0))
+        return make_workload(name, [129024], [2048], 32, 8, 128, "bf16", fn, s)
     if name == "c3s_128k_one_group":
         fn = ones if dense else mask_structured
         return make_workload(name, [129024], [2048], 4, 1, 128, "bf16", fn, s)
