@@ -341,8 +341,8 @@ def time_fp8kv(cpa, bt, steps, warmup=3):
     ms_tok = timed_ms(vp8, "token")
     return {"prefill_ms": round(ms_dim, 4), "prefill_ms_token_major_v": round(ms_tok, 4),
             "kv_bytes": int(kp8.numel() + vp8.numel()), "kv_bytes_bf16": int(2 * (kp8.numel() + vp8.numel())),
-            "note": "dim-major V: codes staged in LDS, converted to bf16 once per workgroup; token-major V: "
-                    "register-staged conversion"}
+            "note": "codes staged in LDS and converted to bf16 once per workgroup; token-major V transposed "
+                    "by ds_read_b64_tr_b8 on the way"}
 
 
 def time_build_bits(cpa, batches, steps):

@@ -213,8 +213,8 @@ cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const v
   a.kv_fp8 = 1;
   a.scale_log2 *= k_scale;   // scores of the stored values times the K scale
   a.out_scale = v_scale;     // the output is linear in V
-  // dim-major V: the direct-to-LDS kernel converts at operand read; token-major V: the
-  // register-staged kernel converts on the way into LDS
+  // either V layout: the direct-to-LDS kernel stages codes and converts each page once per
+  // workgroup; pools whose strides overflow its 32-bit offsets go to the register-staged kernel
   return cpa::launch_prefill(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 

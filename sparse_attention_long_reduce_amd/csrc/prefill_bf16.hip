@@ -81,6 +81,8 @@ constexpr int CH = 512;    // ids resolved at a time
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
 
 template <int D>
 struct Geo {
@@ -94,6 +96,11 @@ struct Geo {
 // chunk position of V chunk c of row r is c ^ swz_v(r)
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// fp8 token-major V staging: 16-code chunk c of token t sits at position c ^ swz_f8(t) of its
+// row, so that the 8 rows of a transposed read fall in 8 different 16-byte bank groups
+template <int D>
+__device__ __forceinline__ int swz_f8(int t) { return D == 128 ? (t & 7) : ((t >> 2) & 1); }
 
 // 16-byte direct-to-LDS copy: each lane's chunk at byte offset `off` from the wave-uniform
 // `base` lands at ldst + 16 * lane (a 32-bit offset keeps the base in scalar registers)
@@ -124,21 +131,27 @@ template <int I>
 using IC = std::integral_constant<int, I>;
 
 // VT: the V pool is dim-major ([d][token] per page and group, row stride a.v_row_stride).
-// F8 (with VT): the pools hold OCP e4m3 codes.  A page is copied into an LDS staging tile as
-// codes, 16 per 16-byte slot: staging slot 32s + m holds the codes that become slots m and
-// m + 32 of slab s of the bf16 operand-order tile (K: 16 dims of one key, V: 16 keys of one dim
-// row).  Once the codes have landed, the whole workgroup converts the page to bf16 exactly
-// (every e4m3 value is a bf16 value), each thread one staging slot per tensor and page, and
-// from then on the page is read as in the bf16 dim-major case.  Converting once per workgroup
-// instead of once per reading wave costs 1/8 of the conversions.  The pipeline runs one page
-// further ahead: iteration i copies K codes of page i+5 and V codes of page i+4, converts K of
-// page i+2 and V of page i+1 (copied in iteration i-3), and reads K of page i+1 and V of page
-// i, so the staging rings hold four pages and the bf16 rings two.  The K scale is folded into
-// the softmax scale and the V scale into the output (a.out_scale).
+// F8: the pools hold OCP e4m3 codes.  A page is copied into an LDS staging tile as codes, 16 per
+// 16-byte slot, and once the codes have landed the whole workgroup converts the page to bf16
+// exactly (every e4m3 value is a bf16 value) into the operand-order tiles of the bf16 dim-major
+// case; from then on the page is read as in that case, whatever the pool's V layout.
+//   K, and V of a dim-major pool: staging slot 32s + m holds the codes that become slots m and
+//   m + 32 of slab s of the bf16 tile (K: 16 dims of one key, V: 16 keys of one dim row); a
+//   thread converts one slot per tensor and page.
+//   V of a token-major pool: staging holds natural rows of 16-code chunks (chunk c of token t at
+//   position c ^ swz_f8(t), so that the reads below avoid bank conflicts).  ds_read_b64_tr_b8
+//   transposes bytes within 16 lanes: lane s supplies half s % 2 of a 16-byte row s / 2, and
+//   lane j receives byte j of each of the 8 rows.  With the rows at 8 consecutive tokens of one
+//   16-dim chunk, lane j gets 8 consecutive keys of dim j: one bf16 operand slot after conversion.
+// Converting once per workgroup instead of once per reading wave costs 1/8 of the conversions.
+// The pipeline runs one page further ahead: iteration i copies K codes of page i+5 and V codes
+// of page i+4, converts K of page i+2 and V of page i+1 (copied in iteration i-3), and reads K
+// of page i+1 and V of page i, so the staging rings hold four pages and the bf16 rings two.
+// The K scale is folded into the softmax scale and the V scale into the output (a.out_scale).
 template <int D, bool SPLIT, bool VT, bool F8>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
   using GE = Geo<D>;
-  static_assert(!F8 || VT, "fp8 pages need dim-major V");
+  constexpr bool VOP = VT || F8;   // V tiles in operand order (8 keys of one dim per slot)
   constexpr int NPW = F8 ? (GE::NPW / 2 > 0 ? GE::NPW / 2 : 1) : GE::NPW;   // copies per wave and page
   constexpr int EB = F8 ? 1 : 2;                                            // bytes per pool element
   __shared__ __attribute__((aligned(1024))) __bf16 kR0[GE::PAGE];
@@ -229,7 +242,13 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     const int sl = (wave & 3) * NPW + j;
     if (F8) {   // staging slot 64 sl + l: slots l % 32 and l % 32 + 32 of bf16 slab sb = 2 sl + l / 32
       const int sb = 2 * sl + hl;
-      if (vrole) {   // slab ((2h + u) DT + dt): dim row 32dt + l % 32, keys 32h + 16u .. +15
+      if (vrole && !VT) {   // natural rows: staging slot p holds chunk p % C8 ^ swz_f8(t) of token t = p / C8
+        constexpr int C8 = D / 16;
+        const int p = 64 * sl + lane;
+        const int t = p / C8;
+        dma_row[j] = t;
+        dma_off[j] = (uint32_t)(t * rs + 16 * ((p % C8) ^ swz_f8<D>(t)));
+      } else if (vrole) {   // slab ((2h + u) DT + dt): dim row 32dt + l % 32, keys 32h + 16u .. +15
         const int tok = 16 * (sb / GE::DT), dt = sb % GE::DT;
         dma_row[j] = tok;
         dma_off[j] = (uint32_t)((32 * dt + l32) * rs + tok);
@@ -370,13 +389,38 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     *reinterpret_cast<uint4*>(d) = fp8x8_to_bf16(make_uint2(c.x, c.y));
     *reinterpret_cast<uint4*>(d + 256) = fp8x8_to_bf16(make_uint2(c.z, c.w));
   };
+  // F8, token-major V: lane item v of a page (src, natural rows) into the bf16 tile dst.  Group
+  // v / 16 is key octet m and 16-dim chunk c; lane v % 16 reads half of one of the 8 rows and
+  // receives dim 16c + v % 16 of keys 8m .. 8m+7, which is slot 32(m % 2) + (16c + v % 16) % 32 of
+  // slab (2(m / 4) + (m / 2) % 2) DT + (16c + v % 16) / 32.
+  auto convert_tr = [&](const __bf16* src, __bf16* dst, int v) __attribute__((always_inline)) {
+    constexpr int C8 = D / 16;
+    const int grp = v >> 4, s16 = v & 15;
+    const int m = grp & 7, c = grp >> 3;
+    const int t = 8 * m + (s16 >> 1);
+    const __attribute__((address_space(3))) char* lp =
+        (const __attribute__((address_space(3))) char*)(const __attribute__((address_space(3))) void*)src +
+        16 * (t * C8 + (c ^ swz_f8<D>(t))) + 8 * (s16 & 1);
+    const v2i32 codes = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)lp);
+    const int col = 16 * c + s16;
+    __bf16* d = dst + ((2 * (m >> 2) + ((m >> 1) & 1)) * GE::DT + (col >> 5)) * 512 + (32 * (m & 1) + (col & 31)) * 8;
+    *reinterpret_cast<uint4*>(d) = fp8x8_to_bf16(make_uint2((uint32_t)codes[0], (uint32_t)codes[1]));
+  };
+  // F8: V lane items per page: NS staging slots (dim-major pool) or 2 NS transposed reads
+  constexpr int NV8 = VT ? NS : 2 * NS;
   // F8: conversion item `it` of this thread in an iteration: item x = tid + 512 it is staging slot
-  // x of the K page (x < NS) or slot x - NS of the V page (wave-uniform choice)
+  // x of the K page (x < NS) or V item x - NS (wave-uniform choice)
   auto convert_item = [&](int it, const __bf16* ksrc, __bf16* kdst, const __bf16* vsrc, __bf16* vdst)
       __attribute__((always_inline)) {
     const int x = tid + THREADS * it;
-    const bool isv = x >= NS;
-    if (x < 2 * NS) convert_slot(isv ? vsrc : ksrc, isv ? vdst : kdst, isv ? x - NS : x);
+    if (VT) {
+      const bool isv = x >= NS;
+      if (x < 2 * NS) convert_slot(isv ? vsrc : ksrc, isv ? vdst : kdst, isv ? x - NS : x);
+    } else if (x < NS) {
+      convert_slot(ksrc, kdst, x);
+    } else if (x < NS + NV8) {
+      convert_tr(vsrc, vdst, x - NS);
+    }
   };
   auto qk = [&](const __bf16* Kl, int h, f32x16& s, const f32x16& c0, const Fill& f, int j0)
       __attribute__((always_inline)) {
@@ -394,7 +438,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         // accumulator row 8(j/4) + 4hl + j%4 holds that key, or its key_perm image
-        const int key = k0 + (VT ? 16 * (j >> 3) + 8 * hl + (j & 7) : 8 * (j >> 2) + 4 * hl + (j & 3));
+        const int key = k0 + (VOP ? 16 * (j >> 3) + 8 * hl + (j & 7) : 8 * (j >> 2) + 4 * hl + (j & 3));
         if (key > row_pos) s[j] = -INFINITY;
       }
     }
@@ -448,7 +492,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 #pragma unroll
       for (int dt = 0; dt < GE::DT; ++dt) {
         bf16x8 va;
-        if (VT) {
+        if (VOP) {
           va = *reinterpret_cast<const bf16x8*>(Vl + ((2 * h + u) * GE::DT + dt) * 512 + k_lane_off);
         } else {
           const v4i16 lo = ds_read_tr(Vl + krow + v_off[dt]);
@@ -524,7 +568,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     // F8, iteration i: item `it` of the conversion of K page i+2 (staging (i+2) mod 4 -> bf16
     // (i+2) mod 2) and V page i+1 (staging (i+1) mod 4 -> bf16 (i+1) mod 2).  Pages past the
     // table convert stale codes into tiles nobody reads.
-    constexpr int NIT = F8 ? (2 * NS + THREADS - 1) / THREADS : 0;   // items per thread and iteration
+    constexpr int NIT = F8 ? (NS + NV8 + THREADS - 1) / THREADS : 0;   // items per thread and iteration
     auto convert_all = [&](int r) __attribute__((always_inline)) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) convert_item(it, kst((r + 2) & 3), kr(r & 1), vst((r + 1) & 3), vr((r + 1) & 1));
@@ -547,7 +591,10 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
       for (int t = tid; t < NS; t += THREADS) {
         convert_slot(kst(0), kR0, t);
         convert_slot(kst(1), kR1, t);
-        convert_slot(vst(0), vR0, t);
+      }
+      for (int v = tid; v < NV8; v += THREADS) {
+        if (VT) convert_slot(vst(0), vR0, v);
+        else convert_tr(vst(0), vR0, v);
       }
       barrier_keep_vm<NPW>();
       fm1 = vrole ? plan(n_iter > 3, kb_at(3), ph_at(3), vst(3)) : plan(n_iter > 4, kb_at(4), ph_at(4), kst(0));
@@ -743,8 +790,9 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const int grid = prefill_grid(a);
   if (grid == 0) return hipSuccess;
   const bool split = a.n_splits > 1;
-  if (a.kv_fp8) {   // fp8 pages, dim-major V, no split
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
+  if (a.kv_fp8) {   // fp8 pages, no split
+    if (a.v_dmajor) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
     return hipGetLastError();
   }
   if (a.v_dmajor) {
@@ -769,7 +817,7 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
-  if (a.kv_fp8 && (!a.v_dmajor || a.n_splits > 1 || a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
+  if (a.kv_fp8 && (a.n_splits > 1 || a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
     return launch_prefill_regstaged(a, true, d, s);   // fp8 forms the direct-to-LDS kernel does not take
   if (!bf16) return launch_prefill_regstaged(a, false, d, s);
   if (a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24))   // 32-bit offsets within a page

@@ -1,9 +1,9 @@
 """GPU parity of the fp8 KV path (cpa_chunked_prefill_fp8kv) against the fp64 oracle.
 
 The pools hold OCP e4m3 codes; the oracle attends over its own dequantization of the same codes,
-decode(x) * scale, so the bars are those of the bf16 path.  Dim-major V runs the direct-to-LDS
-kernel (codes in LDS, converted at operand read), token-major V the register-staged one.  The append of fp8 rows
-is checked bit for bit.
+decode(x) * scale, so the bars are those of the bf16 path.  Both V layouts run the direct-to-LDS
+kernel (codes staged in LDS, each page converted to bf16 once per workgroup; token-major V through
+transposed byte reads).  The append of fp8 rows is checked bit for bit.
 """
 import numpy as np
 import pytest

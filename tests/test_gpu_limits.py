@@ -76,3 +76,54 @@ def test_large_groups(Hq, Hkv, d):
         torch.cuda.synchronize()
         compare(w, o, O, f"G={Hq // Hkv} {v_layout}")
         assert np.max(np.abs(lse.cpu().numpy() - L.T)) < 2 ** -7
+
+
+WIDE = (1 << 24) + 64   # row stride in elements: past the direct-to-LDS kernel's 32-bit offsets
+
+
+def wide_view(x, elem):
+    """x [n][H][R][C] (R = 64 tokens, or d dim rows for dim-major V) as a CUDA view with row stride
+    WIDE elements and the usual nesting (head stride R * WIDE, page stride H * R * WIDE): a pool
+    of n * H * R * WIDE elements of which only the rows' first C are written and read."""
+    n, H, R, C = x.shape
+    buf = torch.empty((n * H * R - 1) * WIDE + C, dtype=elem, device="cuda")
+    v = torch.as_strided(buf, (n, H, R, C), (H * R * WIDE, R * WIDE, WIDE, 1))
+    v.copy_(x.cuda())
+    return v
+
+
+@pytest.mark.parametrize("kind,v_layout", [("bf16", "token"), ("bf16", "dim"), ("fp8", "token"), ("fp8", "dim")])
+def test_wide_row_stride_pools(kind, v_layout):
+    # pools whose offsets within a page overflow 32 bits (and whose page offsets reach 2^32
+    # bytes) go through the register-staged kernel; same bars against the oracle.  One KV group,
+    # two KV blocks (the second partial), three pages: 3 * 64 * WIDE elements per tensor.
+    print(f"\n[case] wide row stride {kind} {v_layout}", flush=True)
+    w = make_workload("wide", [0], [100], 4, 1, 64, "bf16",
+                      lambda rng, *a: mask_bernoulli(rng, *a, p=0.5, local=1), 73)
+    assert w.n_pages == 3
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    if kind == "bf16":
+        kt = torch.from_numpy(w.k_pages).to(torch.bfloat16)
+        vt = torch.from_numpy(w.v_pages).to(torch.bfloat16)
+        kdq, vdq, ks, vs, elem = w.k_pages, w.v_pages, 1.0, 1.0, torch.bfloat16
+    else:
+        ks, vs = 0.37, 1.9
+        kt = (torch.from_numpy(w.k_pages) / ks).to(torch.float8_e4m3fn).view(torch.uint8)
+        vt = (torch.from_numpy(w.v_pages) / vs).to(torch.float8_e4m3fn).view(torch.uint8)
+        kdq, vdq = oracle.dequant_e4m3(kt.numpy(), ks), oracle.dequant_e4m3(vt.numpy(), vs)
+        elem = torch.uint8
+    if v_layout == "dim":
+        vt = vt.transpose(2, 3).contiguous()
+    kw, vw = wide_view(kt, elem), wide_view(vt, elem)
+    if kind == "fp8":
+        kw, vw = kw.view(torch.float8_e4m3fn), vw.view(torch.float8_e4m3fn)
+    o, lse = cpa.chunked_prefill(dv["q"], kw, vw, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                                 return_lse=True, v_layout=v_layout, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    O, L = oracle.paged_attention(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
+    compare(w, o, O, f"wide {kind} {v_layout}")
+    assert np.max(np.abs(lse.cpu().numpy() - L.T)) < 2e-2
+    del kw, vw
+    torch.cuda.empty_cache()
