@@ -9,12 +9,14 @@
 //   phase 1  OR-reduce the group's G * nqb mask rows, 16 KV blocks (one 16-byte load) per
 //            thread and row, four rows' loads in flight per thread, with the causal clip
 //            kb <= prefix_blocks + qi applied per row;
-//            partial ORs of threads that share a column meet in LDS; each 16-block column
-//            becomes 16 bits of a 64-bit word in LDS.  Bit-packed masks (one bit per KV block,
-//            64 blocks per 8-byte word) are OR-reduced a word at a time instead.
-//   phase 2  popcount per word, exclusive scan over words in LDS, then each wave expands
-//            words: lane l of the wave owning word w writes 64w + l at (word offset +
-//            mbcnt rank) when bit l is set.  Positions count .. table_cap-1 get -1.
+//            partial ORs of threads that share a column meet in LDS (a tree over the row
+//            splits); each 16-block column becomes 16 bits of a 64-bit word in LDS.
+//            Bit-packed masks (one bit per KV block, 64 blocks per 8-byte word) are
+//            OR-reduced a word at a time instead.
+//   phase 2  popcount per word, exclusive scan over words (within waves, then over the wave
+//            totals), then each wave expands words: lane l of the wave owning word w writes
+//            64w + l at (word offset + mbcnt rank) when bit l is set.  Positions
+//            count .. table_cap-1 get -1.
 // The result is unique (a set in ascending order), so the kernel is bit-exact by construction.
 #include "cpa_internal.h"
 
@@ -108,10 +110,11 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
       }
       redw[tid] = acc;
       __syncthreads();
-      if (s == 0 && c < nwords) {
-        for (int k = 1; k < rs; ++k) acc |= redw[tid + (k << lgw)];
-        words[c] = acc;
+      for (int h = rs >> 1; h >= 1; h >>= 1) {   // tree OR over the row splits of a column
+        if (s < h) redw[tid] |= redw[tid + (h << lgw)];
+        __syncthreads();
       }
+      if (s == 0 && c < nwords) words[c] = redw[tid];
       __syncthreads();
     }
   }
@@ -183,13 +186,18 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
     }
     red[tid] = make_uint4(acc[0], acc[1], acc[2], acc[3]);
     __syncthreads();
-    if (s == 0 && c < nchunk) {
-      for (int k = 1; k < rsplit; ++k) {
-        const uint4 o = red[tid + (k << lg)];
-        acc[0] |= o.x; acc[1] |= o.y; acc[2] |= o.z; acc[3] |= o.w;
+    for (int h = rsplit >> 1; h >= 1; h >>= 1) {   // tree OR over the row splits of a column
+      if (s < h) {
+        const uint4 o = red[tid + (h << lg)];
+        const uint4 m = red[tid];
+        red[tid] = make_uint4(m.x | o.x, m.y | o.y, m.z | o.z, m.w | o.w);
       }
-      const uint32_t bits = bytes_to_bits(acc);
-      reinterpret_cast<unsigned short*>(words)[c] = (unsigned short)bits;  // little endian
+      __syncthreads();
+    }
+    if (s == 0 && c < nchunk) {
+      const uint4 m = red[tid];
+      const uint32_t v[4] = {m.x, m.y, m.z, m.w};
+      reinterpret_cast<unsigned short*>(words)[c] = (unsigned short)bytes_to_bits(v);  // little endian
     }
     __syncthreads();
   }
@@ -204,27 +212,39 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
     pc[k] = (w < nwords) ? __popcll(words[w]) : 0;
     mine += pc[k];
   }
-  tsum[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < UT; off <<= 1) {  // inclusive Hillis-Steele scan of per-thread sums
-    const int add = (tid >= off) ? tsum[tid - off] : 0;
-    __syncthreads();
-    tsum[tid] += add;
-    __syncthreads();
+  // exclusive scan of the per-thread sums: inclusive scan within each wave, then over the
+  // 16 wave totals in wave 0
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  int run = tsum[tid] - mine;
+  if (lane == 63) tsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int v = lane < UT / 64 ? tsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < UT / 64; off <<= 1) {
+      const int y = __shfl_up(v, off);
+      if (lane >= off) v += y;
+    }
+    if (lane < UT / 64) tsum[UT / 64 + lane] = v;   // inclusive wave prefixes
+  }
+  __syncthreads();
+  int run = (wave > 0 ? tsum[UT / 64 + wave - 1] : 0) + incl - mine;
 #pragma unroll
   for (int k = 0; k < WPT; ++k) {
     const int w = tid * WPT + k;
     if (w < nwords) wpre[w] = run;
     run += pc[k];
   }
-  const int total = tsum[UT - 1];
+  const int total = tsum[UT / 64 + UT / 64 - 1];
   __syncthreads();
 
   int32_t* tab = a.tables + ((size_t)b * a.Hkv + g) * a.table_cap;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   for (int w = wave; w < nwords; w += UT / 64) {
     const unsigned long long word = words[w];
     const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
