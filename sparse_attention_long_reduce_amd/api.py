@@ -15,15 +15,52 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 _KV_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
+def _stream(stream, dev):
+    """The HIP stream handle to launch on: `stream` (which must belong to dev) or dev's current one."""
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    if s.device != dev:
+        raise ValueError(f"the stream belongs to {s.device}, the tensors to {dev}")
     return s.cuda_stream
+
+
+def _on(dev, **tensors):
+    """Check that every given tensor (None skipped) is a CUDA tensor on dev; returns dev."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not (isinstance(t, torch.Tensor) and t.is_cuda):
+            raise TypeError(f"{name} must be a CUDA tensor")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the call's other tensors on {dev}")
+    return dev
+
+
+def _cuda_device(t, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise TypeError(f"{name} must be a CUDA tensor")
+    return t.device
 
 
 def _dev_i32(x, name):
     if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.int32 and x.is_contiguous()):
         raise TypeError(f"{name} must be a contiguous int32 CUDA tensor")
     return x
+
+
+def _out_buffers(out, lse, return_lse, q, dev):
+    """Validate caller-given o / lse (contiguous, q's shape and dtype / float32 [Tq][Hq]) or
+    allocate them."""
+    Tq, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    elif not (out.is_contiguous() and out.shape == q.shape and out.dtype == q.dtype):
+        raise ValueError("out must be a contiguous tensor of q's shape and dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev)
+    elif lse is not None and not (lse.is_contiguous() and tuple(lse.shape) == (Tq, Hq) and lse.dtype == torch.float32):
+        raise ValueError("lse must be a contiguous float32 [Tq][Hq] tensor")
+    _on(dev, out=out, lse=lse)
+    return out, lse
 
 
 def _ptr(x):
@@ -38,21 +75,24 @@ def build_block_tables(masks, prefix_blocks, chunk_blocks, Hkv, table_cap=None, 
     """
     if not (masks.is_cuda and masks.dtype == torch.uint8 and masks.is_contiguous() and masks.dim() == 4):
         raise TypeError("masks must be a contiguous 4-D uint8 CUDA tensor")
+    dev = masks.device
     B, Hq, nqb_max, nkvb_max = masks.shape
     _dev_i32(prefix_blocks, "prefix_blocks")
     _dev_i32(chunk_blocks, "chunk_blocks")
     cap = nkvb_max if table_cap is None else int(table_cap)
     if tables is None:
-        tables = torch.empty((B, Hkv, cap), dtype=torch.int32, device=masks.device)
+        tables = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
     if counts is None:
-        counts = torch.empty((B, Hkv), dtype=torch.int32, device=masks.device)
+        counts = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
     _dev_i32(tables, "tables")
     _dev_i32(counts, "counts")
     if tables.numel() != B * Hkv * cap or counts.numel() != B * Hkv:
         raise ValueError("tables/counts have the wrong size")
-    st = load().cpa_build_block_tables(_ptr(masks), B, Hq, Hkv, nqb_max, nkvb_max,
-                                       _ptr(prefix_blocks), _ptr(chunk_blocks), _ptr(tables), cap,
-                                       _ptr(counts), _stream(stream))
+    _on(dev, prefix_blocks=prefix_blocks, chunk_blocks=chunk_blocks, tables=tables, counts=counts)
+    with torch.cuda.device(dev):
+        st = load().cpa_build_block_tables(_ptr(masks), B, Hq, Hkv, nqb_max, nkvb_max,
+                                           _ptr(prefix_blocks), _ptr(chunk_blocks), _ptr(tables), cap,
+                                           _ptr(counts), _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_build_block_tables")
     return tables, counts
@@ -65,21 +105,24 @@ def build_block_tables_bits(mask_bits, nkvb_max, prefix_blocks, chunk_blocks, Hk
     if not (mask_bits.is_cuda and mask_bits.dtype in (torch.int64, torch.uint64) and mask_bits.is_contiguous()
             and mask_bits.dim() == 4):
         raise TypeError("mask_bits must be a contiguous 4-D int64 CUDA tensor")
+    dev = mask_bits.device
     B, Hq, nqb_max, words = mask_bits.shape
     _dev_i32(prefix_blocks, "prefix_blocks")
     _dev_i32(chunk_blocks, "chunk_blocks")
     cap = int(nkvb_max) if table_cap is None else int(table_cap)
     if tables is None:
-        tables = torch.empty((B, Hkv, cap), dtype=torch.int32, device=mask_bits.device)
+        tables = torch.empty((B, Hkv, cap), dtype=torch.int32, device=dev)
     if counts is None:
-        counts = torch.empty((B, Hkv), dtype=torch.int32, device=mask_bits.device)
+        counts = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
     _dev_i32(tables, "tables")
     _dev_i32(counts, "counts")
     if tables.numel() != B * Hkv * cap or counts.numel() != B * Hkv:
         raise ValueError("tables/counts have the wrong size")
-    st = load().cpa_build_block_tables_bits(_ptr(mask_bits), B, Hq, Hkv, nqb_max, int(nkvb_max), words,
-                                            _ptr(prefix_blocks), _ptr(chunk_blocks), _ptr(tables), cap,
-                                            _ptr(counts), _stream(stream))
+    _on(dev, prefix_blocks=prefix_blocks, chunk_blocks=chunk_blocks, tables=tables, counts=counts)
+    with torch.cuda.device(dev):
+        st = load().cpa_build_block_tables_bits(_ptr(mask_bits), B, Hq, Hkv, nqb_max, int(nkvb_max), words,
+                                                _ptr(prefix_blocks), _ptr(chunk_blocks), _ptr(tables), cap,
+                                                _ptr(counts), _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_build_block_tables_bits")
     return tables, counts
@@ -91,20 +134,24 @@ def build_block_plans(masks, prefix_blocks, chunk_blocks, plan_cap=None, plans=N
     direct block-sparse baseline: (plans int32 [B][Hq][nqb_max][cap], counts int32 [B][Hq][nqb_max])."""
     if not (masks.is_cuda and masks.dtype == torch.uint8 and masks.is_contiguous() and masks.dim() == 4):
         raise TypeError("masks must be a contiguous 4-D uint8 CUDA tensor")
+    dev = masks.device
     B, Hq, nqb_max, nkvb_max = masks.shape
     _dev_i32(prefix_blocks, "prefix_blocks")
     _dev_i32(chunk_blocks, "chunk_blocks")
     cap = nkvb_max if plan_cap is None else int(plan_cap)
     if plans is None:
-        plans = torch.empty((B, Hq, nqb_max, cap), dtype=torch.int32, device=masks.device)
+        plans = torch.empty((B, Hq, nqb_max, cap), dtype=torch.int32, device=dev)
     if plan_counts is None:
-        plan_counts = torch.empty((B, Hq, nqb_max), dtype=torch.int32, device=masks.device)
+        plan_counts = torch.empty((B, Hq, nqb_max), dtype=torch.int32, device=dev)
     _dev_i32(plans, "plans")
     _dev_i32(plan_counts, "plan_counts")
     if plans.numel() != B * Hq * nqb_max * cap or plan_counts.numel() != B * Hq * nqb_max:
         raise ValueError("plans/plan_counts have the wrong size")
-    st = load().cpa_build_block_plans(_ptr(masks), B, Hq, nqb_max, nkvb_max, _ptr(prefix_blocks),
-                                      _ptr(chunk_blocks), _ptr(plans), cap, _ptr(plan_counts), _stream(stream))
+    _on(dev, prefix_blocks=prefix_blocks, chunk_blocks=chunk_blocks, plans=plans, plan_counts=plan_counts)
+    with torch.cuda.device(dev):
+        st = load().cpa_build_block_plans(_ptr(masks), B, Hq, nqb_max, nkvb_max, _ptr(prefix_blocks),
+                                          _ptr(chunk_blocks), _ptr(plans), cap, _ptr(plan_counts),
+                                          _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_build_block_plans")
     return plans, plan_counts
@@ -117,6 +164,7 @@ def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu
     views allowed as in chunked_prefill); plans / plan_counts from build_block_plans."""
     if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("the direct baseline runs bf16 q, k_pages and v_pages")
+    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages)
     if q.dim() != 3 or not q.is_contiguous():
         raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
     Tq, Hq, d = q.shape
@@ -132,15 +180,14 @@ def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu
     if plans.dim() != 4 or plans.shape[0] != B or plans.shape[1] != Hq:
         raise ValueError("plans must be [B][Hq][nqb_max][cap]")
     nqb_max, cap = plans.shape[2], plans.shape[3]
-    if out is None:
-        out = torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
-    st = load().cpa_chunked_prefill_direct(
-        _ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
-        v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1],
-        _ptr(plans), cap, _ptr(plan_counts), nqb_max, _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
-        int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), _stream(stream))
+    _on(dev, page_map=page_map, plans=plans, plan_counts=plan_counts, cu_q=cu_q, prefix_len=prefix_len)
+    out, lse = _out_buffers(out, lse, return_lse, q, dev)
+    with torch.cuda.device(dev):
+        st = load().cpa_chunked_prefill_direct(
+            _ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
+            v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1],
+            _ptr(plans), cap, _ptr(plan_counts), nqb_max, _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
+            int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_chunked_prefill_direct")
     return out, lse
@@ -206,6 +253,7 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     when not given.  v_layout "dim" calls cpa_chunked_prefill_vt.  float8_e4m3fn pools with a
     bf16 q call cpa_chunked_prefill_fp8kv with the dequantization scales k_scale / v_scale.
     """
+    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages)
     fp8 = k_pages.dtype == torch.float8_e4m3fn
     if fp8:
         if q.dtype != torch.bfloat16 or v_pages.dtype != k_pages.dtype:
@@ -240,52 +288,50 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     if cu_q.numel() != B + 1 or counts.numel() != B * Hkv or page_map.dim() != 2 or page_map.shape[0] != B:
         raise ValueError("inconsistent B across cu_q / prefix_len / counts / page_map")
     cap = tables.shape[-1] if tables.numel() else 0
-    if out is None:
-        out = torch.empty_like(q)
-    if return_lse and lse is None:
-        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
-    args = (_ptr(q), _DTYPES[q.dtype], _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1),
-            k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
-            _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
-            _ptr(lse))
-    if fp8:
-        st = load().cpa_chunked_prefill_fp8kv(
-            _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
-            1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), float(k_scale),
-            float(v_scale), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
-            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse),
-            _stream(stream))
+    _on(dev, page_map=page_map, tables=tables, counts=counts, cu_q=cu_q, prefix_len=prefix_len)
+    out, lse = _out_buffers(out, lse, return_lse, q, dev)
+    with torch.cuda.device(dev):
+        hs = _stream(stream, dev)
+        args = (_ptr(q), _DTYPES[q.dtype], _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1),
+                k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
+                _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
+                _ptr(lse))
+        if fp8:
+            st = load().cpa_chunked_prefill_fp8kv(
+                _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
+                1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), float(k_scale),
+                float(v_scale), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
+                _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), hs)
+            if st != 0:
+                raise CpaError(st, "cpa_chunked_prefill_fp8kv")
+            return out, lse
+        split = bool(split_pages and split_pages > 0)
+        if split:
+            need = split_workspace_bytes(Tq, Hq, d, cap, split_pages)
+            if workspace is None:
+                workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            _on(dev, workspace=workspace)
+        if v_layout == "dim":
+            st = load().cpa_chunked_prefill_vt(
+                _ptr(q), _DTYPES[q.dtype], _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
+                _ptr(v_pages), v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map),
+                page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
+                int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq, int(split_pages) if split else 0,
+                _ptr(workspace) if split else None,
+                workspace.numel() * workspace.element_size() if split else 0, hs)
+            if st != 0:
+                raise CpaError(st, "cpa_chunked_prefill_vt")
+            return out, lse
+        if split:
+            st = load().cpa_chunked_prefill_split(*args, Tq, int(split_pages), _ptr(workspace),
+                                                  workspace.numel() * workspace.element_size(), hs)
+            if st != 0:
+                raise CpaError(st, "cpa_chunked_prefill_split")
+            return out, lse
+        st = load().cpa_chunked_prefill(*args, hs)
         if st != 0:
-            raise CpaError(st, "cpa_chunked_prefill_fp8kv")
+            raise CpaError(st, "cpa_chunked_prefill")
         return out, lse
-    split = bool(split_pages and split_pages > 0)
-    if split:
-        need = split_workspace_bytes(Tq, Hq, d, cap, split_pages)
-        if workspace is None:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-        if not workspace.is_cuda:
-            raise TypeError("workspace must be a CUDA tensor")
-    if v_layout == "dim":
-        st = load().cpa_chunked_prefill_vt(
-            _ptr(q), _DTYPES[q.dtype], _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
-            _ptr(v_pages), v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map),
-            page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
-            int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq, int(split_pages) if split else 0,
-            _ptr(workspace) if split else None,
-            workspace.numel() * workspace.element_size() if split else 0, _stream(stream))
-        if st != 0:
-            raise CpaError(st, "cpa_chunked_prefill_vt")
-        return out, lse
-    if split:
-        st = load().cpa_chunked_prefill_split(*args, Tq, int(split_pages), _ptr(workspace),
-                                              workspace.numel() * workspace.element_size(), _stream(stream))
-        if st != 0:
-            raise CpaError(st, "cpa_chunked_prefill_split")
-        return out, lse
-    st = load().cpa_chunked_prefill(*args, _stream(stream))
-    if st != 0:
-        raise CpaError(st, "cpa_chunked_prefill")
-    return out, lse
 
 
 def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len, v_layout="token",
@@ -302,6 +348,7 @@ def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_ch
             raise TypeError(f"{n} must be a contiguous [Tq][Hkv][d] CUDA tensor")
     if v_new.shape != k_new.shape:
         raise ValueError("k_new and v_new must have the same shape")
+    dev = _on(k_new.device, v_new=v_new, k_pages=k_pages, v_pages=v_pages)
     Tq, Hkv, d = k_new.shape
     if k_pages.dim() != 4 or tuple(k_pages.shape[1:]) != (Hkv, BLOCK, d) or k_pages.stride(3) != 1:
         raise ValueError("k_pages must be [n_pages][Hkv][64][d] with d contiguous")
@@ -319,11 +366,13 @@ def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_ch
     B = prefix_len.numel()
     if cu_q.numel() != B + 1 or page_map.dim() != 2 or page_map.shape[0] != B:
         raise ValueError("inconsistent B across cu_q / prefix_len / page_map")
-    st = load().cpa_append_kv(_ptr(k_new), _ptr(v_new), _KV_DTYPES[k_new.dtype], _ptr(k_pages), k_pages.stride(0),
-                              k_pages.stride(1), k_pages.stride(2), _ptr(v_pages), 1 if v_layout == "dim" else 0,
-                              v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), k_pages.shape[0],
-                              _ptr(page_map), page_map.shape[1], _ptr(cu_q), _ptr(prefix_len), B, Hkv, d,
-                              int(max_chunk_len), _stream(stream))
+    _on(dev, page_map=page_map, cu_q=cu_q, prefix_len=prefix_len)
+    with torch.cuda.device(dev):
+        st = load().cpa_append_kv(_ptr(k_new), _ptr(v_new), _KV_DTYPES[k_new.dtype], _ptr(k_pages),
+                                  k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
+                                  1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1),
+                                  v_pages.stride(2), k_pages.shape[0], _ptr(page_map), page_map.shape[1], _ptr(cu_q),
+                                  _ptr(prefix_len), B, Hkv, d, int(max_chunk_len), _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_append_kv")
 
