@@ -17,6 +17,11 @@
  *     synchronising.  Results are visible in stream order.
  *   - Block size: query blocks, KV blocks and KV pages all hold CPA_BLOCK = 64 tokens.
  *   - GQA grouping: query head h belongs to KV group h / (Hq / Hkv).
+ *   - Size limits (CPA_ERR_SHAPE beyond them): strides at most 2^40 elements, at most 65536
+ *     query heads, B * Hkv at most INT_MAX, and at most INT_MAX workgroups per launch (KV
+ *     groups x query tiles x split ranges for the prefill; sequences x chunk pages x KV groups
+ *     for the append).  Far beyond any pool that fits in memory, they keep every size product
+ *     the checks and the kernels form from overflowing.
  *   - Host-side argument checks run before any HIP call; on failure nothing is enqueued and a
  *     CPA_ERR_* code is returned.  Device-resident data (lengths, tables, page ids) cannot be
  *     checked on the host: the kernels clamp every index they derive from it so that no access

@@ -2,6 +2,7 @@
 #include "../../include/cpa.h"
 #include "cpa_internal.h"
 
+#include <climits>
 #include <cmath>
 
 namespace {
@@ -20,6 +21,19 @@ struct VLayout {
   bool dmajor;
 };
 
+// Largest stride (elements) and head count the entry points take: far beyond any pool that fits
+// in memory, and small enough that no size product the checks or the kernels form overflows.
+constexpr int64_t kMaxStride = (int64_t)1 << 40;
+constexpr int kMaxHeads = 65536;
+
+// Workgroups of a prefill launch with n_splits ranges per tile, as the kernels' grid computes
+// it, in 64 bits (the launch takes at most INT_MAX).
+int64_t prefill_workgroups(const cpa::PrefillArgs& a, int64_t n_splits) {
+  const int64_t groups = a.n_groups;
+  const int64_t slots = a.xcd_remap ? 8 * ((groups + 7) / 8) : groups;
+  return slots * a.tiles_per_group * n_splits;
+}
+
 // Checks the arguments of a prefill call and fills the launch arguments (no HIP call).
 // *nothing: the call has no work (B == 0 or max_chunk_len == 0).
 cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
@@ -33,7 +47,7 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   *nothing = false;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || table_cap < 0 || n_pages < 0)
     return CPA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq > kMaxHeads) return CPA_ERR_SHAPE;
   if (!(sm_scale >= 0.f) || std::isinf(sm_scale)) return CPA_ERR_SHAPE;
   if (dtype != CPA_F32 && dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
@@ -44,6 +58,9 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
     return CPA_OK;
   }
   if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  if (token_stride > kMaxStride || head_stride > kMaxStride || page_stride > kMaxStride ||
+      vl.row_stride > kMaxStride || vl.head_stride > kMaxStride || vl.page_stride > kMaxStride)
+    return CPA_ERR_SHAPE;
   if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
     return CPA_ERR_SHAPE;
   const int64_t v_rows = vl.dmajor ? d : 64, v_row_len = vl.dmajor ? 64 : d;
@@ -78,9 +95,11 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   const int nqb_max = (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK;
   a.n_qtiles = (nqb_max + a.qpw - 1) / a.qpw;
   a.tiles_per_group = a.n_qtiles * a.hsplit;
+  if ((int64_t)B * Hkv > INT_MAX) return CPA_ERR_SHAPE;
   a.n_groups = B * Hkv;
   a.xcd_remap = a.n_groups >= 8 ? 1 : 0;
   a.n_splits = 1;
+  if (prefill_workgroups(a, 1) > INT_MAX) return CPA_ERR_SHAPE;
   return CPA_OK;
 }
 
@@ -108,7 +127,7 @@ cpa_status cpa_build_block_tables(const uint8_t* masks, int B, int Hq, int Hkv, 
                                   const int32_t* chunk_blocks, int32_t* tables, int table_cap,
                                   int32_t* counts, hipStream_t stream) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || nqb_max < 0 || nkvb_max < 0 || table_cap < 0) return CPA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq > kMaxHeads || (int64_t)B * Hkv > INT_MAX) return CPA_ERR_SHAPE;
   if (nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
   if (table_cap < nkvb_max) return CPA_ERR_CAPACITY;
   if (B == 0) return CPA_OK;
@@ -126,7 +145,7 @@ cpa_status cpa_build_block_tables_bits(const uint64_t* mask_bits, int B, int Hq,
                                        int32_t* counts, hipStream_t stream) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || nqb_max < 0 || nkvb_max < 0 || table_cap < 0 || mask_words < 0)
     return CPA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq > kMaxHeads || (int64_t)B * Hkv > INT_MAX) return CPA_ERR_SHAPE;
   if (nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
   if (mask_words < (nkvb_max + 63) / 64) return CPA_ERR_SHAPE;
   if (table_cap < nkvb_max) return CPA_ERR_CAPACITY;
@@ -164,12 +183,16 @@ cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, 
                          int64_t n_pages, const int32_t* page_map, int page_map_stride, const int32_t* cu_q,
                          const int32_t* prefix_len, int B, int Hkv, int d, int max_chunk_len,
                          hipStream_t stream) {
-  if (B < 0 || Hkv <= 0 || max_chunk_len < 0 || n_pages < 0) return CPA_ERR_SHAPE;
+  if (B < 0 || Hkv <= 0 || Hkv > kMaxHeads || max_chunk_len < 0 || n_pages < 0) return CPA_ERR_SHAPE;
   if (dtype != CPA_F32 && dtype != CPA_BF16 && dtype != CPA_FP8_E4M3) return CPA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
   if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
   if (B == 0 || max_chunk_len == 0) return CPA_OK;
   if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  if (token_stride > kMaxStride || head_stride > kMaxStride || page_stride > kMaxStride ||
+      v_row_stride > kMaxStride || v_head_stride > kMaxStride || v_page_stride > kMaxStride)
+    return CPA_ERR_SHAPE;
+  if ((int64_t)B * ((max_chunk_len + 63) / 64) * Hkv > INT_MAX) return CPA_ERR_SHAPE;   // workgroups
   if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
     return CPA_ERR_SHAPE;
   const int64_t v_rows = v_dim_major ? d : 64, v_row_len = v_dim_major ? 64 : d;
@@ -242,13 +265,16 @@ cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void
                                       hipStream_t stream) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || plan_cap < 0 || n_pages < 0 || nqb_max < 0)
     return CPA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return CPA_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Hq > kMaxHeads || (int64_t)B * Hkv > INT_MAX) return CPA_ERR_SHAPE;
   if (!(sm_scale >= 0.f) || std::isinf(sm_scale)) return CPA_ERR_SHAPE;
   if (dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
   if (nqb_max < (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK) return CPA_ERR_SHAPE;
   if (B == 0 || max_chunk_len == 0) return CPA_OK;
   if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  if (token_stride > kMaxStride || head_stride > kMaxStride || page_stride > kMaxStride ||
+      v_dim_stride > kMaxStride || v_head_stride > kMaxStride || v_page_stride > kMaxStride)
+    return CPA_ERR_SHAPE;
   if (token_stride < d || head_stride < 64 * token_stride || page_stride < (int64_t)Hkv * head_stride)
     return CPA_ERR_SHAPE;
   if (v_dim_stride < 64 || v_head_stride < (int64_t)d * v_dim_stride || v_page_stride < (int64_t)Hkv * v_head_stride)
@@ -298,7 +324,7 @@ cpa_status prefill_split(const void* q, cpa_dtype dtype, const void* k_pages, co
                                         n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
                                         prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
   if (st != CPA_OK || nothing) return st;
-  const int n_splits = (table_cap + split_pages - 1) / split_pages;
+  const int64_t n_splits = ((int64_t)table_cap + split_pages - 1) / split_pages;
   if (n_splits <= 1)   // one range: the plain path
     return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
   if (dtype != CPA_BF16 || token_stride > (1 << 24) || vl.row_stride > (1 << 24)) return CPA_ERR_UNSUPPORTED;
@@ -307,13 +333,14 @@ cpa_status prefill_split(const void* q, cpa_dtype dtype, const void* k_pages, co
   if (workspace == nullptr) return CPA_ERR_NULL;
   if (!aligned16(workspace)) return CPA_ERR_ALIGN;
   if (workspace_bytes < need) return CPA_ERR_CAPACITY;
-  a.n_splits = n_splits;
+  if (prefill_workgroups(a, n_splits) > INT_MAX) return CPA_ERR_SHAPE;
+  a.n_splits = (int)n_splits;
   a.split_pages = split_pages;
   a.total_q = total_q;
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = a.part_o + (size_t)n_splits * total_q * Hq * d;
   if (cpa::launch_prefill(a, true, d, stream) != hipSuccess) return CPA_ERR_LAUNCH;
-  cpa::MergeArgs m{a.part_o, a.part_lse, n_splits, total_q, Hq, o, lse};
+  cpa::MergeArgs m{a.part_o, a.part_lse, a.n_splits, total_q, Hq, o, lse};
   return cpa::launch_split_merge(m, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 }  // namespace

@@ -309,3 +309,17 @@ def test_plan_flops_matches_oracle_visible_counts():
                 for kb in P[b, h, qi, :C[b, h, qi]].tolist():
                     pairs += sum(1 for t in range(64 * kb, 64 * kb + 64) if t <= int(w.prefix_len[b]) + r)
     assert cpa.plan_flops(P, C, w.prefix_len, w.chunk_len, w.d) == 4 * w.d * pairs
+
+
+def test_size_caps(lib):
+    # strides past 2^40 elements, more than 65536 heads, or a grid past INT_MAX workgroups are
+    # refused on the host: no size product the checks or the kernels form can overflow
+    big = (1 << 40) + 64
+    assert pf(lib, ts=big, hs=64 * big, ps=8 * 64 * big) == 2
+    assert pf(lib, Hq=4 * 32768, Hkv=32768) == 2
+    assert pf(lib, B=1 << 29) == 2                      # B * Hkv = 2^32 KV groups
+    assert pf(lib, B=1 << 26, mcl=1 << 20) == 2         # 2^29 groups x 4096 query tiles
+    assert pfs(lib, B=1 << 20, mcl=1 << 12) == 2        # 2^23 groups x 64 tiles fit; x 4 ranges do not
+    assert ap(lib, ts=big, hs=64 * big, ps=8 * 64 * big) == 2
+    assert ap(lib, Hkv=65537) == 2
+    assert ap(lib, B=1 << 20, mcl=1 << 20) == 2         # 2^20 sequences x 2^14 chunk pages x 8 groups
