@@ -26,7 +26,9 @@
  *     CPA_ERR_* code is returned.  Device-resident data (lengths, tables, page ids) cannot be
  *     checked on the host: the kernels clamp every index they derive from it so that no access
  *     leaves the buffers described here, and the per-call notes say what such data must satisfy
- *     for the result to be meaningful.
+ *     for the result to be meaningful.  The exception is the row offsets cu_q, which address q,
+ *     o and the new K/V rows, buffers whose extent the library is not told: cu_q must be
+ *     non-decreasing with cu_q[B] equal to the buffers' row count Tq.
  */
 #ifndef CPA_H
 #define CPA_H
@@ -125,9 +127,10 @@ cpa_status cpa_build_block_tables_bits(const uint64_t* mask_bits, int B, int Hq,
  *   page_map int32 [B][page_map_stride]: logical KV block -> physical page.
  *   tables, counts, table_cap  as produced by cpa_build_block_tables (ids ascending; counts are
  *            clamped to table_cap).
- *   cu_q     int32 [B+1], prefix_len int32 [B]: device arrays; prefix_len[b] must be a multiple
- *            of 64 (it is the absolute position of the chunk's first row) and the chunk's own K/V
- *            must already be in the cache.  Chunk lengths are clamped to max_chunk_len.
+ *   cu_q     int32 [B+1], prefix_len int32 [B]: device arrays; cu_q non-decreasing from 0 to
+ *            Tq; prefix_len[b] must be a multiple of 64 (it is the absolute position of the
+ *            chunk's first row) and the chunk's own K/V must already be in the cache.  Chunk
+ *            lengths are clamped to max_chunk_len.
  *   max_chunk_len  host int >= every chunk length (sizes the grid).
  *   sm_scale softmax scale, > 0; pass 0 for 1/sqrt(d).
  *   o  (out) [Tq][Hq][d] in `dtype`.  A row with no visible key gets zeros.
