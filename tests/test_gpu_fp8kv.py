@@ -172,3 +172,21 @@ def test_out_of_range_page_id_reads_as_nan(kv):
     assert np.all(np.isnan(on[seeing][:, 4:8])) and not np.any(np.isnan(on[~seeing][:, 4:8]))
     O, _ = oracle.paged_attention(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
     compare(w, o[:, :4], O[:, :4], f"{kv}: group 0 unaffected")
+
+
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_fp8kv_d64_past_the_id_window(v_layout):
+    # d = 64 with tables of ~640 pages: the fp8 pipeline copies one page further ahead, so its
+    # page-id window is refilled at another iteration than the bf16 one; every row checked
+    print(f"\n[case] fp8 kv d64 long {v_layout}", flush=True)
+    w = make_workload("long64", [40960], [192], 8, 2, 64, "bf16", bern(0.9), 63)
+    kc, vc, kdq, vdq = fp8_setup(w)
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    assert int(C.min()) > 600
+    o, lse = run(dv, w, tables, counts, kc, vc, v_layout)
+    torch.cuda.synchronize()
+    O, L = oracle.paged_attention(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
+    compare(w, o, O, f"fp8 d64 long {v_layout}")
+    assert np.max(np.abs(lse.cpu().numpy() - L.T)) < 2 ** -7
