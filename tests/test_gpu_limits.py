@@ -69,12 +69,12 @@ def test_large_groups(Hq, Hkv, d):
     T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
     assert np.array_equal(tables.cpu().numpy(), T)
     O, L = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
-    for v_layout in ("token", "dim"):
+    for v_layout, split in (("token", 0), ("dim", 0), ("token", 4), ("dim", 4)):
         vp = dv["vp"].transpose(2, 3).contiguous() if v_layout == "dim" else dv["vp"]
         o, lse = cpa.chunked_prefill(dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"],
-                                     w.max_chunk_len, return_lse=True, v_layout=v_layout)
+                                     w.max_chunk_len, return_lse=True, v_layout=v_layout, split_pages=split)
         torch.cuda.synchronize()
-        compare(w, o, O, f"G={Hq // Hkv} {v_layout}")
+        compare(w, o, O, f"G={Hq // Hkv} {v_layout} split {split}")
         assert np.max(np.abs(lse.cpu().numpy() - L.T)) < 2 ** -7
 
 
