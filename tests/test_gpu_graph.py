@@ -20,12 +20,21 @@ def bern(p, local=1):
     return lambda rng, *a: mask_bernoulli(rng, *a, p=p, local=local)
 
 
-@pytest.mark.parametrize("mode", ["plain", "split", "dim", "bits"])
+@pytest.mark.parametrize("mode", ["plain", "split", "dim", "bits", "fp8_token", "fp8_dim"])
 def test_capture_and_replay(mode):
     w = make_workload("graph", [0, 192, 4096], [37, 130, 255], 8, 2, 128, "bf16", bern(0.05), 81)
     dv = upload(w)
-    vp = dv["vp"].transpose(2, 3).contiguous() if mode == "dim" else dv["vp"]
-    layout = "dim" if mode == "dim" else "token"
+    kp = dv["kp"]
+    vp = dv["vp"]
+    if mode.startswith("fp8"):   # e4m3 copies of the pools, scale 1/4
+        kp = (kp.float() * 4).to(torch.float8_e4m3fn)
+        vp = (vp.float() * 4).to(torch.float8_e4m3fn)
+    layout = "dim" if mode in ("dim", "fp8_dim") else "token"
+    if layout == "dim" and mode.startswith("fp8"):
+        vp = vp.view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn)
+    elif layout == "dim":
+        vp = vp.transpose(2, 3).contiguous()
+    scale = 0.25 if mode.startswith("fp8") else 1.0
     sp = 2 if mode == "split" else 0
     bits = torch.from_numpy(pack_mask_bits(w.masks).view(np.int64)).cuda()
     tables = torch.empty((w.B, w.Hkv, w.nkvb_max), dtype=torch.int32, device="cuda")
@@ -40,8 +49,9 @@ def test_capture_and_replay(mode):
             cpa.build_block_tables_bits(bits, w.nkvb_max, dv["pb"], dv["cb"], w.Hkv, tables=tables, counts=counts)
         else:
             cpa.build_block_tables(dv["masks"], dv["pb"], dv["cb"], w.Hkv, tables=tables, counts=counts)
-        cpa.chunked_prefill(dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
-                            out=out, lse=lse, split_pages=sp, workspace=ws if sp else None, v_layout=layout)
+        cpa.chunked_prefill(dv["q"], kp, vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                            out=out, lse=lse, split_pages=sp, workspace=ws if sp else None, v_layout=layout,
+                            k_scale=scale, v_scale=scale)
 
     step()
     torch.cuda.synchronize()
