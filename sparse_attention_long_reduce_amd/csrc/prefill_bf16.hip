@@ -230,7 +230,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 
   // ---- direct-to-LDS plan ------------------------------------------------------------------
   // waves 0-3 move K, waves 4-7 move V; wave w's instruction j fills the 1 KiB slab
-  // s = 4w' + j of its tensor (w' = w % 4), lane l the 16-byte slot l of that slab.
+  // s = NPW w' + j of its tensor's tile (w' = w % 4), lane l the 16-byte slot l of that slab.
   const bool vrole = wave >= 4;
   const char* const tg = vrole ? vg : kg;  // this wave's tensor of group g
   const int64_t pstride = (vrole ? a.v_page_stride : a.page_stride) * EB;   // bytes
@@ -380,8 +380,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   // QK: S^T = K Q^T for half h of the page in LDS tile Kl; copy instructions j0 .. j0+NJ-1 of f
   // go out in between
   constexpr int NJ = NPW / 2 > 0 ? NPW / 2 : 1;   // copy instructions per unit
-  // F8: staging slot t of a page (src, codes) to slots t % 32 and t % 32 + 32 of bf16 slab t / 32
-  // (dst)
+  // F8: converts staging slot t of a page (codes at src) into slots t % 32 and t % 32 + 32 of
+  // slab t / 32 of the bf16 tile dst
   constexpr int NS = GE::PAGE / 16;   // staging slots of one tensor's page
   auto convert_slot = [&](const __bf16* src, __bf16* dst, int t) __attribute__((always_inline)) {
     const uint4 c = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(src) + 16 * t);
@@ -403,7 +403,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
         16 * (t * C8 + (c ^ swz_f8<D>(t))) + 8 * (s16 & 1);
     const v2i32 codes = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)lp);
     const int col = 16 * c + s16;
-    __bf16* d = dst + ((2 * (m >> 2) + ((m >> 1) & 1)) * GE::DT + (col >> 5)) * 512 + (32 * (m & 1) + (col & 31)) * 8;
+    const int slab = (2 * (m >> 2) + ((m >> 1) & 1)) * GE::DT + (col >> 5);
+    __bf16* d = dst + slab * 512 + (32 * (m & 1) + (col & 31)) * 8;
     *reinterpret_cast<uint4*>(d) = fp8x8_to_bf16(make_uint2((uint32_t)codes[0], (uint32_t)codes[1]));
   };
   // F8: V lane items per page: NS staging slots (dim-major pool) or 2 NS transposed reads
