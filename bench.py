@@ -56,6 +56,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def hardware_info(dev):
+    """The device the line was measured on, and the host CPU the oracle ran on."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    info = {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1)}
+    clock = getattr(p, "clock_rate", None)
+    if clock:
+        info["max_engine_clock_mhz"] = round(clock / 1000)
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["host_cpu"] = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return info
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in ("prefill_bf16.hip", "prefill_common.h", "cpa_internal.h"):
@@ -583,6 +600,7 @@ def main():
         result["split_kv"] = {"split_pages": batches[0].split_pages,
                               "unsplit_prefill_ms": round(unsplit["prefill_ms"], 4),
                               "speedup_over_unsplit": round(unsplit["prefill_ms"] / r["prefill_ms"], 4)}
+    result["hardware"] = hardware_info(torch.device("cuda", 0))
     result["pages_context"] = ("CompactAttention reports up to 2.72x attention speedup at 128K on "
                                "LLaMA-3.1-8B-Instruct (hardware not stated); context only")
     if not args.no_cpu_baseline:
