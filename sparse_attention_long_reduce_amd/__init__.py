@@ -7,7 +7,8 @@ Thin wrappers over the C ABI in include/cpa.h:
   bit-packed masks (one bit per block)
 * chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len,
                   max_chunk_len, split_pages=0, v_layout="token") -> (o, lse)
-  (split_pages > 0: split-KV over page ranges with an LSE merge; plan_split_pages picks one;
+  (split_pages > 0: split-KV over page ranges with an LSE merge; plan_split_pages picks one,
+  split_pages="auto" applies it for the device;
   v_layout "dim": V pages stored [page][group][d][64])
 * build_block_plans(masks, prefix_blocks, chunk_blocks) and chunked_prefill_direct(...): the
   direct block-sparse baseline, every (head, query block) over its own mask row

@@ -66,3 +66,9 @@ def test_caller_outputs_are_checked():
     o2, lse2 = cpa.chunked_prefill(q, kp, vp, pm, t, c, cu, pl, 64, out=o, lse=lse)
     torch.cuda.synchronize()
     assert o2 is o and lse2 is lse
+
+
+def test_split_pages_takes_int_or_auto():
+    q, kp, vp, pm, t, c, cu, pl = _cpu_args()
+    with pytest.raises(ValueError, match="auto"):
+        cpa.chunked_prefill(q, kp, vp, pm, t, c, cu, pl, 64, split_pages="fastest")

@@ -140,3 +140,38 @@ def test_split_full_size(name):
     heads = torch.from_numpy(S[:, 1]).cuda()
     compare(w, o[rows, heads].float().cpu().numpy(), Os, f"{name} split {sp}")
     assert np.max(np.abs(lse[rows, heads].cpu().numpy() - Ls)) < 2e-2
+
+
+@pytest.mark.parametrize("name", ["g4_d64", "g4_ragged_multi"])
+def test_auto_split(name):
+    # split_pages="auto" runs the range length plan_split_pages gives for this device: the same
+    # launch, bit for bit, as passing that length; fp8 and fp32 pools (no split-KV form) run unsplit
+    print(f"\n[case] auto split {name}", flush=True)
+    w = make_small(name)
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sp = cpa.plan_split_pages(w.B, w.Hq, w.Hkv, w.max_chunk_len, tables.shape[-1], n_cus)
+    assert sp > 0   # a few tiles on a full GPU: the plan splits
+    o1, l1 = split_prefill(dv, w, tables, counts, "auto")
+    o2, l2 = split_prefill(dv, w, tables, counts, sp)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    O, L = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
+    compare(w, o1, O, f"{name} auto split")
+    kq = (dv["kp"].float() / 0.5).to(torch.float8_e4m3fn)
+    vq = (dv["vp"].float() / 0.5).to(torch.float8_e4m3fn)
+    f1 = cpa.chunked_prefill(dv["q"], kq, vq, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                             return_lse=True, split_pages="auto", k_scale=0.5, v_scale=0.5)
+    f2 = cpa.chunked_prefill(dv["q"], kq, vq, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                             return_lse=True, k_scale=0.5, v_scale=0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(f1[0], f2[0]) and torch.equal(f1[1], f2[1])
+    q32, k32, v32 = dv["q"].float(), dv["kp"].float(), dv["vp"].float()
+    g1 = cpa.chunked_prefill(q32, k32, v32, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                             return_lse=True, split_pages="auto")
+    g2 = cpa.chunked_prefill(q32, k32, v32, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
