@@ -393,9 +393,12 @@ def time_build_bits(cpa, batches, steps):
                          "frac": round(gbs / HBM_PEAK_GBS, 5), "algorithmic_bytes": nbytes + tbytes}}
 
 
-def time_append(cpa, bt, steps):
-    """HIP-event time of cpa_append_kv writing the batch's chunk rows (taken from the pool itself,
-    so the pool's contents do not change) into the pool in the bench's V layout."""
+def time_append(cpa, bt, steps, reps=20):
+    """Time of cpa_append_kv writing the batch's chunk rows (taken from the pool itself, so the
+    pool's contents do not change) into the pool in the bench's V layout.  `us` is the GPU time of
+    one call: HIP events around replays of a captured graph of `reps` calls back to back, so the
+    host's per-call overhead (the binding's checks) is not in it; `us_eager_call` is the event time
+    of one eager call, which includes that overhead whenever the host is slower than the kernel."""
     import numpy as np
     import torch
     w = bt.w
@@ -411,17 +414,32 @@ def time_append(cpa, bt, steps):
     def run():
         cpa.append_kv(k_rows, v_rows, bt.kp, vpool, bt.pm, bt.cu, bt.pl, w.max_chunk_len, v_layout=bt.v_layout)
 
+    def event_times(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
     for _ in range(3):
         run()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for e0, e1 in ev:
-        e0.record()
-        run()
-        e1.record()
     torch.cuda.synchronize()
-    us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+    eager_us = event_times(run, steps)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side), torch.cuda.graph(graph, stream=side):
+        for _ in range(reps):
+            run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    us = event_times(graph.replay, steps) / reps
+    del graph
     nbytes = 2 * 2 * k_rows.numel() * k_rows.element_size()   # K and V, read once and written once
-    return {"us": round(us, 2), "rows": int(k_rows.shape[0]),
+    return {"us": round(us, 2), "us_eager_call": round(eager_us, 2), "rows": int(k_rows.shape[0]),
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes": nbytes}}

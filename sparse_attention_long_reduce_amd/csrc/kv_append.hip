@@ -26,11 +26,14 @@ template <int EB, int D>   // element bytes, head dim
 __global__ __launch_bounds__(AT) void kv_append_kernel(const AppendArgs a) {
   constexpr int EPC = 16 / EB;     // elements per 16-byte chunk
   constexpr int CPR = D / EPC;     // chunks per token row
-  constexpr int LS = D + EPC;      // LDS row stride (elements), +16 bytes against bank conflicts
+  // LDS tile [64][D], 16-byte chunk c of row r at chunk slot c ^ ((r / EPC) % CPR): the second
+  // pass reads one column at rows EPC apart across lanes, which then fall in distinct banks
+  static_assert((CPR & (CPR - 1)) == 0, "the swizzle stays within a row");
+  auto sw = [](int r) { return (r / EPC) % CPR; };
   typedef uint4 chunk_t;
   typedef typename std::conditional<EB == 1, uint8_t,
                                     typename std::conditional<EB == 2, uint16_t, uint32_t>::type>::type E;
-  __shared__ __attribute__((aligned(16))) unsigned char tile_raw[64 * LS * EB];
+  __shared__ __attribute__((aligned(16))) unsigned char tile_raw[64 * D * EB];
 
   const int n_cp = a.max_chunk_len > 0 ? (a.max_chunk_len + 63) / 64 : 0;
   const int wg = blockIdx.x;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(AT) void kv_append_kernel(const AppendArgs a) {
     if (!a.v_dmajor) {
       *reinterpret_cast<chunk_t*>(vdst + ((size_t)slot * a.v_row_stride + c * EPC) * EB) = vv;
     } else {
-      *reinterpret_cast<chunk_t*>(tile_raw + ((size_t)r * LS + c * EPC) * EB) = vv;
+      *reinterpret_cast<chunk_t*>(tile_raw + ((size_t)r * D + (c ^ sw(r)) * EPC) * EB) = vv;
     }
   }
   if (!a.v_dmajor) return;
@@ -78,14 +81,15 @@ __global__ __launch_bounds__(AT) void kv_append_kernel(const AppendArgs a) {
     const int x = i / SPR, s0 = (i % SPR) * EPC;
     if (s0 >= nv) continue;
     unsigned char* row = reinterpret_cast<unsigned char*>(vdst) + ((size_t)x * a.v_row_stride + s0) * EB;
-    const E* col = reinterpret_cast<const E*>(tile_raw) + x;
+    // element x of row t: chunk slot (x / EPC) ^ sw(t), element x % EPC
+    auto at = [&](int t) { return reinterpret_cast<const E*>(tile_raw)[t * D + (((x / EPC) ^ sw(t)) * EPC) + x % EPC]; };
     if (s0 + EPC <= nv) {
       E buf[EPC];
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) buf[e] = col[(size_t)(s0 + e) * LS];
+      for (int e = 0; e < EPC; ++e) buf[e] = at(s0 + e);
       *reinterpret_cast<chunk_t*>(row) = __builtin_bit_cast(chunk_t, buf);
     } else {   // the chunk's last, partial page: only the slots it owns
-      for (int e = 0; s0 + e < nv; ++e) reinterpret_cast<E*>(row)[e] = col[(size_t)(s0 + e) * LS];
+      for (int e = 0; s0 + e < nv; ++e) reinterpret_cast<E*>(row)[e] = at(s0 + e);
     }
   }
 }
