@@ -6,10 +6,12 @@ every selected KV block, attention over the selected blocks read in place), plus
 attention (torch SDPA, closed forms, the log-sum-exp merge identity) and brute-force loops.
 """
 import math
+from types import SimpleNamespace
 
 import numpy as np
 import pytest
 import torch
+from hypothesis import given, settings, strategies as st
 
 import oracle
 from workloads import BLOCK, make_workload, make_config
@@ -79,6 +81,35 @@ def test_tables_equal_loop_definition(seed, G, noise, values):
     T, C = tables_of(w, cap=w.nkvb_max + 3)
     ref = loop_tables(w)
     for (b, g), sel in ref.items():
+        assert C[b, g] == len(sel)
+        assert list(T[b, g, :C[b, g]]) == sel
+        assert np.all(T[b, g, C[b, g]:] == -1)
+
+
+@st.composite
+def raw_mask_inputs(draw):
+    """Byte masks drawn directly, with nonzero entries anywhere: past the causal limit, in padding
+    rows past a sequence's query blocks and in padding columns past its KV extent."""
+    B = draw(st.integers(1, 3))
+    G, Hkv = draw(st.sampled_from([1, 2, 3, 4])), draw(st.integers(1, 3))
+    nqb_max = draw(st.integers(1, 5))
+    cb = [draw(st.integers(0, nqb_max)) for _ in range(B)]
+    pb = [draw(st.integers(0, 6)) for _ in range(B)]
+    nkvb_max = max(1, max(p + c for p, c in zip(pb, cb)) + draw(st.integers(0, 3)))
+    density = draw(st.floats(0.0, 1.0))
+    rng = np.random.default_rng(draw(st.integers(0, 2 ** 31 - 1)))
+    shape = (B, G * Hkv, nqb_max, nkvb_max)
+    masks = np.where(rng.random(shape) < density, rng.integers(1, 256, size=shape), 0).astype(np.uint8)
+    return SimpleNamespace(masks=masks, prefix_blocks=np.array(pb, np.int32), chunk_blocks=np.array(cb, np.int32),
+                           Hkv=Hkv)
+
+
+@settings(max_examples=200, deadline=None)
+@given(raw_mask_inputs())
+def test_tables_equal_loop_definition_on_drawn_masks(w):
+    nkvb_max = w.masks.shape[3]
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, nkvb_max)
+    for (b, g), sel in loop_tables(w).items():
         assert C[b, g] == len(sel)
         assert list(T[b, g, :C[b, g]]) == sel
         assert np.all(T[b, g, C[b, g]:] == -1)
@@ -498,6 +529,20 @@ def test_block_plans_equal_loop_definition(seed, noise):
                             expect.append(kb)
                 assert counts[b, h, qi] == len(expect)
                 assert plans[b, h, qi].tolist() == expect + [-1] * (w.nkvb_max + 3 - len(expect))
+
+
+@settings(max_examples=200, deadline=None)
+@given(raw_mask_inputs())
+def test_block_plans_equal_loop_definition_on_drawn_masks(w):
+    B, Hq, nqb_max, nkvb_max = w.masks.shape
+    plans, counts = oracle.block_plans(w.masks, w.prefix_blocks, w.chunk_blocks, nkvb_max)
+    for b in range(B):
+        for h in range(Hq):
+            for qi in range(nqb_max):
+                expect = [kb for kb in range(nkvb_max) if qi < w.chunk_blocks[b] and w.masks[b, h, qi, kb] != 0
+                          and kb <= w.prefix_blocks[b] + qi]
+                assert counts[b, h, qi] == len(expect)
+                assert plans[b, h, qi].tolist() == expect + [-1] * (nkvb_max - len(expect))
 
 
 def test_block_plans_one_head_one_block_is_the_union_table():
