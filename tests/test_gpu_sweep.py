@@ -11,6 +11,8 @@ not.  It then runs the path as a caller would, against the oracle at every step:
   attend   over the appended pools: the bars of the hand-picked cases, LSE included;
   direct   (bf16 cases) the per-head baseline's plans bit-exact and its output within the bars.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -25,7 +27,7 @@ from _gpu import compare, upload
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-N_CASES = 32
+N_CASES = int(os.environ.get("CPA_SWEEP_CASES", "32"))   # more for a longer soak of the same draw
 
 
 def draw(i):
