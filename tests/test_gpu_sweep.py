@@ -22,7 +22,7 @@ import sparse_attention_long_reduce_amd as cpa
 from workloads import make_workload
 from workloads.configs import mask_all, mask_bernoulli, pack_mask_bits
 
-from _gpu import compare, upload
+from _gpu import compare, sample_rows, upload
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -134,3 +134,43 @@ def test_sweep(i):
         Od, Ld = oracle.block_sparse_attention(w.q, Ko, Vo, w.page_map, Pn, Cn, w.cu_q, w.prefix_len, Hkv)
         compare(w, od, Od, f"sweep {i} direct")
         check_lse(ld, Ld, 2 ** -7)
+
+
+N_LONG = 12
+
+
+def draw_long(i):
+    rng = np.random.default_rng(7500 + i)
+    B = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 2, 4, 8, 12, 16]))
+    mode = str(rng.choice(["bf16", "bf16", "f32"]))
+    return dict(prefix=(64 * rng.integers(1000, 1601, size=B)).tolist(), chunk=rng.integers(1, 601, size=B).tolist(),
+                G=G, Hkv=int(rng.integers(1, 3)), d=int(rng.choice([64, 128])),
+                p=float(rng.choice([0.05, 0.5, 1.0])), local=int(rng.integers(0, 3)), mode=mode,
+                v_layout=str(rng.choice(["token", "dim"])),
+                split=int(rng.choice([0, 64, 256])) if mode == "bf16" else 0)
+
+
+@pytest.mark.parametrize("i", range(N_LONG))
+def test_sweep_long(i):
+    # contexts of 64K-102K tokens: tables of hundreds to 1600 pages, most past the kernel's window
+    # of 1024 resolved page ids; tables in full, attention on sampled rows
+    c = draw_long(i)
+    print(f"\n[case] long sweep {i}: {c}", flush=True)
+    Hq, Hkv = c["G"] * c["Hkv"], c["Hkv"]
+    w = make_workload(f"long{i}", c["prefix"], c["chunk"], Hq, Hkv, c["d"], c["mode"], mask_fn(c), 7600 + i)
+    dv = upload(w)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, Hkv, w.nkvb_max)
+    tables, counts = cpa.build_block_tables(dv["masks"], dv["pb"], dv["cb"], Hkv)
+    assert np.array_equal(tables.cpu().numpy(), T) and np.array_equal(counts.cpu().numpy(), C)
+    vp = dv["vp"].transpose(2, 3).contiguous() if c["v_layout"] == "dim" else dv["vp"]
+    o, lse = cpa.chunked_prefill(dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                                 return_lse=True, v_layout=c["v_layout"], split_pages=c["split"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    S = sample_rows(w, 96, seed=i)
+    Os, Ls = oracle.attention_rows(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, Hkv, S)
+    r = torch.from_numpy(w.cu_q[S[:, 0]] + S[:, 2]).cuda()
+    h = torch.from_numpy(S[:, 1]).cuda()
+    compare(w, o[r, h].float().cpu().numpy(), Os, f"long sweep {i}")
+    assert np.max(np.abs(lse[r, h].cpu().numpy() - Ls)) < (1e-4 if c["mode"] == "f32" else 2 ** -7)
