@@ -136,7 +136,7 @@ def test_sweep(i):
         check_lse(ld, Ld, 2 ** -7)
 
 
-N_LONG = 12
+N_LONG = int(os.environ.get("CPA_SWEEP_LONG_CASES", "12"))
 
 
 def draw_long(i):
