@@ -48,7 +48,7 @@ typedef enum {
   CPA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
   CPA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
   CPA_ERR_ALIGN = 3,       /* a pointer or stride breaks the alignment stated below         */
-  CPA_ERR_UNSUPPORTED = 4, /* dtype, head dim or group size this build does not implement  */
+  CPA_ERR_UNSUPPORTED = 4, /* dtype, head dim or group size the library does not implement */
   CPA_ERR_CAPACITY = 5,    /* table capacity smaller than the KV-block count               */
   CPA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch                      */
 } cpa_status;
