@@ -252,8 +252,9 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     the workspace (a CUDA uint8 tensor of split_workspace_bytes(...) bytes) is allocated here
     when not given.  split_pages="auto" picks the range length with plan_split_pages for the
     device's compute units: a split when the call has fewer tiles than CUs and the split kernel
-    takes the pools (bf16, row strides up to 2^24 elements), else none.  v_layout "dim" calls cpa_chunked_prefill_vt.  float8_e4m3fn pools with a
-    bf16 q call cpa_chunked_prefill_fp8kv with the dequantization scales k_scale / v_scale.
+    takes the pools (bf16, row strides up to 2^24 elements), else none.  v_layout "dim" calls
+    cpa_chunked_prefill_vt.  float8_e4m3fn pools with a bf16 q call cpa_chunked_prefill_fp8kv
+    with the dequantization scales k_scale / v_scale.
     """
     auto = isinstance(split_pages, str)
     if auto and split_pages != "auto":
@@ -294,10 +295,13 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
         raise ValueError("inconsistent B across cu_q / prefix_len / counts / page_map")
     cap = tables.shape[-1] if tables.numel() else 0
     _on(dev, page_map=page_map, tables=tables, counts=counts, cu_q=cu_q, prefix_len=prefix_len)
-    if auto:   # the split kernel takes bf16 pools whose rows (tokens, or dims of dim-major V) are at most 2^24 apart
-        splittable = q.dtype == torch.bfloat16 and not fp8 and max(k_pages.stride(2), v_pages.stride(2)) <= (1 << 24)
-        split_pages = plan_split_pages(B, Hq, Hkv, max_chunk_len, cap,
-                                       torch.cuda.get_device_properties(dev).multi_processor_count) if splittable else 0
+    if auto:
+        # the split kernel takes bf16 pools whose rows (tokens, or dims of dim-major V) are at
+        # most 2^24 elements apart
+        splittable = (q.dtype == torch.bfloat16 and not fp8
+                      and max(k_pages.stride(2), v_pages.stride(2)) <= (1 << 24))
+        n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        split_pages = plan_split_pages(B, Hq, Hkv, max_chunk_len, cap, n_cus) if splittable else 0
     out, lse = _out_buffers(out, lse, return_lse, q, dev)
     with torch.cuda.device(dev):
         hs = _stream(stream, dev)
