@@ -48,7 +48,7 @@ typedef enum {
   CPA_ERR_NULL = 1,        /* a required pointer is NULL                                   */
   CPA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
   CPA_ERR_ALIGN = 3,       /* a pointer or stride breaks the alignment stated below         */
-  CPA_ERR_UNSUPPORTED = 4, /* dtype, head dim or group size the library does not implement */
+  CPA_ERR_UNSUPPORTED = 4, /* dtype, head dim or path the library does not implement      */
   CPA_ERR_CAPACITY = 5,    /* table capacity smaller than the KV-block count               */
   CPA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch                      */
 } cpa_status;
@@ -122,8 +122,9 @@ cpa_status cpa_build_block_tables_bits(const uint64_t* mask_bits, int B, int Hq,
  *            c contiguous); the dense layout [n_pages][Hkv][64][d] has page_stride = Hkv*64*d,
  *            head_stride = 64*d, token_stride = d.  Base pointers 16-byte aligned and every
  *            stride a multiple of 16 bytes.
- *   n_pages  physical pages in the pool.  A page id outside [0, n_pages), or a table entry
- *            outside [0, page_map_stride), is never dereferenced: its keys and values read as NaN.
+ *   n_pages  physical pages in the pool, >= 1 when there is work (B > 0, max_chunk_len > 0;
+ *            else CPA_ERR_SHAPE).  A page id outside [0, n_pages), or a table entry outside
+ *            [0, page_map_stride), is never dereferenced: its keys and values read as NaN.
  *   page_map int32 [B][page_map_stride]: logical KV block -> physical page.
  *   tables, counts, table_cap  as produced by cpa_build_block_tables (ids ascending; counts are
  *            clamped to table_cap).
@@ -139,10 +140,10 @@ cpa_status cpa_build_block_tables_bits(const uint64_t* mask_bits, int B, int Hq,
  *
  * Supported: dtype CPA_BF16 (bf16 MFMA, fp32 accumulation and softmax, P rounded to bf16
  * before the PV product) and CPA_F32 (fp32 MFMA end to end); d in {64, 128};
- * G = Hq/Hkv in {1, 2, 4} or a multiple of 4 up to 32.
+ * G = Hq/Hkv any divisor (a workgroup takes four (query block, head) pairs of one group).
  * Errors: CPA_ERR_NULL, CPA_ERR_SHAPE (negative sizes, Hq % Hkv != 0, table_cap < 0,
- * page_map_stride < 1 with B > 0, strides too small to hold a page), CPA_ERR_ALIGN,
- * CPA_ERR_UNSUPPORTED, CPA_ERR_LAUNCH.
+ * page_map_stride < 1 or n_pages < 1 with work to do, strides too small to hold a page),
+ * CPA_ERR_ALIGN, CPA_ERR_UNSUPPORTED (dtype, d), CPA_ERR_LAUNCH.
  */
 cpa_status cpa_chunked_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
                                const void* v_pages, int64_t page_stride, int64_t head_stride,
@@ -315,8 +316,8 @@ cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void
  *   v_pages     e4m3 pool, token-major (v_dim_major = 0, v_row_stride = token stride) or
  *               dim-major (v_dim_major = 1, v_row_stride = dim stride), strides in bytes.
  *   k_scale, v_scale  finite, > 0 (else CPA_ERR_SHAPE): the per-tensor dequantization scales.
- * Other arguments and errors as cpa_chunked_prefill (dtype bf16 for q and o; strides 16-byte
- * multiples).  With dim-major V the pages are staged in LDS as codes and converted at operand
+ * Other arguments and errors as cpa_chunked_prefill (dtype bf16 for q and o; pool strides are
+ * in bytes and must be 16-byte multiples, else CPA_ERR_ALIGN).  With dim-major V the pages are staged in LDS as codes and converted at operand
  * read; with token-major V they are converted on their way into LDS.  No split-KV form.
  */
 cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const void* v_pages, int64_t page_stride,

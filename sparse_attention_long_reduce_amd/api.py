@@ -47,6 +47,13 @@ def _dev_i32(x, name):
     return x
 
 
+def _i32(x, name):
+    """Dtype and layout of an int32 index tensor (its device is checked with the others)."""
+    if not (isinstance(x, torch.Tensor) and x.dtype == torch.int32 and x.is_contiguous()):
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return x
+
+
 def _out_buffers(out, lse, return_lse, q, dev):
     """Validate caller-given o / lse (contiguous, q's shape and dtype / float32 [Tq][Hq]) or
     allocate them."""
@@ -164,7 +171,6 @@ def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu
     views allowed as in chunked_prefill); plans / plan_counts from build_block_plans."""
     if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("the direct baseline runs bf16 q, k_pages and v_pages")
-    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages)
     if q.dim() != 3 or not q.is_contiguous():
         raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
     Tq, Hq, d = q.shape
@@ -175,12 +181,17 @@ def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu
         raise ValueError("v_pages must be dim-major [n_pages][Hkv][d][64] with the token dimension contiguous")
     for t, nm in ((page_map, "page_map"), (plans, "plans"), (plan_counts, "plan_counts"), (cu_q, "cu_q"),
                   (prefix_len, "prefix_len")):
-        _dev_i32(t, nm)
+        _i32(t, nm)
     B = prefix_len.numel()
     if plans.dim() != 4 or plans.shape[0] != B or plans.shape[1] != Hq:
         raise ValueError("plans must be [B][Hq][nqb_max][cap]")
     nqb_max, cap = plans.shape[2], plans.shape[3]
-    _on(dev, page_map=page_map, plans=plans, plan_counts=plan_counts, cu_q=cu_q, prefix_len=prefix_len)
+    if tuple(plan_counts.shape) != (B, Hq, nqb_max):
+        raise ValueError("plan_counts must be [B][Hq][nqb_max], matching plans")
+    if cu_q.numel() != B + 1 or page_map.dim() != 2 or page_map.shape[0] != B:
+        raise ValueError("inconsistent B across cu_q / prefix_len / page_map")
+    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, plans=plans,
+              plan_counts=plan_counts, cu_q=cu_q, prefix_len=prefix_len)
     out, lse = _out_buffers(out, lse, return_lse, q, dev)
     with torch.cuda.device(dev):
         st = load().cpa_chunked_prefill_direct(
@@ -213,14 +224,15 @@ def plan_flops(plans, plan_counts, prefix_len, chunk_len, d):
     return 4 * d * total
 
 
+PAIRS_PER_TILE = 4   # (query block, head) pairs per prefill workgroup
+
+
 def prefill_tiles(B, Hq, Hkv, max_chunk_len):
-    """Workgroups cpa_chunked_prefill launches without split-KV (one per group and query tile):
-    a tile is the group's heads (up to 4 per workgroup) times 1, 2 or 4 query blocks."""
+    """Workgroups cpa_chunked_prefill launches without split-KV: per KV group, its (query block,
+    head) pairs in tiles of four consecutive ones (pairs numbered query block * G + head)."""
     G = Hq // Hkv
-    hpw = min(G, 4)
-    qpw = 4 // hpw
     nqb = -(-int(max_chunk_len) // BLOCK)
-    return B * Hkv * -(-nqb // qpw) * (G // hpw)
+    return B * Hkv * -(-(nqb * G) // PAIRS_PER_TILE)
 
 
 def plan_split_pages(B, Hq, Hkv, max_chunk_len, table_cap, n_cus, max_splits=16):
@@ -259,7 +271,6 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     auto = isinstance(split_pages, str)
     if auto and split_pages != "auto":
         raise ValueError('split_pages must be an int or "auto"')
-    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages)
     fp8 = k_pages.dtype == torch.float8_e4m3fn
     if fp8:
         if q.dtype != torch.bfloat16 or v_pages.dtype != k_pages.dtype:
@@ -285,16 +296,17 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     if k_pages.stride(3) != 1:
         raise ValueError("the head dimension of the pages must be contiguous")
     n_pages, Hkv = k_pages.shape[0], k_pages.shape[1]
-    _dev_i32(page_map, "page_map")
-    _dev_i32(tables, "tables")
-    _dev_i32(counts, "counts")
-    _dev_i32(cu_q, "cu_q")
-    _dev_i32(prefix_len, "prefix_len")
+    for t, nm in ((page_map, "page_map"), (tables, "tables"), (counts, "counts"), (cu_q, "cu_q"),
+                  (prefix_len, "prefix_len")):
+        _i32(t, nm)
     B = prefix_len.numel()
     if cu_q.numel() != B + 1 or counts.numel() != B * Hkv or page_map.dim() != 2 or page_map.shape[0] != B:
         raise ValueError("inconsistent B across cu_q / prefix_len / counts / page_map")
-    cap = tables.shape[-1] if tables.numel() else 0
-    _on(dev, page_map=page_map, tables=tables, counts=counts, cu_q=cu_q, prefix_len=prefix_len)
+    if tables.dim() != 3 or tables.shape[0] != B or tables.shape[1] != Hkv:
+        raise ValueError("tables must be [B][Hkv][cap] (B sequences, Hkv KV groups)")
+    cap = tables.shape[2]
+    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, tables=tables,
+              counts=counts, cu_q=cu_q, prefix_len=prefix_len)
     if auto:
         # the split kernel takes bf16 pools whose rows (tokens, or dims of dim-major V) are at
         # most 2^24 elements apart

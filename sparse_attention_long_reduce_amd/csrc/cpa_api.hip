@@ -1,5 +1,5 @@
 // C ABI: host-side argument checks, work decomposition and launches (see include/cpa.h).
-#include "../../include/cpa.h"
+#include "cpa.h"
 #include "cpa_internal.h"
 
 #include <climits>
@@ -43,7 +43,7 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
                            const int32_t* counts, const int32_t* cu_q,
                            const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
                            int max_chunk_len, float sm_scale, void* o, float* lse,
-                           cpa::PrefillArgs& a, bool* nothing) {
+                           cpa::PrefillArgs& a, bool* nothing, int kv_elem_bytes = 0) {
   *nothing = false;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || table_cap < 0 || n_pages < 0)
     return CPA_ERR_SHAPE;
@@ -52,12 +52,14 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   if (dtype != CPA_F32 && dtype != CPA_BF16) return CPA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return CPA_ERR_UNSUPPORTED;
   const int G = Hq / Hkv;
-  if (!(G == 1 || G == 2 || G == 4 || (G % 4 == 0 && G <= 32))) return CPA_ERR_UNSUPPORTED;
   if (B == 0 || max_chunk_len == 0) {
     *nothing = true;
     return CPA_OK;
   }
   if (page_map_stride < 1) return CPA_ERR_SHAPE;
+  // the kernels stage page 0 of the pool for copy slots that have no page to fill, so a call
+  // with work needs a pool of at least one page
+  if (n_pages < 1) return CPA_ERR_SHAPE;
   if (token_stride > kMaxStride || head_stride > kMaxStride || page_stride > kMaxStride ||
       vl.row_stride > kMaxStride || vl.head_stride > kMaxStride || vl.page_stride > kMaxStride)
     return CPA_ERR_SHAPE;
@@ -69,7 +71,8 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
     return CPA_ERR_SHAPE;
   if (!q || !k_pages || !v_pages || !page_map || !counts || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
   if (table_cap > 0 && !tables) return CPA_ERR_NULL;
-  const int eb = dtype == CPA_BF16 ? 2 : 4;
+  // bytes per pool element: that of q's dtype unless the pools hold another format (fp8)
+  const int eb = kv_elem_bytes > 0 ? kv_elem_bytes : dtype == CPA_BF16 ? 2 : 4;
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return CPA_ERR_ALIGN;
   if ((token_stride * eb) % 16 || (head_stride * eb) % 16 || (page_stride * eb) % 16) return CPA_ERR_ALIGN;
   if ((vl.row_stride * eb) % 16 || (vl.head_stride * eb) % 16 || (vl.page_stride * eb) % 16) return CPA_ERR_ALIGN;
@@ -89,13 +92,10 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   a.out_scale = 1.0f;
   a.o = o; a.lse = lse;
   a.G = G;
-  a.hpw = G >= 4 ? 4 : G;
-  a.qpw = 4 / a.hpw;
-  a.hsplit = G / a.hpw;
-  const int nqb_max = (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK;
-  a.n_qtiles = (nqb_max + a.qpw - 1) / a.qpw;
-  a.tiles_per_group = a.n_qtiles * a.hsplit;
-  if ((int64_t)B * Hkv > INT_MAX) return CPA_ERR_SHAPE;
+  const int64_t nqb_max = (max_chunk_len + CPA_BLOCK - 1) / CPA_BLOCK;
+  const int64_t tiles = (nqb_max * G + cpa::PAIRS_PER_TILE - 1) / cpa::PAIRS_PER_TILE;
+  if (tiles > INT_MAX || (int64_t)B * Hkv > INT_MAX) return CPA_ERR_SHAPE;
+  a.tiles_per_group = (int)tiles;
   a.n_groups = B * Hkv;
   a.xcd_remap = a.n_groups >= 8 ? 1 : 0;
   a.n_splits = 1;
@@ -113,7 +113,7 @@ const char* cpa_status_string(cpa_status s) {
     case CPA_ERR_NULL: return "a required pointer is NULL";
     case CPA_ERR_SHAPE: return "invalid or inconsistent size";
     case CPA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
-    case CPA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or group size";
+    case CPA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or path";
     case CPA_ERR_CAPACITY: return "table capacity smaller than the KV-block count, or workspace too small";
     case CPA_ERR_LAUNCH: return "kernel launch failed";
   }
@@ -231,7 +231,8 @@ cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const v
   const VLayout vl{v_page_stride, v_head_stride, v_row_stride, v_dim_major == 1};
   const cpa_status st = prepare_prefill(q, CPA_BF16, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
                                         n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
-                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
+                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing,
+                                        /*kv_elem_bytes=*/1);
   if (st != CPA_OK || nothing) return st;
   a.kv_fp8 = 1;
   a.scale_log2 *= k_scale;   // scores of the stored values times the K scale
@@ -388,3 +389,4 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
 }
 
 }  // extern "C"
+

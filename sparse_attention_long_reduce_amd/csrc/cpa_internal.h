@@ -5,6 +5,9 @@
 
 namespace cpa {
 
+// (query block, head) pairs per prefill workgroup: one pair per two waves (64 query rows)
+constexpr int PAIRS_PER_TILE = 4;
+
 struct UnionArgs {
   const uint8_t* masks;
   int B, Hq, Hkv, nqb_max, nkvb_max;
@@ -47,11 +50,9 @@ struct PrefillArgs {
   float* lse;
   // work decomposition (filled by the launcher)
   int G;                // query heads per KV group
-  int hpw;              // query heads per workgroup (one wave each, per query block)
-  int qpw;              // query blocks per workgroup
-  int hsplit;           // workgroups per (group, query-block tile) along the heads: G / hpw
-  int n_qtiles;         // query-block tiles per group: ceil(max query blocks / qpw)
-  int tiles_per_group;  // n_qtiles * hsplit
+  // A KV group's (query block, head) pairs, numbered qi * G + h, are cut into tiles of
+  // PAIRS_PER_TILE consecutive pairs (see tile_pairs in prefill_common.h)
+  int tiles_per_group;  // ceil(max query blocks * G / PAIRS_PER_TILE)
   int n_groups;         // B * Hkv
   int xcd_remap;        // 1: keep each KV group's tiles on one XCD (see the prefill kernel)
   // split-KV: the pages each tile visits are cut into n_splits near-equal ranges (at most

@@ -6,11 +6,13 @@
 // which are accessed where they lie in the paged cache, with no KV compaction.
 //
 // Work decomposition.  A workgroup is 8 waves and owns one KV group g of one sequence b and one
-// tile of query blocks.  With G = Hq/Hkv query heads per group, a wave holds one query head x
-// 32 chunk rows; two waves cover the 64 rows of a query block.  For G = 4 the workgroup is the
-// group's four heads on one query block; G = 2 (1) packs 2 (4) query blocks; G > 4 splits the
-// heads over G/4 workgroups.  Every selected KV page is brought into LDS once per workgroup
-// and read by all eight waves, i.e. by every head and row of the tile.
+// tile of four (query block, head) pairs.  With G = Hq/Hkv query heads per group, the group's
+// pairs are numbered qi * G + h and a tile takes four consecutive ones (tile_pairs in
+// prefill_common.h); two waves cover the 64 rows of a pair, one query head x 32 chunk rows
+// each.  For G = 4 a tile is the group's four heads on one query block; G = 2 (1) packs 2 (4)
+// query blocks; G = 8 gives each query block two tiles; any other G fills the four slots the
+// same way, a tile then spanning two query blocks.  Every selected KV page is brought into LDS
+// once per workgroup and read by all eight waves, i.e. by every head and row of the tile.
 //
 // Page staging.  Each page (64 tokens x d, K and V) is copied HBM -> LDS by the gfx950
 // direct-to-LDS loads (global_load_lds_dwordx4): every instruction moves 64 16-byte chunks,
@@ -77,6 +79,7 @@ namespace {
 constexpr int THREADS = 512;
 constexpr int WIN = 1024;  // circular window of resolved page ids
 constexpr int CH = 512;    // ids resolved at a time
+static_assert((WIN & (WIN - 1)) == 0 && (CH & (CH - 1)) == 0 && CH <= WIN, "window sizes");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -176,23 +179,22 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   if (!decode_tile(a, lane, gi, rank, split)) return;
   const int b = gi / a.Hkv;
   const int g = gi - b * a.Hkv;
-  const int hsub = rank % a.hsplit;
-  const int qt = a.n_qtiles - 1 - rank / a.hsplit;  // heaviest (last) query blocks first
+  const int t_pairs = a.tiles_per_group - 1 - rank;   // heaviest (last) query blocks first
 
   const int P = max(a.prefix_len[b], 0);
   const int q0 = a.cu_q[b];
   const int Cn = min(max(a.cu_q[b + 1] - q0, 0), a.max_chunk_len);
   const int nqb = (Cn + 63) >> 6;
-  const int qi_first = qt * a.qpw;
+  const int half = wave & 1;       // which 32 rows of the query block
+  const int pair = wave >> 1;      // (query block, head) pair slot of this wave
+  int qi_first, qi_span, qi_w, h_w;
+  tile_pairs(t_pairs, pair, a.G, qi_first, qi_span, qi_w, h_w);
   if (qi_first >= nqb) return;  // uniform over the workgroup
   const int qb0 = P >> 6;
   const int L = P + Cn;
-  const int half = wave & 1;       // which 32 rows of the query block
-  const int pair = wave >> 1;      // (head, query block) pair of this wave
-  const int qi_w = qi_first + pair / a.hpw;
-  const int head = g * a.G + hsub * a.hpw + (pair % a.hpw);
+  const int head = g * a.G + h_w;
   const bool active = qi_w < nqb;
-  const int qi_last = min(qi_first + a.qpw - 1, nqb - 1);
+  const int qi_last = min(qi_span, nqb - 1);
 
   const int cnt = min(max(a.counts[gi], 0), a.table_cap);
   const int32_t* tab = a.tables + (size_t)gi * a.table_cap;
@@ -322,7 +324,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     for (int j = 0; j < NPW; ++j) fill_one(f, j);
   };
 
-  // resolve table entries [base, base + CH) into window slots (base + j) % WIN
+  // resolve table entries [base, base + CH) into window slots (base + j) mod WIN (indices are
+  // non-negative and WIN, CH powers of two)
   auto load_chunk = [&](int base) __attribute__((always_inline)) {
     for (int j = tid; j < CH && base + j < n_iter; j += THREADS) {
       const int kb = tab[base + j];
@@ -331,8 +334,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
         ph = pmap[kb];
         if (ph < 0 || (int64_t)ph >= a.n_pages) ph = -1;
       }
-      win_kb[(base + j) % WIN] = kb;
-      win_ph[(base + j) % WIN] = ph;
+      win_kb[(base + j) & (WIN - 1)] = kb;
+      win_ph[(base + j) & (WIN - 1)] = ph;
     }
   };
 
@@ -551,8 +554,8 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   if (n_iter > 0) {
     load_chunk(0);
     __syncthreads();
-    auto kb_at = [&](int j) __attribute__((always_inline)) { return win_kb[j % WIN]; };
-    auto ph_at = [&](int j) __attribute__((always_inline)) { return win_ph[j % WIN]; };
+    auto kb_at = [&](int j) __attribute__((always_inline)) { return win_kb[j & (WIN - 1)]; };
+    auto ph_at = [&](int j) __attribute__((always_inline)) { return win_ph[j & (WIN - 1)]; };
     auto kr = [&](int t) __attribute__((always_inline)) { return t == 0 ? kR0 : t == 1 ? kR1 : t == 2 ? kR2 : kR3; };
     auto vr = [&](int t) __attribute__((always_inline)) { return t == 0 ? vR0 : t == 1 ? vR1 : t == 2 ? vR2 : vR3; };
     // F8: bf16 pages in tiles 0 and 1, the four staging pages of codes in tiles 2 and 3
@@ -643,7 +646,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     // end of iteration i: resolve the next chunk of the window when entry i + 2 + FOK (the
     // furthest read below) starts one, read the ids of iteration i+2, shift the queue
     auto advance = [&](const int i) __attribute__((always_inline)) {
-      if ((i + 2 + FOK) % CH == 0 && i + 2 + FOK < n_iter) {
+      if (((i + 2 + FOK) & (CH - 1)) == 0 && i + 2 + FOK < n_iter) {
         load_chunk(i + 2 + FOK);
         __syncthreads();
       }

@@ -101,6 +101,20 @@ __device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int lane, int&
   return true;
 }
 
+// Pairs of tile t of a KV group with G query heads.  The group's (query block qi, head h) pairs
+// are numbered qi * G + h and tile t holds pairs 4t .. 4t+3, so every group size fills the
+// workgroup's four pair slots (a tile may span two or more query blocks).  For wave pair slot
+// `slot`: qi_w / h_w are that pair's query block and head within the group; qi_first / qi_last are
+// the first and last query block the tile touches (before clamping to the chunk).
+__device__ __forceinline__ void tile_pairs(int t, int slot, int G, int& qi_first, int& qi_last, int& qi_w, int& h_w) {
+  const int p0 = PAIRS_PER_TILE * t;
+  qi_first = p0 / G;
+  qi_last = (p0 + PAIRS_PER_TILE - 1) / G;
+  const int p = p0 + slot;
+  qi_w = p / G;
+  h_w = p - qi_w * G;
+}
+
 inline int prefill_grid(const PrefillArgs& a) {
   const int per_group = a.tiles_per_group * a.n_splits;
   return a.xcd_remap ? 8 * ((a.n_groups + 7) / 8) * per_group : a.n_groups * per_group;

@@ -98,23 +98,22 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
   if (!decode_tile(a, lane, gi, rank, split)) return;
   const int b = gi / a.Hkv;
   const int g = gi - b * a.Hkv;
-  const int hsub = rank % a.hsplit;
-  const int qt = a.n_qtiles - 1 - rank / a.hsplit;  // heaviest (last) query blocks first
+  const int t_pairs = a.tiles_per_group - 1 - rank;   // heaviest (last) query blocks first
 
   const int P = max(a.prefix_len[b], 0);
   const int q0 = a.cu_q[b];
   const int Cn = min(max(a.cu_q[b + 1] - q0, 0), a.max_chunk_len);
   const int nqb = (Cn + 63) >> 6;
-  const int qi_first = qt * a.qpw;
+  const int half = wave & 1;       // which 32 rows of the query block
+  const int pair = wave >> 1;      // (query block, head) pair slot of this wave
+  int qi_first, qi_span, qi_w, h_w;
+  tile_pairs(t_pairs, pair, a.G, qi_first, qi_span, qi_w, h_w);
   if (qi_first >= nqb) return;  // uniform over the workgroup
   const int qb0 = P >> 6;
   const int L = P + Cn;
-  const int half = wave & 1;       // which 32 rows of the query block
-  const int pair = wave >> 1;      // (head, query block) pair of this wave
-  const int qi_w = qi_first + pair / a.hpw;
-  const int head = g * a.G + hsub * a.hpw + (pair % a.hpw);
+  const int head = g * a.G + h_w;
   const bool active = qi_w < nqb;
-  const int qi_last = min(qi_first + a.qpw - 1, nqb - 1);
+  const int qi_last = min(qi_span, nqb - 1);
 
   const int cnt = min(max(a.counts[gi], 0), a.table_cap);
   const int32_t* tab = a.tables + (size_t)gi * a.table_cap;

@@ -72,3 +72,25 @@ def test_split_pages_takes_int_or_auto():
     q, kp, vp, pm, t, c, cu, pl = _cpu_args()
     with pytest.raises(ValueError, match="auto"):
         cpa.chunked_prefill(q, kp, vp, pm, t, c, cu, pl, 64, split_pages="fastest")
+
+
+def test_prefill_refuses_mis_shaped_tables():
+    # the kernel reads tables + group * cap for every (sequence, group): a table of the wrong
+    # shape is refused before any device or library call (CPU tensors reach the shape checks)
+    q, kp, vp, pm, t, c, cu, pl = _cpu_args()
+    for bad in (torch.zeros(2, dtype=torch.int32),              # flat
+                torch.zeros(1, 2, 2, dtype=torch.int32),        # two groups for Hkv = 1
+                torch.zeros(2, 1, 2, dtype=torch.int32)):       # two sequences for B = 1
+        with pytest.raises(ValueError, match="tables"):
+            cpa.chunked_prefill(q, kp, vp, pm, bad, c, cu, pl, 64)
+
+
+def test_direct_refuses_mis_shaped_plan_counts():
+    q, kp, vp, pm, t, c, cu, pl = _cpu_args()
+    vd = vp.transpose(2, 3).contiguous()
+    plans = torch.zeros(1, 4, 1, 2, dtype=torch.int32)
+    for bad in (torch.zeros(4, dtype=torch.int32),               # [B*Hq] only: no query-block axis
+                torch.zeros(1, 4, 2, dtype=torch.int32),         # two query blocks for plans of one
+                torch.zeros(1, 2, 1, dtype=torch.int32)):        # two heads for Hq = 4
+        with pytest.raises(ValueError, match="plan_counts"):
+            cpa.chunked_prefill_direct(q, kp, vd, pm, plans, bad, cu, pl, 64)

@@ -35,6 +35,8 @@ SMALL = {
     "g1_d128": dict(prefix_len=[1024, 64], chunk_len=[192, 100], Hq=2, Hkv=2, d=128, mask_fn=bern(0.3)),
     "all_zero": dict(prefix_len=[256], chunk_len=[128], Hq=8, Hkv=2, d=128, mask_fn=lambda rng, *a: mask_all(rng, *a, value=0)),
     "zero_len_chunk": dict(prefix_len=[128, 256], chunk_len=[0, 128], Hq=8, Hkv=2, d=64, mask_fn=bern(0.3)),
+    "g3_ragged": dict(prefix_len=[0, 448], chunk_len=[200, 129], Hq=6, Hkv=2, d=128, mask_fn=bern(0.1)),
+    "g7_d64": dict(prefix_len=[640, 64], chunk_len=[300, 64], Hq=14, Hkv=2, d=64, mask_fn=bern(0.1)),
 }
 
 

@@ -35,6 +35,8 @@ SMALL = {
     "g4_f32_d64_stripes": dict(prefix_len=[1536], chunk_len=[512], Hq=8, Hkv=2, d=64, dtype="f32", mask_fn=lambda rng, *a: mask_stripes(rng, *a, p=0.1, shared_per_group=False)),
     "all_zero_bf16": dict(prefix_len=[256], chunk_len=[128], Hq=8, Hkv=2, d=128, dtype="bf16", mask_fn=lambda rng, *a: mask_all(rng, *a, value=0)),
     "zero_len_chunk": dict(prefix_len=[128, 256], chunk_len=[0, 128], Hq=8, Hkv=2, d=64, dtype="bf16", mask_fn=bern(0.3)),
+    "g3_bf16_ragged": dict(prefix_len=[0, 448], chunk_len=[200, 129], Hq=6, Hkv=2, d=128, dtype="bf16", mask_fn=bern(0.1)),
+    "g7_bf16_d64": dict(prefix_len=[640, 64], chunk_len=[300, 64], Hq=14, Hkv=2, d=64, dtype="bf16", mask_fn=bern(0.1)),
 }
 
 
@@ -158,7 +160,8 @@ def test_dim_major_poison_unselected_pages():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("name", ["c3_128k_last_chunk", "c5b_varlen_independent", "c3s_128k_one_group"])
+@pytest.mark.parametrize("name", ["c3_128k_last_chunk", "c5b_varlen_independent", "c3s_128k_one_group",
+                                  "c3g7_128k_gqa7"])
 def test_dim_major_full_size(name):
     print(f"\n[case] dim-major V full {name}", flush=True)
     w = make_config(name)

@@ -239,7 +239,7 @@ CONFIG_NAMES = (
 
 SEEDS = {"c1_tiny_f32": 1001, "c2_32k_bf16": 1002, "c3_128k_last_chunk": 1003,
          "c4_128k_chunked": 1004, "c5a_varlen_shared": 1005, "c5b_varlen_independent": 1006,
-         "c3s_128k_one_group": 1007, "c3d_128k_no_noise": 1003}
+         "c3s_128k_one_group": 1007, "c3d_128k_no_noise": 1003, "c3g7_128k_gqa7": 1008}
 
 # One KV group's share of the 128K last-chunk workload: what each of 8 GPUs would hold if the
 # layer's 8 KV groups were split across them (4 query heads, 1 KV head); 32 query tiles.
@@ -250,6 +250,10 @@ SHARD_NAMES = ("c3s_128k_one_group",)
 # and local window are exactly the headline's and the group unions stay sparse (about a quarter
 # of the blocks) instead of near-dense.
 DIAG_NAMES = ("c3d_128k_no_noise",)
+
+# A parity case for a group size that is not a power of two: the 128K last chunk with 28 query
+# heads over 4 KV heads (G = 7, a grouping some GQA models use), the headline's mask generator.
+GQA_NAMES = ("c3g7_128k_gqa7",)
 
 C4_SEQ = 131072
 C4_CHUNK = 2048
@@ -330,6 +334,9 @@ def make_config(name: str, dense: bool = False, chunk: int = 63, seed: int | Non
     if name == "c3d_128k_no_noise":
         fn = ones if dense else (lambda rng, *a: mask_structured(rng, *a, bern_p=0.0))
         return make_workload(name, [129024], [2048], 32, 8, 128, "bf16", fn, s)
+    if name == "c3g7_128k_gqa7":
+        fn = ones if dense else mask_structured
+        return make_workload(name, [129024], [2048], 28, 4, 128, "bf16", fn, s)
     if name == "c3s_128k_one_group":
         fn = ones if dense else mask_structured
         return make_workload(name, [129024], [2048], 4, 1, 128, "bf16", fn, s)
