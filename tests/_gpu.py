@@ -54,8 +54,11 @@ def compare(w, o_gpu, O_ref, what=""):
     return mx, mean, rel
 
 
-def sample_rows(w, n, seed=0):
-    """(b, h, r) samples: random rows plus the first/last rows of tiles and of each chunk."""
+def sample_rows(w, n, seed=0, per_tile=2):
+    """(b, h, r) samples that reach every tile of the prefill: for every sequence b, KV group g
+    and query block qi, `per_tile` rows of that block (one in each 32-row half, the halves two
+    different waves compute) at random heads of g; the first/last rows of tiles and of each
+    chunk; and random rows until there are at least n beyond the per-tile ones."""
     rng = np.random.default_rng(seed)
     out = set()
     for b in range(w.B):
@@ -66,9 +69,91 @@ def sample_rows(w, n, seed=0):
             for r in (0, 31, 32, 63, 64, C - 64, C - 33, C - 1):
                 if 0 <= r < C:
                     out.add((b, h, r))
-    while len(out) < n:
+        for g in range(w.Hkv):
+            for qi in range((C + 63) // 64):
+                for k in range(per_tile):
+                    lo = 64 * qi + 32 * (k % 2)
+                    hi = min(C, lo + 32)
+                    if lo >= C:
+                        lo, hi = 64 * qi, min(C, 64 * qi + 64)
+                    out.add((b, g * w.G + int(rng.integers(0, w.G)), int(rng.integers(lo, hi))))
+    n_tile = len(out)
+    while len(out) < n_tile + n:
         b = int(rng.integers(0, w.B))
         C = int(w.chunk_len[b])
         if C:
             out.add((b, int(rng.integers(0, w.Hq)), int(rng.integers(0, C))))
     return np.array(sorted(out), dtype=np.int64)
+
+
+def tiles_reached(w, S):
+    """Number of (sequence, KV group, query block) tiles that the samples S reach, and the total."""
+    seen = {(int(b), int(h) // w.G, int(r) // 64) for b, h, r in S}
+    total = sum(w.Hkv * ((int(c) + 63) // 64) for c in w.chunk_len)
+    return len(seen), total
+
+
+def oracle_full(w, T, C, q=None, k_pages=None, v_pages=None, workers=None):
+    """The oracle's O [Tq][Hq][d] and LSE [Hq][Tq] for every row, computed one (sequence, KV
+    group, row range) at a time in a thread pool: each piece is oracle.paged_attention on that
+    sequence's rows and that group's heads and pages (groups and rows are independent by the
+    definition), with BLAS kept to one thread per piece."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+    q = w.q if q is None else q
+    kp = w.k_pages if k_pages is None else k_pages
+    vp = w.v_pages if v_pages is None else v_pages
+    Tq, Hq, d = q.shape
+    G = w.G
+    O = np.zeros((Tq, Hq, d), dtype=np.float64)
+    LSE = np.full((Hq, Tq), -np.inf, dtype=np.float64)
+    workers = workers or min(16, os.cpu_count() or 1)
+    pieces = []
+    n_bg = max(1, sum(1 for b in range(w.B) if w.chunk_len[b] > 0) * w.Hkv)
+    for b in range(w.B):
+        q0, q1 = int(w.cu_q[b]), int(w.cu_q[b + 1])
+        if q1 == q0:
+            continue
+        n_split = max(1, min(-(-workers // n_bg), (q1 - q0) // 64))
+        step = -(-(q1 - q0) // (64 * n_split)) * 64
+        for g in range(w.Hkv):
+            for r0 in range(0, q1 - q0, step):
+                pieces.append((b, g, r0, min(q1 - q0, r0 + step)))
+
+    def run(piece):
+        b, g, r0, r1 = piece
+        q0 = int(w.cu_q[b])
+        o, lse = oracle.paged_attention(
+            q[q0 + r0:q0 + r1, g * G:(g + 1) * G], kp[:, g:g + 1], vp[:, g:g + 1], w.page_map[b:b + 1],
+            T[b:b + 1, g:g + 1], C[b:b + 1, g:g + 1], np.array([0, r1 - r0], dtype=np.int64),
+            np.array([int(w.prefix_len[b]) + r0], dtype=np.int64), 1)
+        O[q0 + r0:q0 + r1, g * G:(g + 1) * G] = o
+        LSE[g * G:(g + 1) * G, q0 + r0:q0 + r1] = lse
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(run, pieces))
+    return O, LSE
+
+
+def error_stats(o, O_ref):
+    """max-abs, mean-abs and rel-L2 of o (GPU, any float dtype) against the fp64 oracle."""
+    o = o.float().cpu().numpy().astype(np.float64) if isinstance(o, torch.Tensor) else np.asarray(o, np.float64)
+    err = np.abs(o - O_ref)
+    return {"max_abs": float(err.max()), "mean_abs": float(err.mean()),
+            "rel_l2": float(np.linalg.norm(o - O_ref) / max(np.linalg.norm(O_ref), 1e-300)),
+            "ref_rms": float(np.sqrt(np.mean(O_ref ** 2))), "elements": int(err.size)}
+
+
+def report(name, stats):
+    """Print one parity line and, when CPA_PARITY_REPORT names a file, append it there as JSON."""
+    import json
+    import os
+    line = {"case": name, **stats}
+    print(f"[parity] {json.dumps(line)}", flush=True)
+    path = os.environ.get("CPA_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")

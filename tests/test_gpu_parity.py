@@ -16,7 +16,9 @@ import oracle
 from workloads import make_config, make_workload
 from workloads.configs import mask_all, mask_bernoulli, mask_stripes, mask_structured
 
-from _gpu import compare, gpu_prefill, gpu_tables, sample_rows, upload
+import sparse_attention_long_reduce_amd as cpa
+
+from _gpu import compare, error_stats, gpu_prefill, gpu_tables, oracle_full, report, sample_rows, tiles_reached, upload
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -51,6 +53,14 @@ SMALL = {
     "all_zero_bf16": dict(prefix_len=[256], chunk_len=[128], Hq=8, Hkv=2, d=128, dtype="bf16", mask_fn=lambda rng, *a: mask_all(rng, *a, value=0)),
     "stripes_g4_f32_d128": dict(prefix_len=[1536], chunk_len=[512], Hq=8, Hkv=2, d=128, dtype="f32", mask_fn=lambda rng, *a: mask_stripes(rng, *a, p=0.1, shared_per_group=False)),
     "zero_len_chunk": dict(prefix_len=[128, 256], chunk_len=[0, 128], Hq=8, Hkv=2, d=64, dtype="bf16", mask_fn=bern(0.3)),
+    # group sizes that are not powers of two: a workgroup's four (query block, head) pairs then
+    # span two query blocks, and tiles end inside a query block's heads
+    "g3_bf16_ragged": dict(prefix_len=[0, 448], chunk_len=[200, 129], Hq=6, Hkv=2, d=128, dtype="bf16", mask_fn=bern(0.1)),
+    "g5_bf16_d64": dict(prefix_len=[320], chunk_len=[250], Hq=5, Hkv=1, d=64, dtype="bf16", mask_fn=bern(0.15)),
+    "g6_f32_d64": dict(prefix_len=[256, 0], chunk_len=[192, 70], Hq=12, Hkv=2, d=64, dtype="f32", mask_fn=bern(0.2)),
+    "g7_bf16_d128": dict(prefix_len=[640, 64], chunk_len=[300, 64], Hq=14, Hkv=2, d=128, dtype="bf16", mask_fn=bern(0.1)),
+    "g7_f32_d128": dict(prefix_len=[128], chunk_len=[190], Hq=7, Hkv=1, d=128, dtype="f32", mask_fn=bern(0.3)),
+    "g12_bf16_d64": dict(prefix_len=[192, 512], chunk_len=[128, 65], Hq=24, Hkv=2, d=64, dtype="bf16", mask_fn=bern(0.1)),
 }
 
 
@@ -126,7 +136,7 @@ def test_config1_full():
 BIG = [("c2_32k_bf16", {}), ("c3_128k_last_chunk", {}), ("c4_128k_chunked", {"chunk": 0}),
        ("c4_128k_chunked", {"chunk": 17}), ("c4_128k_chunked", {"chunk": 63}),
        ("c5a_varlen_shared", {}), ("c5b_varlen_independent", {}), ("c3_128k_last_chunk", {"dense": True}),
-       ("c3d_128k_no_noise", {})]
+       ("c3d_128k_no_noise", {}), ("c3g7_128k_gqa7", {})]
 
 
 @pytest.mark.parametrize("name,kw", BIG, ids=[f"{n}{kw}" for n, kw in BIG])
@@ -144,16 +154,46 @@ def test_full_size_configs(name, kw):
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     vmax = float(dv["vp"].abs().max())
     assert float(o.abs().max()) <= vmax * (1 + 2 ** -7)
-    # sampled rows against the oracle
+    # sampled rows against the oracle: 384 random rows plus two rows of every (sequence, KV
+    # group, query block) tile, one in each 32-row half
     S = sample_rows(w, 384, seed=1)
+    reached, total = tiles_reached(w, S)
+    assert reached == total
     Os, Ls = oracle.attention_rows(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len,
                                    w.Hkv, S)
     rows = torch.from_numpy(w.cu_q[S[:, 0]] + S[:, 2]).cuda()
     heads = torch.from_numpy(S[:, 1]).cuda()
     og = o[rows, heads].float().cpu().numpy()
     compare(w, og, Os, f"{name}{kw}")
+    report(f"sampled {name}{kw} ({len(S)} rows, {total} tiles)", error_stats(og, Os))
     lg = lse[rows, heads].cpu().numpy()
     assert np.max(np.abs(lg - Ls)) < 2e-2
+
+
+WHOLE = ["c2_32k_bf16", "c3_128k_last_chunk", "c5a_varlen_shared", "c5b_varlen_independent"]
+
+
+@pytest.mark.parametrize("name", WHOLE)
+def test_whole_output_against_oracle(name):
+    # every output element of the workload, in the layout the benchmark times (dim-major V),
+    # against the oracle; the tolerances are the bf16 bars, and the errors are reported
+    print(f"\n[case] whole output {name}", flush=True)
+    w = config(name)
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    T, C = oracle_tables(w)
+    assert np.array_equal(tables.cpu().numpy(), T) and np.array_equal(counts.cpu().numpy(), C)
+    vdim = dv["vp"].transpose(2, 3).contiguous()
+    o, lse = cpa.chunked_prefill(dv["q"], dv["kp"], vdim, dv["pm"], tables, counts, dv["cu"], dv["pl"],
+                                 w.max_chunk_len, return_lse=True, v_layout="dim")
+    torch.cuda.synchronize()
+    O, L = oracle_full(w, T, C)
+    compare(w, o, O, f"whole {name}")
+    st = error_stats(o, O)
+    lg = lse.cpu().numpy().astype(np.float64)
+    st["lse_max_abs"] = float(np.max(np.abs(lg - L.T)))
+    report(f"whole {name}", st)
+    assert st["lse_max_abs"] < 2 ** -7
 
 
 def poisoned(w, T, C, value=np.nan):
@@ -283,3 +323,33 @@ def test_sm_scale_argument():
     O, _ = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len,
                                   w.Hkv, scale=0.05)
     compare(w, o, O, "sm_scale")
+
+
+@pytest.mark.parametrize("name", ["c3_128k_last_chunk", "c5b_varlen_independent"])
+def test_prescaled_q_rounding_cost(name):
+    # The bf16 kernel multiplies Q by scale * log2(e) and rounds the product back to bf16 before
+    # the QK product (an input rounding the plain definition does not have).  Its cost: the error
+    # of the GPU against the oracle on the original Q, against the oracle on that rounded Q (what
+    # the kernel's products see), and between the two oracles, on rows reaching every tile.
+    from workloads.configs import bf16_round
+    print(f"\n[case] pre-scaled Q rounding {name}", flush=True)
+    w = config(name)
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    T, C = oracle_tables(w)
+    o, lse = gpu_prefill(dv, w, tables, counts)
+    torch.cuda.synchronize()
+    S = sample_rows(w, 384, seed=4)
+    cs32 = np.float32(np.float32(1.0) / np.sqrt(np.float32(w.d))) * np.float32(1.4426950408889634)
+    q_r = bf16_round(w.q.astype(np.float32) * cs32).astype(np.float64) / (math.log2(math.e) / math.sqrt(w.d))
+    O, _ = oracle.attention_rows(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv, S)
+    O_r, _ = oracle.attention_rows(q_r, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv, S)
+    rows = torch.from_numpy(w.cu_q[S[:, 0]] + S[:, 2]).cuda()
+    og = o[rows, torch.from_numpy(S[:, 1]).cuda()].float().cpu().numpy()
+    e_def, e_rnd, e_ora = error_stats(og, O), error_stats(og, O_r), error_stats(O_r, O)
+    report(f"q-rounding {name}: gpu vs oracle(q)", e_def)
+    report(f"q-rounding {name}: gpu vs oracle(rounded q)", e_rnd)
+    report(f"q-rounding {name}: oracle(rounded q) vs oracle(q)", e_ora)
+    compare(w, og, O, name)
+    # the rounding of Q is a small part of the bf16 budget: the oracles differ far below the bars
+    assert e_ora["max_abs"] < 2e-3 and e_ora["mean_abs"] < 2e-4
