@@ -57,14 +57,16 @@ def log(*a):
 
 
 def hardware_info(dev):
-    """The device the line was measured on, and the host CPU the oracle ran on."""
+    """The device the line was measured on (with the peak engine clock HIP reports), and the host
+    CPU the oracle ran on."""
     import torch
+    from sparse_attention_long_reduce_amd import diag
     p = torch.cuda.get_device_properties(dev)
     info = {"gpu": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
             "memory_gib": round(p.total_memory / 2**30, 1)}
-    clock = getattr(p, "clock_rate", None)
-    if clock:
-        info["max_engine_clock_mhz"] = round(clock / 1000)
+    eng_khz, wall_khz = diag.clock_rates(dev.index or 0)
+    info["max_engine_clock_mhz"] = round(eng_khz / 1000)
+    info["wall_clock_mhz"] = round(wall_khz / 1000, 3)
     try:
         with open("/proc/cpuinfo") as f:
             info["host_cpu"] = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
@@ -94,17 +96,27 @@ def read_traffic(workload_key, v_layout):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, T, C, max_seconds=15.0):
-    """The fp64 oracle (tables in full + attention on a bounded row sample) on the host cores."""
+def cpu_baseline(w, max_seconds=15.0):
+    """The fp64 oracle (tables in full + attention on a bounded row sample) on all host cores:
+    the BLAS pool is set to os.cpu_count() threads for the run (numpy's other operations run on
+    one thread); the attention leg uses the oracle's own tables."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+    host_cores = os.cpu_count() or 1
+    default_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    with threadpool_limits(limits=host_cores, user_api="blas"):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        r = _cpu_baseline_run(w, max_seconds, np, oracle)
+    r["cores"] = int(threads)
+    r["host_cores"] = int(host_cores)
+    r["blas_threads_default"] = int(default_threads)
+    return r
+
+
+def _cpu_baseline_run(w, max_seconds, np, oracle):
     t0 = time.perf_counter()
-    oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
     t_tab = time.perf_counter() - t0
     # whole query blocks of one KV group's heads, longest sequence and last blocks first
     flops = 0
@@ -129,10 +141,10 @@ def cpu_baseline(w, T, C, max_seconds=15.0):
         if done:
             break
     secs = t_tab + t_att
-    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"numpy fp64 oracle: table build for the whole batch ({t_tab:.2f} s) + attention for "
-                      f"{n_rows} query rows (whole query blocks of KV groups in order, last blocks first) of "
-                      f"sequence {b} ({t_att:.2f} s); value = selected FLOPs of those rows / wall time",
+    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "kind": "oracle",
+            "sample": f"numpy fp64 oracle: table build for the whole batch ({t_tab:.2f} s) + attention over its "
+                      f"own tables for {n_rows} query rows (whole query blocks of KV groups in order, last blocks "
+                      f"first) of sequence {b} ({t_att:.2f} s); value = selected FLOPs of those rows / wall time",
             "seconds": round(secs, 3)}
 
 
@@ -247,8 +259,11 @@ def timed(cpa, batches, modes, steps, warmup):
         build = np.array([[e[0].elapsed_time(e[1]) for e in ev[s][m]] for s in range(steps)])   # ms
         pre = np.array([[e[1].elapsed_time(e[2]) for e in ev[s][m]] for s in range(steps)])
         step = np.array([ev[s][m][0][0].elapsed_time(ev[s][m][-1][2]) for s in range(steps)])
-        out.append({"step_ms": float(step.mean()), "build_ms": float(build.sum(1).mean()),
+        out.append({"step_ms": float(step.mean()), "step_ms_median": float(np.median(step)),
+                    "step_ms_min": float(step.min()), "build_ms": float(build.sum(1).mean()),
+                    "build_ms_median": float(np.median(build.sum(1))), "build_ms_min": float(build.sum(1).min()),
                     "prefill_ms": float(pre.sum(1).mean()), "prefill_ms_median": float(np.median(pre.sum(1))),
+                    "prefill_ms_min": float(pre.sum(1).min()),
                     "prefill_launch_ms": float(pre.mean()), "launches_per_step": nb})
     return out
 
@@ -461,6 +476,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a device-to-device copy of 1 GiB three times (the reference "
                          "kernel that scales the HBM byte counters)")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="only run the bf16 MFMA-loop probe (cpa_diag_mfma_loop) and print its rate and the "
+                         "engine clock it ran at")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: every figure it reports is one GPU's (the path shards "
@@ -480,6 +498,19 @@ def main():
         return
 
     import sparse_attention_long_reduce_amd as cpa
+    from sparse_attention_long_reduce_amd import diag
+
+    if args.mfma_peak:
+        dev = torch.device("cuda:0")
+        out = {}
+        for threads in (256, 512):
+            r = diag.mfma_peak(dev, threads=threads)
+            out[f"waves_per_simd_{threads // 256}"] = {k: (round(v, 3) if isinstance(v, float) else v)
+                                                        for k, v in r.items()}
+        out["published_peak_tflops"] = MFMA_BF16_PEAK_TFLOPS
+        out["hardware"] = hardware_info(dev)
+        print(json.dumps(out), flush=True)
+        return
 
     name, desc = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -586,6 +617,13 @@ def main():
         "prefill_tflops": round(pre_tflops, 2),
         "prefill_ms": round(r["prefill_ms"], 4),
         "table_build_us": round(r["build_ms"] * 1e3, 2),
+        "timing_stats_ms": {"step": {"mean": round(r["step_ms"], 4), "median": round(r["step_ms_median"], 4),
+                                     "min": round(r["step_ms_min"], 4)},
+                            "prefill": {"mean": round(r["prefill_ms"], 4), "median": round(r["prefill_ms_median"], 4),
+                                        "min": round(r["prefill_ms_min"], 4)},
+                            "table_build": {"mean": round(r["build_ms"], 5), "median": round(r["build_ms_median"], 5),
+                                            "min": round(r["build_ms_min"], 5)},
+                            "note": f"over {args.steps} timed steps; value and roofline use the mean"},
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": read_traffic(args.workload, args.v_layout),
@@ -619,12 +657,21 @@ def main():
                               "unsplit_prefill_ms": round(unsplit["prefill_ms"], 4),
                               "speedup_over_unsplit": round(unsplit["prefill_ms"] / r["prefill_ms"], 4)}
     result["hardware"] = hardware_info(torch.device("cuda", 0))
+    # the measured MFMA ceiling of this device: a loop of independent bf16 MFMAs, two waves per SIMD
+    mp = diag.mfma_peak(torch.device("cuda", 0))
+    result["roofline"]["measured_peak"] = {
+        "achieved_tflops": round(mp["tflops"], 1), "engine_clock_mhz": round(mp["engine_clock_mhz"]),
+        "frac_of_published": round(mp["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+        "prefill_frac_of_measured": round(pre_tflops / mp["tflops"], 4),
+        "note": "cpa_diag_mfma_loop: 4 independent v_mfma_f32_32x32x16_bf16 chains per wave, two waves per SIMD, "
+                "one workgroup per CU, no memory traffic; clock = shader cycles / wall-clock ticks of workgroup 0"}
+    result["hardware"]["engine_clock_mhz_mfma_loop"] = round(mp["engine_clock_mhz"])
     result["pages_context"] = ("CompactAttention reports up to 2.72x attention speedup at 128K on "
                                "LLaMA-3.1-8B-Instruct (hardware not stated); context only")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         bt = batches[-1]
-        result["cpu_baseline"] = cpu_baseline(bt.w, bt.tables.cpu().numpy(), bt.counts.cpu().numpy())
+        result["cpu_baseline"] = cpu_baseline(bt.w)
     print(json.dumps(result), flush=True)
 
 

@@ -7,8 +7,8 @@ LIB_PATH = os.path.join(_HERE, "libcpa.so")
 
 EXPORTS = ("cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables", "cpa_build_block_tables_bits",
            "cpa_chunked_prefill", "cpa_chunked_prefill_direct", "cpa_chunked_prefill_fp8kv",
-           "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string",
-           "cpa_version")
+           "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes",
+           "cpa_status_string", "cpa_version")
 
 _lib = None
 
@@ -57,6 +57,29 @@ def load():
     lib.cpa_version.restype = i32
     lib.cpa_version.argtypes = []
     _lib = lib
+    return lib
+
+
+DIAG_LIB_PATH = os.path.join(_HERE, "libcpa_diag.so")
+DIAG_EXPORTS = ("cpa_diag_clock_rates", "cpa_diag_mfma_loop")
+_diag = None
+
+
+def load_diag():
+    """Load libcpa_diag.so (the measurement helpers of include/cpa_diag.h) once."""
+    global _diag
+    if _diag is not None:
+        return _diag
+    if not os.path.exists(DIAG_LIB_PATH):
+        raise RuntimeError(f"{DIAG_LIB_PATH} is missing: build it with "
+                           "`python -m sparse_attention_long_reduce_amd.build` first")
+    lib = ctypes.CDLL(DIAG_LIB_PATH)
+    c = ctypes
+    lib.cpa_diag_mfma_loop.restype = c.c_int
+    lib.cpa_diag_mfma_loop.argtypes = [c.c_int, c.c_int, c.c_int, c.c_void_p, c.c_void_p, c.c_void_p]
+    lib.cpa_diag_clock_rates.restype = c.c_int
+    lib.cpa_diag_clock_rates.argtypes = [c.c_int, c.POINTER(c.c_int), c.POINTER(c.c_int)]
+    _diag = lib
     return lib
 
 

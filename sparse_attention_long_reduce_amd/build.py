@@ -9,6 +9,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libcpa.so")
+DIAG_LIB_PATH = os.path.join(PKG, "libcpa_diag.so")
+DIAG_SOURCES = ("diag_mfma.hip",)   # measurement helpers (include/cpa_diag.h), a library of their own
 SOURCES = ("block_union.hip", "block_plans.hip", "prefill_regstaged.hip", "prefill_bf16.hip", "prefill_direct.hip",
            "kv_append.hip", "cpa_api.hip")
 ARCH = os.environ.get("CPA_OFFLOAD_ARCH", "gfx950")
@@ -35,21 +37,23 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libcpa.so; always recompiles.  Returns the library path."""
+    """Compile every source and link libcpa.so (and the measurement helpers' libcpa_diag.so);
+    always recompiles.  Returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
     cmds = []
-    for src in SOURCES:
+    for src in SOURCES + DIAG_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out, file=sys.stderr)
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    for path, o in ((LIB_PATH, objs[:len(SOURCES)]), (DIAG_LIB_PATH, objs[len(SOURCES):])):
+        tmp = path + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *o])
+        os.replace(tmp, path)
     return LIB_PATH
 
 

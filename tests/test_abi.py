@@ -9,13 +9,20 @@ import pytest
 import sparse_attention_long_reduce_amd as cpa
 from sparse_attention_long_reduce_amd import _lib
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cpa.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "cpa.h")
+DIAG_HEADER = os.path.join(INCLUDE, "cpa_diag.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(cpa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_header_is_covered():
+    # each header under include/ is checked against a library below
+    assert sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h")) == ["cpa.h", "cpa_diag.h"]
 
 
 @pytest.fixture(scope="module")
@@ -34,6 +41,38 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
+
+
+@pytest.fixture(scope="module")
+def diag():
+    if not os.path.exists(_lib.DIAG_LIB_PATH):
+        pytest.fail("libcpa_diag.so is not built (run __graft_entry__.build())")
+    return _lib.load_diag()
+
+
+def test_diag_exports_every_declared_symbol(diag):
+    names = declared_functions(DIAG_HEADER)
+    assert set(names) == {"cpa_diag_mfma_loop", "cpa_diag_clock_rates"}
+    for n in names:
+        assert hasattr(diag, n), n
+    assert set(_lib.DIAG_EXPORTS) == set(names)
+
+
+def test_diag_validation(diag):
+    import ctypes
+    ml = diag.cpa_diag_mfma_loop
+    assert ml(0, 512, 10, FAKE, FAKE, None) == 2
+    assert ml(1, 32, 10, FAKE, FAKE, None) == 2
+    assert ml(1, 576, 10, FAKE, FAKE, None) == 2
+    assert ml(1, 100, 10, FAKE, FAKE, None) == 2
+    assert ml(1, 512, 0, FAKE, FAKE, None) == 2
+    assert ml(1, 512, 10 ** 7 + 1, FAKE, FAKE, None) == 2
+    assert ml(1, 512, 10, None, FAKE, None) == 1
+    assert ml(1, 512, 10, FAKE, None, None) == 1
+    assert ml(1, 512, 10, FAKE, FAKE + 4, None) == 3
+    x = ctypes.c_int(0)
+    assert diag.cpa_diag_clock_rates(0, None, ctypes.byref(x)) == 1
+    assert diag.cpa_diag_clock_rates(0, ctypes.byref(x), None) == 1
 
 
 def test_status_strings(lib):
@@ -92,9 +131,7 @@ def test_prefill_validation(lib):
     assert pf(lib, d=96) == 4
     assert pf(lib, d=256) == 4
     assert pf(lib, dtype=7) == 4
-    assert pf(lib, Hq=24, Hkv=8) == 4  # G = 3
-    assert pf(lib, Hq=30, Hkv=8) == 2
-    assert pf(lib, Hq=36, Hkv=1) == 4  # G=36 > 32
+    assert pf(lib, Hq=30, Hkv=8) == 2  # Hq % Hkv != 0
     assert pf(lib, scale=-1.0) == 2
     assert pf(lib, scale=float("nan")) == 2
     assert pf(lib, scale=float("inf")) == 2
@@ -111,6 +148,12 @@ def test_prefill_validation(lib):
     assert pf(lib, ts=132, hs=64 * 132, ps=8 * 64 * 132) == 3    # bf16 row of 264 B
     assert pf(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
     assert pf(lib, mcl=0, q=NULL) == 0
+    # an empty pool with work to do: idle copy slots stage page 0, so it is refused
+    assert pf(lib, npages=0) == 2
+    assert pf(lib, npages=-1) == 2
+    assert pf(lib, npages=0, B=0) == 0
+    assert pfv(lib, npages=0) == 2
+    assert pfs(lib, npages=0) == 2
 
 
 def pfs(lib, dtype=1, total_q=256, split=4, ws=FAKE, ws_bytes=1 << 30, **kw):
@@ -257,6 +300,11 @@ def test_fp8kv_validation(lib):
     assert pf8(lib, q=NULL) == 1
     assert pf8(lib, k=FAKE + 8) == 3
     assert pf8(lib, vdm=1, vrs=63, vhs=128 * 64, vps=8 * 128 * 64) == 2
+    # fp8 strides are bytes: rows, heads and pages must start on 16-byte boundaries
+    assert pf8(lib, ts=136, hs=64 * 136, ps=8 * 64 * 136) == 3
+    assert pf8(lib, vdm=1, vrs=72, vhs=128 * 72, vps=8 * 128 * 72) == 3
+    assert pf8(lib, vrs=136, vhs=64 * 136, vps=8 * 64 * 136) == 3
+    assert pf8(lib, npages=0) == 2               # a call with work needs a non-empty pool
     assert pf8(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
 
 
@@ -267,9 +315,12 @@ def test_split_planner():
     # the whole layer (32 heads, 8 groups) already has a tile per CU
     assert cpa.prefill_tiles(1, 32, 8, 2048) == 256
     assert cpa.plan_split_pages(1, 32, 8, 2048, 2048, 256) == 0
-    # G = 1 packs 4 query blocks, G = 8 splits the heads in two
+    # G = 1 packs 4 query blocks, G = 8 splits the heads in two, G = 3 / 7 tiles span query blocks
     assert cpa.prefill_tiles(2, 8, 8, 300) == 2 * 8 * 2 * 1
     assert cpa.prefill_tiles(1, 16, 2, 128) == 1 * 2 * 2 * 2
+    assert cpa.prefill_tiles(1, 24, 8, 2048) == 8 * 24          # 32 query blocks x 3 heads / 4
+    assert cpa.prefill_tiles(1, 28, 4, 2048) == 4 * 56          # 32 x 7 / 4
+    assert cpa.prefill_tiles(1, 5, 1, 100) == 3                 # 2 query blocks x 5 heads -> 10 pairs
     assert cpa.plan_split_pages(1, 4, 1, 64, 1, 256) == 0
 
 
