@@ -191,6 +191,35 @@ cpa_status cpa_chunked_prefill_split(const void* q, cpa_dtype dtype, const void*
                                      int total_q, int split_pages, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * cpa_chunked_prefill_split_static - cpa_chunked_prefill_split with no workspace argument and no
+ * allocation of any kind, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The split partials live in a
+ * device array inside the library, CPA_STATIC_SCRATCH_BYTES (64 MiB) large, that every GPU the
+ * library runs on holds from the first call on that GPU until the process ends; its address on
+ * a device is looked up on that first call (the stream's device, or the current one for the
+ * default stream).  Same attention, kernels and results as cpa_chunked_prefill_split.
+ *
+ * Arguments as cpa_chunked_prefill_split without workspace / workspace_bytes.  The caller still
+ * passes q, the pools, tables and the outputs.
+ * Errors: those of cpa_chunked_prefill_split; CPA_ERR_CAPACITY when
+ * cpa_split_workspace_bytes(total_q, Hq, d, table_cap, split_pages) exceeds
+ * CPA_STATIC_SCRATCH_BYTES (checked before any HIP call); CPA_ERR_LAUNCH when the array's
+ * device address cannot be obtained.  Every call on one GPU shares that GPU's array and it keeps
+ * the last call's contents (nothing in it needs to start at zero: every partial the merge reads
+ * is written first by the same call), so calls that overlap in time on one GPU (different
+ * streams, or threads) race and must be serialised by the caller.
+ */
+#define CPA_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
+cpa_status cpa_chunked_prefill_split_static(const void* q, cpa_dtype dtype, const void* k_pages,
+                                            const void* v_pages, int64_t page_stride, int64_t head_stride,
+                                            int64_t token_stride, int64_t n_pages, const int32_t* page_map,
+                                            int page_map_stride, const int32_t* tables, int table_cap,
+                                            const int32_t* counts, const int32_t* cu_q,
+                                            const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                                            int max_chunk_len, float sm_scale, void* o, float* lse,
+                                            int total_q, int split_pages, hipStream_t stream);
+
 /* Bytes of workspace cpa_chunked_prefill_split needs (0 when it needs none, or for
  * non-positive arguments): ceil(table_cap / split_pages) * total_q * Hq * (d + 1) * 4 when
  * that split count exceeds 1. */

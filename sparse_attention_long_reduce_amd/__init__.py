@@ -27,6 +27,7 @@ from .api import (  # noqa: F401
     build_block_tables_bits,
     chunked_prefill,
     chunked_prefill_direct,
+    chunked_prefill_split_static,
     plan_flops,
     plan_split_pages,
     prefill_tiles,

@@ -359,6 +359,48 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
         return out, lse
 
 
+STATIC_SCRATCH_BYTES = 64 * 1024 * 1024   # CPA_STATIC_SCRATCH_BYTES
+
+
+def chunked_prefill_split_static(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len,
+                                 split_pages, sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None):
+    """Split-KV attention (token-major V pools, bf16) whose partials live in the library's own
+    per-device array instead of a workspace (cpa_chunked_prefill_split_static): the call
+    allocates nothing when out (and lse, if wanted) are given.  Same results as
+    chunked_prefill(..., split_pages=split_pages)."""
+    if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("the split path runs bf16 q, k_pages and v_pages")
+    if q.dim() != 3 or not q.is_contiguous():
+        raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
+    Tq, Hq, d = q.shape
+    if k_pages.dim() != 4 or k_pages.shape[2] != BLOCK or k_pages.shape[3] != d or k_pages.stride(3) != 1:
+        raise ValueError("k_pages must be [n_pages][Hkv][64][d] with d contiguous")
+    if v_pages.shape != k_pages.shape or v_pages.stride() != k_pages.stride():
+        raise ValueError("v_pages must match k_pages in shape and strides")
+    n_pages, Hkv = k_pages.shape[0], k_pages.shape[1]
+    for t, nm in ((page_map, "page_map"), (tables, "tables"), (counts, "counts"), (cu_q, "cu_q"),
+                  (prefix_len, "prefix_len")):
+        _i32(t, nm)
+    B = prefix_len.numel()
+    if cu_q.numel() != B + 1 or counts.numel() != B * Hkv or page_map.dim() != 2 or page_map.shape[0] != B:
+        raise ValueError("inconsistent B across cu_q / prefix_len / counts / page_map")
+    if tables.dim() != 3 or tables.shape[0] != B or tables.shape[1] != Hkv:
+        raise ValueError("tables must be [B][Hkv][cap] (B sequences, Hkv KV groups)")
+    cap = tables.shape[2]
+    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, tables=tables,
+              counts=counts, cu_q=cu_q, prefix_len=prefix_len)
+    out, lse = _out_buffers(out, lse, return_lse, q, dev)
+    with torch.cuda.device(dev):
+        st = load().cpa_chunked_prefill_split_static(
+            _ptr(q), BF16, _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
+            n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
+            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq,
+            int(split_pages), _stream(stream, dev))
+    if st != 0:
+        raise CpaError(st, "cpa_chunked_prefill_split_static")
+    return out, lse
+
+
 def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len, v_layout="token",
               stream=None):
     """Write each sequence's chunk rows k_new / v_new [Tq][Hkv][d] into their slots of the paged

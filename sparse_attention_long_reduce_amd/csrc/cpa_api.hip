@@ -4,6 +4,7 @@
 
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 namespace {
 
@@ -390,3 +391,65 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
 
 }  // extern "C"
 
+// ---- split-KV without a caller workspace ---------------------------------------------------
+// cpa_chunked_prefill_split_static keeps the split partials in `scratch`, a device array of
+// CPA_STATIC_SCRATCH_BYTES that every GPU the library runs on holds until the process ends.  In
+// host code the array's name is only a host-side handle, never a device address: its address
+// on a device is looked up once per device, with that device current, and only that address
+// is handed to the kernels.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[CPA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `device`'s copy of scratch (nullptr if the lookup fails).
+void* scratch_address(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[device] == nullptr) {
+    int current = -1;
+    if (hipGetDevice(&current) != hipSuccess) return nullptr;
+    if (current != device && hipSetDevice(device) != hipSuccess) return nullptr;
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    const hipError_t r = current != device ? hipSetDevice(current) : hipSuccess;   // restore the caller's device
+    if (e != hipSuccess || r != hipSuccess || addr == nullptr) return nullptr;
+    g_scratch_addr[device] = addr;
+  }
+  return g_scratch_addr[device];
+}
+
+}  // namespace
+
+extern "C" cpa_status cpa_chunked_prefill_split_static(
+    const void* q, cpa_dtype dtype, const void* k_pages, const void* v_pages, int64_t page_stride,
+    int64_t head_stride, int64_t token_stride, int64_t n_pages, const int32_t* page_map, int page_map_stride,
+    const int32_t* tables, int table_cap, const int32_t* counts, const int32_t* cu_q, const int32_t* prefix_len,
+    int B, int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse, int total_q,
+    int split_pages, hipStream_t stream) {
+  if (split_pages <= 0 || total_q < 0) return CPA_ERR_SHAPE;
+  // the partials must fit the array; checked before anything touches the device
+  if (cpa_split_workspace_bytes(total_q, Hq, d, table_cap, split_pages) > (size_t)CPA_STATIC_SCRATCH_BYTES)
+    return CPA_ERR_CAPACITY;
+  const VLayout vl{page_stride, head_stride, token_stride, false};
+  cpa::PrefillArgs a;
+  bool nothing;
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
+                                        n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
+                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
+  if (st != CPA_OK || nothing) return st;
+  int device = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &device) != hipSuccess) return CPA_ERR_LAUNCH;
+  } else if (hipGetDevice(&device) != hipSuccess) {
+    return CPA_ERR_LAUNCH;
+  }
+  void* ws = scratch_address(device);
+  if (ws == nullptr) return CPA_ERR_LAUNCH;
+  return prefill_split(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl, n_pages, page_map,
+                       page_map_stride, tables, table_cap, counts, cu_q, prefix_len, B, Hq, Hkv, d, max_chunk_len,
+                       sm_scale, o, lse, total_q, split_pages, ws, (size_t)CPA_STATIC_SCRATCH_BYTES, stream);
+}

@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables",
                           "cpa_build_block_tables_bits", "cpa_chunked_prefill", "cpa_chunked_prefill_direct",
-                          "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_split", "cpa_chunked_prefill_vt",
-                          "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
+                          "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_split", "cpa_chunked_prefill_split_static",
+                          "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(_lib.EXPORTS) == set(names)
@@ -182,6 +182,33 @@ def test_split_validation(lib):
     assert pfs(lib, B=0, q=NULL) == 0
     assert lib.cpa_split_workspace_bytes(256, 32, 128, 16, 16) == 0   # one range: no workspace
     assert lib.cpa_split_workspace_bytes(0, 32, 128, 16, 4) == 0
+
+
+def pss(lib, dtype=1, total_q=256, split=4, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
+             tab=FAKE, cap=16, cnt=FAKE, cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0,
+             o=FAKE, lse=NULL)
+    a.update(kw)
+    return lib.cpa_chunked_prefill_split_static(a["q"], dtype, a["k"], a["v"], a["ps"], a["hs"], a["ts"],
+                                                a["npages"], a["pm"], a["pms"], a["tab"], a["cap"], a["cnt"], a["cu"],
+                                                a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["mcl"], a["scale"],
+                                                a["o"], a["lse"], total_q, split, None)
+
+
+def test_split_static_validation(lib):
+    # every refusal below happens on the host before the scratch array is looked up
+    limit = 64 * 1024 * 1024
+    assert pss(lib, split=0) == 2
+    assert pss(lib, total_q=-1) == 2
+    # 4 ranges x total_q x 32 heads x 129 floats: 1016 rows fit in 64 MiB, 1017 do not
+    assert lib.cpa_split_workspace_bytes(1016, 32, 128, 16, 4) <= limit
+    assert lib.cpa_split_workspace_bytes(1017, 32, 128, 16, 4) > limit
+    assert pss(lib, total_q=1017) == 5
+    assert pss(lib, total_q=1 << 20, split=1) == 5
+    assert pss(lib, d=96) == 4
+    assert pss(lib, q=NULL) == 1
+    assert pss(lib, npages=0) == 2
+    assert pss(lib, B=0, q=NULL) == 0
 
 
 def pfv(lib, dtype=1, total_q=256, split=0, ws=NULL, ws_bytes=0, vps=8 * 128 * 64, vhs=128 * 64, vds=64, **kw):
