@@ -8,7 +8,8 @@
 // One workgroup of 1024 threads per (sequence, KV group).
 //   phase 1  OR-reduce the group's G * nqb mask rows, 16 KV blocks (one 16-byte load) per
 //            thread and row, four rows' loads in flight per thread, with the causal clip
-//            kb <= prefix_blocks + qi applied per row;
+//            kb <= prefix_blocks + qi applied per row; a thread walks its rows (head, query
+//            block) by stepping, with no division per row;
 //            partial ORs of threads that share a column meet in LDS (a tree over the row
 //            splits); each 16-block column becomes 16 bits of a 64-bit word in LDS.
 //            Bit-packed masks (one bit per KV block, 64 blocks per 8-byte word) are
@@ -43,6 +44,63 @@ __device__ __forceinline__ uint32_t bytes_to_bits(const uint32_t v[4]) {
     bits |= ((t >> 31) & 1u) << (4 * w + 3);
   }
   return bits;
+}
+
+// Phase 2 for one (sequence, KV group), called by every thread of the workgroup: the
+// group's nwords 64-bit words (in LDS) -> ascending ids of their set bits at tab[0 .. total),
+// -1 up to table_cap, and *count = total.  Popcount per word, an exclusive scan over words
+// (within waves by shuffles, then over the wave totals), then each wave expands words: lane l
+// of the wave owning word w writes 64w + l at (the word's offset + its mbcnt rank) when bit l
+// is set.  wpre [MAX_WORDS] and tsum [2 * UT / 64] are LDS scratch.
+__device__ __forceinline__ void expand_words(const unsigned long long* words, int nwords, int32_t* tab,
+                                             int table_cap, int32_t* count, int* wpre, int* tsum) {
+  const int tid = threadIdx.x;
+  constexpr int WPT = MAX_WORDS / UT;  // words per thread in the scan
+  int pc[WPT];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int w = tid * WPT + k;
+    pc[k] = (w < nwords) ? __popcll(words[w]) : 0;
+    mine += pc[k];
+  }
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) tsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int v = lane < UT / 64 ? tsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < UT / 64; off <<= 1) {
+      const int y = __shfl_up(v, off);
+      if (lane >= off) v += y;
+    }
+    if (lane < UT / 64) tsum[UT / 64 + lane] = v;   // inclusive wave prefixes
+  }
+  __syncthreads();
+  int run = (wave > 0 ? tsum[UT / 64 + wave - 1] : 0) + incl - mine;
+#pragma unroll
+  for (int k = 0; k < WPT; ++k) {
+    const int w = tid * WPT + k;
+    if (w < nwords) wpre[w] = run;
+    run += pc[k];
+  }
+  const int total = tsum[UT / 64 + UT / 64 - 1];
+  __syncthreads();
+  for (int w = wave; w < nwords; w += UT / 64) {
+    const unsigned long long word = words[w];
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0u));
+    if ((word >> lane) & 1ull) tab[wpre[w] + (int)rank] = (w << 6) + lane;
+  }
+  for (int i = total + tid; i < table_cap; i += UT) tab[i] = -1;
+  if (tid == 0) *count = total;
 }
 
 // VEC: byte masks read 16 bytes at a time; BITS: bit-packed masks (a.mask_bits)
@@ -88,22 +146,29 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
       if (c < nwords) {
         const int kb0 = c << 6;
         const int qi_lo = max(0, kb0 - qb0);
-        const int nq = nqb - qi_lo;
+        const int nq = nqb - qi_lo;   // >= 1: c < nwords
         const int nrows = G * nq;
-        auto row = [&](int t) __attribute__((always_inline)) {
-          const int hh = t / nq;
-          const int qi = qi_lo + (t - hh * nq);
-          unsigned long long v = wbase[((size_t)hh * a.nqb_max + qi) * wstride + c];
-          const int nallow = qb0 + qi - kb0 + 1;   // bits 0 .. nallow-1 are causally reachable
-          if (nallow < 64) v &= (1ull << nallow) - 1ull;   // nallow >= 1 here (qi >= qi_lo)
-          return v;
-        };
+        // row t = (head hh, query block qi_lo + qr), walked from t = s in steps of rs rows
+        // without a division per row
+        int hh = s / nq, qr = s - (s / nq) * nq;
+        const int dh = rs / nq, dq = rs - (rs / nq) * nq;
         for (int t0 = s; t0 < nrows; t0 += 4 * rs) {
           unsigned long long v[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int t = t0 + u * rs;
-            v[u] = t < nrows ? row(t) : 0ull;
+            v[u] = 0ull;
+            if (t0 + u * rs < nrows) {
+              const int qi = qi_lo + qr;
+              v[u] = wbase[((size_t)hh * a.nqb_max + qi) * wstride + c];
+              const int nallow = qb0 + qi - kb0 + 1;   // bits 0 .. nallow-1 are causally reachable (>= 1)
+              if (nallow < 64) v[u] &= (1ull << nallow) - 1ull;
+            }
+            qr += dq;
+            hh += dh;
+            if (qr >= nq) {
+              qr -= nq;
+              ++hh;
+            }
           }
           acc |= (v[0] | v[1]) | (v[2] | v[3]);
         }
@@ -134,11 +199,8 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
       const int kb0 = c << 4;
       const int qi_lo = max(0, kb0 - qb0);  // first query block that can reach column kb0
       const int nq = nqb - qi_lo;
-      // mask bytes of row t (head t / nq of the group, query block qi_lo + t % nq) at column
-      // kb0, causally clipped
-      auto row = [&](int t, uint32_t v[4]) __attribute__((always_inline)) {
-        const int hh = t / nq;
-        const int qi = qi_lo + (t - hh * nq);
+      // mask bytes of row (head hh of the group, query block qi) at column kb0, causally clipped
+      auto row = [&](int hh, int qi, uint32_t v[4]) __attribute__((always_inline)) {
         const uint8_t* rowp = gbase + ((size_t)hh * a.nqb_max + qi) * row_stride + kb0;
         if (VEC) {
           const uint4 x = *reinterpret_cast<const uint4*>(rowp);
@@ -167,15 +229,24 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
         }
       };
       const int nrows = G * nq;
+      // row t = (head hh, query block qi_lo + qr), walked from t = s in steps of rsplit rows
+      // without a division per row
+      int hh = s / nq, qr = s - (s / nq) * nq;
+      const int dh = rsplit / nq, dq = rsplit - (rsplit / nq) * nq;
       for (int t0 = s; t0 < nrows; t0 += 4 * rsplit) {
         uint32_t v[4][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int t = t0 + u * rsplit;
-          if (t < nrows) {
-            row(t, v[u]);
+          if (t0 + u * rsplit < nrows) {
+            row(hh, qi_lo + qr, v[u]);
           } else {
             v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0u;
+          }
+          qr += dq;
+          hh += dh;
+          if (qr >= nq) {
+            qr -= nq;
+            ++hh;
           }
         }
 #pragma unroll
@@ -202,69 +273,21 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
     __syncthreads();
   }
 
-  // ---- phase 2: popcount, exclusive scan over words, expansion ----------------------------
-  constexpr int WPT = MAX_WORDS / UT;  // words per thread in the scan
-  int pc[WPT];
-  int mine = 0;
-#pragma unroll
-  for (int k = 0; k < WPT; ++k) {
-    const int w = tid * WPT + k;
-    pc[k] = (w < nwords) ? __popcll(words[w]) : 0;
-    mine += pc[k];
-  }
-  // exclusive scan of the per-thread sums: inclusive scan within each wave, then over the
-  // 16 wave totals in wave 0
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) tsum[wave] = incl;
-  __syncthreads();
-  if (wave == 0) {
-    int v = lane < UT / 64 ? tsum[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < UT / 64; off <<= 1) {
-      const int y = __shfl_up(v, off);
-      if (lane >= off) v += y;
-    }
-    if (lane < UT / 64) tsum[UT / 64 + lane] = v;   // inclusive wave prefixes
-  }
-  __syncthreads();
-  int run = (wave > 0 ? tsum[UT / 64 + wave - 1] : 0) + incl - mine;
-#pragma unroll
-  for (int k = 0; k < WPT; ++k) {
-    const int w = tid * WPT + k;
-    if (w < nwords) wpre[w] = run;
-    run += pc[k];
-  }
-  const int total = tsum[UT / 64 + UT / 64 - 1];
-  __syncthreads();
-
-  int32_t* tab = a.tables + ((size_t)b * a.Hkv + g) * a.table_cap;
-  for (int w = wave; w < nwords; w += UT / 64) {
-    const unsigned long long word = words[w];
-    const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
-                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0u));
-    if ((word >> lane) & 1ull) tab[wpre[w] + (int)rank] = (w << 6) + lane;
-  }
-  for (int i = total + tid; i < a.table_cap; i += UT) tab[i] = -1;
-  if (tid == 0) a.counts[(size_t)b * a.Hkv + g] = total;
+  // ---- phase 2 ------------------------------------------------------------------------------
+  expand_words(words, nwords, a.tables + ((size_t)b * a.Hkv + g) * a.table_cap, a.table_cap,
+               a.counts + (size_t)b * a.Hkv + g, wpre, tsum);
 }
 
 }  // namespace
 
 hipError_t launch_block_union(const UnionArgs& a, hipStream_t s) {
   if (a.B == 0 || a.Hkv == 0) return hipSuccess;
+  const bool vec = (a.nkvb_max % 16 == 0) && ((uintptr_t)a.masks % 16 == 0);
   dim3 grid((unsigned)(a.B * a.Hkv)), block(UT);
   if (a.use_bits) {
     hipLaunchKernelGGL((block_union_kernel<false, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  const bool vec = (a.nkvb_max % 16 == 0) && ((uintptr_t)a.masks % 16 == 0);
   if (vec)
     hipLaunchKernelGGL((block_union_kernel<true, false>), grid, block, 0, s, a);
   else

@@ -99,6 +99,35 @@ def test_small_tables_and_prefill(name):
         assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("cap_extra", [0, 1, 7])
+def test_tables_one_block_sequences(cap_extra):
+    # one KV block per sequence, at the minimum capacity and above it
+    w = make_workload("one_block", [0, 0, 0], [40, 64, 1], 8, 2, 64, "bf16", bern(0.5), 6)
+    assert w.nkvb_max == 1
+    dv = upload(w)
+    cap = 1 + cap_extra
+    tables, counts = gpu_tables(dv, w, cap)
+    T, C = oracle_tables(w, cap)
+    assert np.array_equal(tables.cpu().numpy(), T) and np.array_equal(counts.cpu().numpy(), C)
+
+
+@pytest.mark.parametrize("nkvb", [3, 63, 64, 65, 129])
+def test_tables_word_boundaries(nkvb):
+    # extents around the 64-block words of the build's bitsets and 16-block load columns, at the
+    # minimum capacity, from bytes and from bit-packed masks
+    w = make_workload(f"w{nkvb}", [64 * (nkvb - 2)], [128], 8, 2, 64, "bf16", bern(0.3), nkvb,
+                      noncausal_noise=0.2)
+    assert w.nkvb_max == nkvb
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    T, C = oracle_tables(w)
+    assert np.array_equal(tables.cpu().numpy(), T) and np.array_equal(counts.cpu().numpy(), C)
+    from workloads.configs import pack_mask_bits
+    bits = torch.from_numpy(pack_mask_bits(w.masks).view(np.int64)).cuda()
+    t2, c2 = cpa.build_block_tables_bits(bits, w.nkvb_max, dv["pb"], dv["cb"], w.Hkv)
+    assert np.array_equal(t2.cpu().numpy(), T) and np.array_equal(c2.cpu().numpy(), C)
+
+
 def test_tables_unaligned_mask_width():
     # nkvb_max = 70 is not a multiple of 16: the byte path of the union kernel
     w = make_workload("w70", [64 * 66], [256], 8, 2, 64, "bf16", bern(0.03), 5, noncausal_noise=0.2)
