@@ -1,8 +1,8 @@
 """Seeded sweep of the whole path over random shapes within the documented limits.
 
 Each case draws a batch (1-4 sequences, prefixes of 0-40 blocks, chunks of 0-400 tokens, so
-ragged query tiles, partial last pages and empty chunks occur), a group size the attention
-kernels take (1, 2, 4, 8, 12, 16) with 1-3 KV groups, d 64 or 128, a mask density from empty to
+ragged query tiles, partial last pages and empty chunks occur), a group size (1, 2, 4, 8, 12, 16;
+a second draw takes any size 1-16) with 1-3 KV groups, d 64 or 128, a mask density from empty to
 full, and one way to run attention: bf16, fp32 or fp8 pools, token- or dim-major V, split-KV or
 not.  It then runs the path as a caller would, against the oracle at every step:
 
@@ -68,11 +68,34 @@ def fp8_codes(x, scale):
 def test_sweep(i):
     c = draw(i)
     print(f"\n[case] sweep {i}: {c}", flush=True)
+    run_case(i, c, 7100 + i, 7200 + i)
+
+
+N_ANY_G = int(os.environ.get("CPA_SWEEP_ANY_G_CASES", "16"))
+
+
+def draw_any_group(i):
+    # the same draw with any group size 1-16 (3, 5, 6, 7, 9, ... included)
+    c = draw(i)
+    rng = np.random.default_rng(7800 + i)
+    c["G"] = int(rng.integers(1, 17))
+    c["Hkv"] = int(rng.integers(1, 4))
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_ANY_G))
+def test_sweep_any_group(i):
+    c = draw_any_group(i)
+    print(f"\n[case] any-group sweep {i}: {c}", flush=True)
+    run_case(i, c, 7900 + i, 8000 + i)
+
+
+def run_case(i, c, wseed, rseed):
     Hq, Hkv, d, mode = c["G"] * c["Hkv"], c["Hkv"], c["d"], c["mode"]
     w = make_workload(f"sweep{i}", c["prefix"], c["chunk"], Hq, Hkv, d, "f32" if mode == "f32" else "bf16",
-                      mask_fn(c), 7100 + i)
+                      mask_fn(c), wseed)
     dv = upload(w)
-    rng = np.random.default_rng(7200 + i)
+    rng = np.random.default_rng(rseed)
     new = rng.standard_normal((2, w.q.shape[0], Hkv, d), dtype=np.float32)
     if mode == "fp8":
         ks, vs = c["scales"]
