@@ -258,6 +258,44 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
                                   hipStream_t stream);
 
 /*
+ * cpa_chunked_prefill_fused - cpa_build_block_tables and cpa_chunked_prefill(_vt) in one launch:
+ * the block union moves into the prefill's prologue.  Each workgroup ORs the masks of its KV
+ * group itself (the Q-block union and the intra-group union of the CompactAttention abstract,
+ * with the causal clip of cpa_build_block_tables) into a bitmap in LDS and walks the blocks it
+ * selects in ascending order.  Neither tables nor counts are read or written.  The result is
+ * bitwise that of cpa_build_block_tables with prefix_blocks[b] = prefix_len[b] / 64 and
+ * chunk_blocks[b] = ceil(chunk length / 64), followed by cpa_chunked_prefill (v_dim_major = 0)
+ * or cpa_chunked_prefill_vt (v_dim_major = 1) on those tables.
+ *
+ * Why: chunked prefill repeats the table build at every chunk (CompactAttention abstract); one
+ * launch instead of two removes a launch and its gap per chunk.  Every tile of a group repeats
+ * the union (the group's masks are read once from HBM, then from L2).
+ *
+ *   masks, nqb_max, nkvb_max  as cpa_build_block_tables (uint8 [B][Hq][nqb_max][nkvb_max],
+ *            nonzero = selected; nkvb_max <= CPA_MAX_KV_BLOCKS).  Query blocks at or past
+ *            nqb_max, and blocks at or past nkvb_max, select nothing (the table build's clamps).
+ *            Rows are read 16 bytes at a time when nkvb_max % 16 == 0 and masks is 16-byte
+ *            aligned, else a byte at a time.
+ *   v_dim_major, v_page_stride, v_head_stride, v_row_stride  the V pool as cpa_append_kv
+ *            describes it: token-major (0, v_row_stride = token stride) or dim-major (1,
+ *            v_row_stride = dim stride).
+ * Other arguments as cpa_chunked_prefill.
+ * Supported: CPA_BF16, d in {64, 128}, any G, row strides (token_stride, v_row_stride) up to
+ * 2^24 elements (else CPA_ERR_UNSUPPORTED).
+ * Errors: those of cpa_chunked_prefill (without the table checks), CPA_ERR_SHAPE (v_dim_major
+ * not 0 or 1, nqb_max or nkvb_max negative, nkvb_max > CPA_MAX_KV_BLOCKS), CPA_ERR_NULL (masks
+ * NULL with nqb_max, nkvb_max > 0).
+ */
+cpa_status cpa_chunked_prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                                     int64_t head_stride, int64_t token_stride, const void* v_pages,
+                                     int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
+                                     int64_t v_row_stride, int64_t n_pages, const int32_t* page_map,
+                                     int page_map_stride, const uint8_t* masks, int nqb_max, int nkvb_max,
+                                     const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv,
+                                     int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     hipStream_t stream);
+
+/*
  * cpa_append_kv - write each sequence's chunk of new K and V rows into the paged cache, the step
  * before attention in chunked prefill (CompactAttention abstract: the chunk attends over KV
  * blocks that live in a paged cache and are read in place, so its own K/V must be there).

@@ -12,6 +12,9 @@ Thin wrappers over the C ABI in include/cpa.h:
   v_layout "dim": V pages stored [page][group][d][64])
 * build_block_plans(masks, prefix_blocks, chunk_blocks) and chunked_prefill_direct(...): the
   direct block-sparse baseline, every (head, query block) over its own mask row
+* chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len,
+                        v_layout="token") -> (o, lse): the table build and the prefill in one
+  launch (each workgroup builds its group's union from the masks)
 * append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len,
             v_layout="token"): the chunk's K/V rows into the paged cache
 
@@ -27,6 +30,7 @@ from .api import (  # noqa: F401
     build_block_tables_bits,
     chunked_prefill,
     chunked_prefill_direct,
+    chunked_prefill_fused,
     chunked_prefill_split_static,
     plan_flops,
     plan_split_pages,

@@ -359,6 +359,54 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
         return out, lse
 
 
+def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len, sm_scale=0.0,
+                          out=None, lse=None, return_lse=False, stream=None, v_layout="token"):
+    """The table build and the prefill in one launch (cpa_chunked_prefill_fused): every
+    workgroup ORs its KV group's rows of masks (uint8 [B][Hq][nqb_max][nkvb_max]) itself, with
+    prefix_blocks = prefix_len / 64 and chunk_blocks = ceil(chunk length / 64).  Bitwise the
+    result of build_block_tables followed by chunked_prefill on the same inputs.  bf16 q and
+    pools; k_pages / v_pages / v_layout as in chunked_prefill."""
+    if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("the fused path runs bf16 q, k_pages and v_pages")
+    if q.dim() != 3 or not q.is_contiguous():
+        raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
+    Tq, Hq, d = q.shape
+    if k_pages.dim() != 4 or k_pages.shape[2] != BLOCK or k_pages.shape[3] != d or k_pages.stride(3) != 1:
+        raise ValueError("k_pages must be [n_pages][Hkv][64][d] with d contiguous")
+    n_pages, Hkv = k_pages.shape[0], k_pages.shape[1]
+    if v_layout == "token":
+        vshape = (n_pages, Hkv, BLOCK, d)
+    elif v_layout == "dim":
+        vshape = (n_pages, Hkv, d, BLOCK)
+    else:
+        raise ValueError("v_layout must be 'token' or 'dim'")
+    if v_pages.dim() != 4 or tuple(v_pages.shape) != vshape or v_pages.stride(3) != 1:
+        raise ValueError(f"v_pages must be {list(vshape)} with the last dimension contiguous")
+    if not (isinstance(masks, torch.Tensor) and masks.dtype == torch.uint8 and masks.dim() == 4
+            and masks.is_contiguous()):
+        raise TypeError("masks must be a contiguous uint8 [B][Hq][nqb_max][nkvb_max] tensor")
+    for t, nm in ((page_map, "page_map"), (cu_q, "cu_q"), (prefix_len, "prefix_len")):
+        _i32(t, nm)
+    B = prefix_len.numel()
+    if masks.shape[0] != B or masks.shape[1] != Hq:
+        raise ValueError("masks must be [B][Hq][nqb_max][nkvb_max] (B sequences, Hq query heads)")
+    if cu_q.numel() != B + 1 or page_map.dim() != 2 or page_map.shape[0] != B:
+        raise ValueError("inconsistent B across cu_q / prefix_len / page_map / masks")
+    dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, masks=masks, cu_q=cu_q,
+              prefix_len=prefix_len)
+    out, lse = _out_buffers(out, lse, return_lse, q, dev)
+    with torch.cuda.device(dev):
+        st = load().cpa_chunked_prefill_fused(
+            _ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
+            1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages,
+            _ptr(page_map), page_map.shape[1], _ptr(masks), masks.shape[2], masks.shape[3], _ptr(cu_q),
+            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse),
+            _stream(stream, dev))
+    if st != 0:
+        raise CpaError(st, "cpa_chunked_prefill_fused")
+    return out, lse
+
+
 STATIC_SCRATCH_BYTES = 64 * 1024 * 1024   # CPA_STATIC_SCRATCH_BYTES
 
 

@@ -11,7 +11,8 @@
 //            kb <= prefix_blocks + qi applied per row; a thread walks its rows (head, query
 //            block) by stepping, with no division per row;
 //            partial ORs of threads that share a column meet in LDS (a tree over the row
-//            splits); each 16-block column becomes 16 bits of a 64-bit word in LDS.
+//            splits); each 16-block column becomes 16 bits of a 64-bit word in LDS
+//            (union_byte_rows, shared with the fused prefill).
 //            Bit-packed masks (one bit per KV block, 64 blocks per 8-byte word) are
 //            OR-reduced a word at a time instead.
 //   phase 2  popcount per word, exclusive scan over words (within waves, then over the wave
@@ -19,32 +20,13 @@
 //            64w + l at (word offset + mbcnt rank) when bit l is set.  Positions
 //            count .. table_cap-1 get -1.
 // The result is unique (a set in ascending order), so the kernel is bit-exact by construction.
-#include "cpa_internal.h"
+#include "union_common.h"
 
 namespace cpa {
 namespace {
 
 constexpr int UT = 1024;              // threads per workgroup
 constexpr int MAX_WORDS = 65536 / 64;  // 64-bit words for the largest supported KV extent
-
-// 0x80 in every byte of x that is nonzero
-__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
-  return (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
-}
-
-// 16 mask bytes -> 16 bits (bit j set iff byte j nonzero)
-__device__ __forceinline__ uint32_t bytes_to_bits(const uint32_t v[4]) {
-  uint32_t bits = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t t = nonzero_bytes(v[w]);
-    bits |= ((t >> 7) & 1u) << (4 * w + 0);
-    bits |= ((t >> 15) & 1u) << (4 * w + 1);
-    bits |= ((t >> 23) & 1u) << (4 * w + 2);
-    bits |= ((t >> 31) & 1u) << (4 * w + 3);
-  }
-  return bits;
-}
 
 // Phase 2 for one (sequence, KV group), called by every thread of the workgroup: the
 // group's nwords 64-bit words (in LDS) -> ascending ids of their set bits at tab[0 .. total),
@@ -182,95 +164,9 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
       if (s == 0 && c < nwords) words[c] = redw[tid];
       __syncthreads();
     }
-  }
-  const int nchunk = BITS ? 0 : (nkvb + 15) >> 4;
-  int lg = 0;
-  while ((1 << lg) < nchunk && (1 << lg) < UT) ++lg;
-  const int cols = 1 << lg;
-  const int rsplit = UT >> lg;
-  const size_t row_stride = (size_t)a.nkvb_max;
-  const uint8_t* gbase = a.masks + ((size_t)b * a.Hq + (size_t)g * G) * a.nqb_max * row_stride;
-
-  for (int c0 = 0; c0 < nchunk; c0 += cols) {
-    const int c = c0 + (tid & (cols - 1));
-    const int s = tid >> lg;
-    uint32_t acc[4] = {0u, 0u, 0u, 0u};
-    if (c < nchunk) {
-      const int kb0 = c << 4;
-      const int qi_lo = max(0, kb0 - qb0);  // first query block that can reach column kb0
-      const int nq = nqb - qi_lo;
-      // mask bytes of row (head hh of the group, query block qi) at column kb0, causally clipped
-      auto row = [&](int hh, int qi, uint32_t v[4]) __attribute__((always_inline)) {
-        const uint8_t* rowp = gbase + ((size_t)hh * a.nqb_max + qi) * row_stride + kb0;
-        if (VEC) {
-          const uint4 x = *reinterpret_cast<const uint4*>(rowp);
-          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-        } else {
-          const int lim = min(16, a.nkvb_max - kb0);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int j = 4 * w + k;
-              if (j < lim) word |= (uint32_t)rowp[j] << (8 * k);
-            }
-            v[w] = word;
-          }
-        }
-        const int nallow = qb0 + qi - kb0 + 1;  // bytes 0 .. nallow-1 are causally reachable
-        if (nallow < 16) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int keep = min(max(nallow - 4 * w, 0), 4);
-            const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : ((1u << (8 * keep)) - 1u);
-            v[w] &= m;
-          }
-        }
-      };
-      const int nrows = G * nq;
-      // row t = (head hh, query block qi_lo + qr), walked from t = s in steps of rsplit rows
-      // without a division per row
-      int hh = s / nq, qr = s - (s / nq) * nq;
-      const int dh = rsplit / nq, dq = rsplit - (rsplit / nq) * nq;
-      for (int t0 = s; t0 < nrows; t0 += 4 * rsplit) {
-        uint32_t v[4][4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (t0 + u * rsplit < nrows) {
-            row(hh, qi_lo + qr, v[u]);
-          } else {
-            v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0u;
-          }
-          qr += dq;
-          hh += dh;
-          if (qr >= nq) {
-            qr -= nq;
-            ++hh;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) acc[w] |= v[u][w];
-      }
-    }
-    red[tid] = make_uint4(acc[0], acc[1], acc[2], acc[3]);
-    __syncthreads();
-    for (int h = rsplit >> 1; h >= 1; h >>= 1) {   // tree OR over the row splits of a column
-      if (s < h) {
-        const uint4 o = red[tid + (h << lg)];
-        const uint4 m = red[tid];
-        red[tid] = make_uint4(m.x | o.x, m.y | o.y, m.z | o.z, m.w | o.w);
-      }
-      __syncthreads();
-    }
-    if (s == 0 && c < nchunk) {
-      const uint4 m = red[tid];
-      const uint32_t v[4] = {m.x, m.y, m.z, m.w};
-      reinterpret_cast<unsigned short*>(words)[c] = (unsigned short)bytes_to_bits(v);  // little endian
-    }
-    __syncthreads();
+  } else {   // union_byte_rows (union_common.h)
+    const uint8_t* gbase = a.masks + ((size_t)b * a.Hq + (size_t)g * G) * a.nqb_max * (size_t)a.nkvb_max;
+    union_byte_rows<UT, 4, VEC>(gbase, (size_t)a.nkvb_max, a.nqb_max, G, qb0, nqb, a.nkvb_max, words, red);
   }
 
   // ---- phase 2 ------------------------------------------------------------------------------

@@ -44,7 +44,8 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
                            const int32_t* counts, const int32_t* cu_q,
                            const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
                            int max_chunk_len, float sm_scale, void* o, float* lse,
-                           cpa::PrefillArgs& a, bool* nothing, int kv_elem_bytes = 0) {
+                           cpa::PrefillArgs& a, bool* nothing, int kv_elem_bytes = 0,
+                           bool with_tables = true) {
   *nothing = false;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_chunk_len < 0 || table_cap < 0 || n_pages < 0)
     return CPA_ERR_SHAPE;
@@ -70,8 +71,8 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   if (vl.row_stride < v_row_len || vl.head_stride < v_rows * vl.row_stride ||
       vl.page_stride < (int64_t)Hkv * vl.head_stride)
     return CPA_ERR_SHAPE;
-  if (!q || !k_pages || !v_pages || !page_map || !counts || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
-  if (table_cap > 0 && !tables) return CPA_ERR_NULL;
+  if (!q || !k_pages || !v_pages || !page_map || !cu_q || !prefix_len || !o) return CPA_ERR_NULL;
+  if (with_tables && (!counts || (table_cap > 0 && !tables))) return CPA_ERR_NULL;
   // bytes per pool element: that of q's dtype unless the pools hold another format (fp8)
   const int eb = kv_elem_bytes > 0 ? kv_elem_bytes : dtype == CPA_BF16 ? 2 : 4;
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return CPA_ERR_ALIGN;
@@ -387,6 +388,34 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
                                         prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
   if (st != CPA_OK || nothing) return st;
   return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+cpa_status cpa_chunked_prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                                     int64_t head_stride, int64_t token_stride, const void* v_pages, int v_dim_major,
+                                     int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride,
+                                     int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                                     const uint8_t* masks, int nqb_max, int nkvb_max, const int32_t* cu_q,
+                                     const int32_t* prefix_len, int B, int Hq, int Hkv, int d, int max_chunk_len,
+                                     float sm_scale, void* o, float* lse, hipStream_t stream) {
+  if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
+  if (nqb_max < 0 || nkvb_max < 0 || nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
+  cpa::PrefillArgs a;
+  bool nothing;
+  const VLayout vl{v_page_stride, v_head_stride, v_row_stride, v_dim_major == 1};
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
+                                        n_pages, page_map, page_map_stride, nullptr, 0, nullptr, cu_q, prefix_len,
+                                        B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing,
+                                        /*kv_elem_bytes=*/0, /*with_tables=*/false);
+  if (st != CPA_OK || nothing) return st;
+  if (!masks && nqb_max > 0 && nkvb_max > 0) return CPA_ERR_NULL;
+  // the direct-to-LDS bf16 kernel: 32-bit offsets within a page
+  if (dtype != CPA_BF16 || token_stride > (1 << 24) || v_row_stride > (1 << 24)) return CPA_ERR_UNSUPPORTED;
+  a.fused = 1;
+  a.masks = masks;
+  a.mask_nqb = nqb_max;
+  a.mask_nkvb = nkvb_max;
+  a.mask_vec = (nkvb_max % 16 == 0 && aligned16(masks)) ? 1 : 0;
+  return cpa::launch_prefill(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
 }  // extern "C"

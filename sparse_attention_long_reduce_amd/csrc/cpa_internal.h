@@ -8,6 +8,9 @@ namespace cpa {
 // (query block, head) pairs per prefill workgroup: one pair per two waves (64 query rows)
 constexpr int PAIRS_PER_TILE = 4;
 
+// 64-bit words of a per-group block bitmap at the largest supported KV extent (65536 blocks)
+constexpr int MAX_KV_WORDS = 65536 / 64;
+
 struct UnionArgs {
   const uint8_t* masks;
   int B, Hq, Hkv, nqb_max, nkvb_max;
@@ -64,6 +67,13 @@ struct PrefillArgs {
   int total_q;          // rows of all sequences (the partials' row dimension)
   float* part_o;
   float* part_lse;
+  // fused block union (fused == 1): no tables / counts; every workgroup ORs its KV group's
+  // rows of masks (uint8 [B][Hq][mask_nqb][mask_nkvb], nonzero = selected) itself, with
+  // prefix_blocks = prefix_len / 64 and chunk_blocks = the chunk's query blocks.  mask_vec: rows
+  // can be read 16 bytes at a time (mask_nkvb % 16 == 0 and a 16-byte aligned base).
+  int fused;
+  const uint8_t* masks;
+  int mask_nqb, mask_nkvb, mask_vec;
 };
 
 struct MergeArgs {

@@ -69,7 +69,17 @@
 // Split-KV (SPLIT): a workgroup runs one of n_splits near-equal ranges of its tile's pages and
 // writes that range's normalised output (fp32) and LSE into the caller's workspace;
 // split_merge_kernel combines the ranges of each row by their LSEs.
+//
+// Fused block union (FU): no table is given.  Each workgroup first ORs the masks of its KV
+// group (the G heads over the chunk's query blocks, causally clipped) into an LDS bitmap with
+// the table-build kernel's own routine (union_byte_rows), and counts the set bits before each
+// 64-bit word.  Table position p is the p-th set bit in ascending order, so the page ids are
+// expanded from the bitmap a window chunk at a time, and the pages visited and their order are
+// exactly those of the separate table-build launch: the output is bitwise the same.  Every tile
+// of a group repeats the union (its masks are read from L2 after the first tile), which costs a
+// few microseconds per workgroup against a separate launch.
 #include "prefill_common.h"
+#include "union_common.h"
 
 #include <type_traits>
 
@@ -151,8 +161,9 @@ using IC = std::integral_constant<int, I>;
 // of page i+4, converts K of page i+2 and V of page i+1 (copied in iteration i-3), and reads K
 // of page i+1 and V of page i, so the staging rings hold four pages and the bf16 rings two.
 // The K scale is folded into the softmax scale and the V scale into the output (a.out_scale).
-template <int D, bool SPLIT, bool VT, bool F8>
+template <int D, bool SPLIT, bool VT, bool F8, bool FU>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
+  static_assert(!(FU && (SPLIT || F8)), "the fused union runs the plain bf16 path");
   using GE = Geo<D>;
   constexpr bool VOP = VT || F8;   // V tiles in operand order (8 keys of one dim per slot)
   constexpr int NPW = F8 ? (GE::NPW / 2 > 0 ? GE::NPW / 2 : 1) : GE::NPW;   // copies per wave and page
@@ -168,6 +179,9 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   __shared__ __attribute__((aligned(1024))) __bf16 sink[NPW * 512];  // target of idle copies
   __shared__ int win_kb[WIN];
   __shared__ int win_ph[WIN];
+  // FU: the group's block bitmap and, per word, the set bits before it
+  __shared__ unsigned long long uw[FU ? MAX_KV_WORDS : 1];
+  __shared__ int upre[FU ? MAX_KV_WORDS : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,7 +190,7 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const int hl = lane >> 5;  // lane half
 
   int gi, rank, split;
-  if (!decode_tile(a, lane, gi, rank, split)) return;
+  if (!decode_tile<FU>(a, lane, gi, rank, split)) return;
   const int b = gi / a.Hkv;
   const int g = gi - b * a.Hkv;
   const int t_pairs = a.tiles_per_group - 1 - rank;   // heaviest (last) query blocks first
@@ -196,10 +210,87 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   const bool active = qi_w < nqb;
   const int qi_last = min(qi_span, nqb - 1);
 
-  const int cnt = min(max(a.counts[gi], 0), a.table_cap);
-  const int32_t* tab = a.tables + (size_t)gi * a.table_cap;
-  int n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
-  int n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
+  int cnt;
+  const int32_t* tab = nullptr;
+  int nwords = 0;
+  if constexpr (FU) {
+    // the union over the group's rows, clamped as the table-build kernel clamps its lengths
+    // (prefix_blocks = qb0, chunk_blocks = nqb)
+    const int uqb0 = min(qb0, a.mask_nkvb);
+    const int unqb = min(min(nqb, a.mask_nqb), a.mask_nkvb - uqb0);
+    nwords = (uqb0 + unqb + 63) >> 6;
+    for (int w = tid; w < nwords; w += THREADS) uw[w] = 0ull;
+    __syncthreads();
+    uint4* red = reinterpret_cast<uint4*>(kR0);   // scratch until the first page copies
+    const uint8_t* gbase = a.masks + ((size_t)b * a.Hq + (size_t)g * a.G) * a.mask_nqb * (size_t)a.mask_nkvb;
+    if (a.mask_vec)
+      union_byte_rows<THREADS, 8, true>(gbase, (size_t)a.mask_nkvb, a.mask_nqb, a.G, uqb0, unqb, a.mask_nkvb, uw, red);
+    else
+      union_byte_rows<THREADS, 8, false>(gbase, (size_t)a.mask_nkvb, a.mask_nqb, a.G, uqb0, unqb, a.mask_nkvb, uw,
+                                         red);
+    // exclusive prefix of the set bits over words: within waves by shuffles, then over the
+    // wave totals
+    constexpr int WPT = MAX_KV_WORDS / THREADS;
+    int pc[WPT];
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int w = tid * WPT + k;
+      pc[k] = w < nwords ? __popcll(uw[w]) : 0;
+      mine += pc[k];
+    }
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    int* tsum = reinterpret_cast<int*>(red);
+    if (lane == 63) tsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int x = 0; x < THREADS / 64; ++x) {
+      const int t = tsum[x];
+      before += x < wave ? t : 0;
+      total += t;
+    }
+    int run = before + incl - mine;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int w = tid * WPT + k;
+      if (w < nwords) upre[w] = run;
+      run += pc[k];
+    }
+    __syncthreads();
+    cnt = total;
+  } else {
+    cnt = min(max(a.counts[gi], 0), a.table_cap);
+    tab = a.tables + (size_t)gi * a.table_cap;
+  }
+  // FU: set bits of the bitmap past block lim (the table entries with id > lim); wave-uniform
+  auto bits_above = [&](int lim) __attribute__((always_inline)) {
+    const int first = lim + 1;
+    int c = 0;
+    for (int w0 = first >> 6; w0 < nwords; w0 += 64) {
+      const int w = w0 + lane;
+      unsigned long long x = w < nwords ? uw[w] : 0ull;
+      if (w == (first >> 6)) x &= ~0ull << (first & 63);
+      c += __popcll(x);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+    // every lane holds the total: say so, so that the loop bounds derived from it stay scalar
+    return __builtin_amdgcn_readfirstlane(c);
+  };
+  int n_iter, n_vis;
+  if constexpr (FU) {
+    n_iter = cnt - bits_above(qb0 + qi_last);
+    n_vis = active ? cnt - bits_above(qb0 + qi_w) : 0;
+  } else {
+    n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
+    n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
+  }
   if (SPLIT) {   // this workgroup's range: the tile's pages cut into n_splits near-equal ranges
     const int len = (n_iter + a.n_splits - 1) / a.n_splits;
     const int lo = min(n_iter, split * len);
@@ -326,16 +417,30 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
 
   // resolve table entries [base, base + CH) into window slots (base + j) mod WIN (indices are
   // non-negative and WIN, CH powers of two)
+  auto resolve = [&](int pos, int kb) __attribute__((always_inline)) {
+    int ph = -1;
+    if (kb >= 0 && kb < a.page_map_stride) {
+      ph = pmap[kb];
+      if (ph < 0 || (int64_t)ph >= a.n_pages) ph = -1;
+    }
+    win_kb[pos & (WIN - 1)] = kb;
+    win_ph[pos & (WIN - 1)] = ph;
+  };
   auto load_chunk = [&](int base) __attribute__((always_inline)) {
-    for (int j = tid; j < CH && base + j < n_iter; j += THREADS) {
-      const int kb = tab[base + j];
-      int ph = -1;
-      if (kb >= 0 && kb < a.page_map_stride) {
-        ph = pmap[kb];
-        if (ph < 0 || (int64_t)ph >= a.n_pages) ph = -1;
+    if constexpr (FU) {
+      // entry p is the p-th set bit: lane l of the wave on word w holds entry upre[w] + (its
+      // rank among the word's set bits) when bit l is set
+      const int hi = min(base + CH, n_iter);
+      for (int w = wave; w < nwords; w += THREADS / 64) {
+        const unsigned long long word = uw[w];
+        const int p0 = upre[w];
+        if (p0 >= hi || p0 + (int)__popcll(word) <= base) continue;
+        const int pos = p0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0u));
+        if (((word >> lane) & 1ull) && pos >= base && pos < hi) resolve(pos, (w << 6) + lane);
       }
-      win_kb[(base + j) & (WIN - 1)] = kb;
-      win_ph[(base + j) & (WIN - 1)] = ph;
+    } else {
+      for (int j = tid; j < CH && base + j < n_iter; j += THREADS) resolve(base + j, tab[base + j]);
     }
   };
 
@@ -794,17 +899,23 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   const int grid = prefill_grid(a);
   if (grid == 0) return hipSuccess;
   const bool split = a.n_splits > 1;
+  const dim3 g(grid), t(THREADS);
+  if (a.fused) {   // bf16 pages, no split
+    if (a.v_dmajor) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false, true>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, true>), g, t, 0, s, a);
+    return hipGetLastError();
+  }
   if (a.kv_fp8) {   // fp8 pages, no split
-    if (a.v_dmajor) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    if (a.v_dmajor) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true, false>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true, false>), g, t, 0, s, a);
     return hipGetLastError();
   }
   if (a.v_dmajor) {
-    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false, false>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false, false>), g, t, 0, s, a);
   } else {
-    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false, false>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, false>), g, t, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -821,6 +932,8 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
+  if (a.fused)   // the caller has checked: bf16, no split, no fp8, row strides within 32-bit offsets
+    return d == 64 ? launch_bf16<64>(a, s) : launch_bf16<128>(a, s);
   if (a.kv_fp8 && (a.n_splits > 1 || a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
     return launch_prefill_regstaged(a, true, d, s);   // fp8 forms the direct-to-LDS kernel does not take
   if (!bf16) return launch_prefill_regstaged(a, false, d, s);

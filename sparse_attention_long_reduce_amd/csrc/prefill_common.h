@@ -56,10 +56,23 @@ __device__ __forceinline__ int count_above(const int32_t* tab, int cnt, int nqb,
   return c;
 }
 
+// Pages KV group gi's tiles are expected to visit: its table length, or with FU (no table
+// yet) the sequence's causal extent in blocks, the bound of its table length.
+template <bool FU>
+__device__ __forceinline__ int group_weight(const PrefillArgs& a, int gi) {
+  if (FU) {
+    const int b = gi / a.Hkv;
+    const int cn = min(max(a.cu_q[b + 1] - a.cu_q[b], 0), a.max_chunk_len);
+    return (max(a.prefix_len[b], 0) >> 6) + ((cn + 63) >> 6);
+  }
+  return min(max(a.counts[gi], 0), a.table_cap);
+}
+
 // Position of lane j's KV group (j < ngx, the groups gi = xcd + 8*j) when the groups of one XCD
-// are sorted by table length, longest first (ties by j); wave-uniform loop over ngx <= 64.
+// are sorted by group_weight, heaviest first (ties by j); wave-uniform loop over ngx <= 64.
+template <bool FU>
 __device__ __forceinline__ int weight_rank(const PrefillArgs& a, int xcd, int ngx, int lane) {
-  const int c = lane < ngx ? min(max(a.counts[xcd + 8 * lane], 0), a.table_cap) : -1;
+  const int c = lane < ngx ? group_weight<FU>(a, xcd + 8 * lane) : -1;
   int r = 0;
   for (int i = 0; i < ngx; ++i) {
     const int ci = __shfl(c, i);
@@ -75,7 +88,9 @@ __device__ __forceinline__ int weight_rank(const PrefillArgs& a, int xcd, int ng
 // decreasing table length (a tile visits about as many pages as its group's table holds), and
 // within a group the tiles of rank 0 (the last query blocks, which see the most pages) first,
 // the split ranges of one tile next to each other.  Beyond 64 groups per XCD the groups go in
-// index order.  Returns false for padding.
+// index order.  Returns false for padding.  FU: the tables are built by the workgroups
+// themselves, so groups are ordered by their causal extent instead.
+template <bool FU>
 __device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int lane, int& gi, int& rank, int& split) {
   const int per_group = a.tiles_per_group * a.n_splits;   // work items of one KV group
   int w;
@@ -87,7 +102,7 @@ __device__ __forceinline__ bool decode_tile(const PrefillArgs& a, int lane, int&
     int k = slot / per_group;
     w = slot - k * per_group;
     if (ngx <= 64) {
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(weight_rank(a, xcd, ngx, lane) == k);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(weight_rank<FU>(a, xcd, ngx, lane) == k);
       k = __builtin_ctzll(hit);
     }
     gi = xcd + 8 * k;

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(THREADS) void prefill_kernel(const PrefillArgs a) {
 
   // ---- tile decode ---------------------------------------------------------------------
   int gi, rank, split;   // split-KV is not taken on this path (n_splits == 1)
-  if (!decode_tile(a, lane, gi, rank, split)) return;
+  if (!decode_tile<false>(a, lane, gi, rank, split)) return;
   const int b = gi / a.Hkv;
   const int g = gi - b * a.Hkv;
   const int t_pairs = a.tiles_per_group - 1 - rank;   // heaviest (last) query blocks first

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables",
                           "cpa_build_block_tables_bits", "cpa_chunked_prefill", "cpa_chunked_prefill_direct",
-                          "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_split", "cpa_chunked_prefill_split_static",
+                          "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_fused", "cpa_chunked_prefill_split",
+                          "cpa_chunked_prefill_split_static",
                           "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -220,6 +221,38 @@ def pfv(lib, dtype=1, total_q=256, split=0, ws=NULL, ws_bytes=0, vps=8 * 128 * 6
                                       a["npages"], a["pm"], a["pms"], a["tab"], a["cap"], a["cnt"], a["cu"],
                                       a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["mcl"], a["scale"], a["o"],
                                       a["lse"], total_q, split, ws, ws_bytes, None)
+
+
+def pfu(lib, dtype=1, vdm=1, vps=8 * 128 * 64, vhs=128 * 64, vrs=64, masks=FAKE, nqb=4, nkvb=16, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
+             cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL)
+    a.update(kw)
+    return lib.cpa_chunked_prefill_fused(a["q"], dtype, a["k"], a["ps"], a["hs"], a["ts"], a["v"], vdm, vps, vhs,
+                                         vrs, a["npages"], a["pm"], a["pms"], masks, nqb,
+                                         nkvb, a["cu"], a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["mcl"],
+                                         a["scale"], a["o"], a["lse"], None)
+
+
+def test_fused_validation(lib):
+    assert pfu(lib, vdm=2) == 2                       # V layout flag
+    assert pfu(lib, nqb=-1) == 2
+    assert pfu(lib, nkvb=-1) == 2
+    assert pfu(lib, nkvb=65537) == 2                  # beyond CPA_MAX_KV_BLOCKS
+    assert pfu(lib, masks=NULL) == 1
+    assert pfu(lib, masks=NULL, nkvb=0, dtype=0) == 4   # no mask byte to read: NULL passes that check
+    assert pfu(lib, dtype=0) == 4                     # bf16 only
+    assert pfu(lib, d=96) == 4
+    assert pfu(lib, vrs=1 << 25, vhs=128 << 25, vps=8 * (128 << 25)) == 4   # 32-bit offsets within a page
+    assert pfu(lib, vrs=63) == 2                      # a dim row must hold the page's 64 tokens
+    assert pfu(lib, vdm=0, vps=8 * 64 * 128, vhs=64 * 128, vrs=120) == 2    # a token row must hold d
+    assert pfu(lib, vdm=0, vps=8 * 64 * 132, vhs=64 * 132, vrs=132) == 3    # 264-byte bf16 rows
+    assert pfu(lib, q=NULL) == 1
+    assert pfu(lib, cu=NULL) == 1
+    assert pfu(lib, o=FAKE + 2) == 3
+    assert pfu(lib, Hq=30) == 2                       # Hq % Hkv
+    assert pfu(lib, npages=0) == 2
+    assert pfu(lib, B=0, q=NULL, masks=NULL) == 0     # nothing to do
+    assert pfu(lib, mcl=0) == 0
 
 
 def test_vt_validation(lib):
