@@ -20,7 +20,7 @@ def bern(p, local=1):
     return lambda rng, *a: mask_bernoulli(rng, *a, p=p, local=local)
 
 
-@pytest.mark.parametrize("mode", ["plain", "split", "dim", "bits", "fp8_token", "fp8_dim"])
+@pytest.mark.parametrize("mode", ["plain", "split", "dim", "bits", "fp8_token", "fp8_dim", "fused_token", "fused_dim"])
 def test_capture_and_replay(mode):
     w = make_workload("graph", [0, 192, 4096], [37, 130, 255], 8, 2, 128, "bf16", bern(0.05), 81)
     dv = upload(w)
@@ -29,7 +29,8 @@ def test_capture_and_replay(mode):
     if mode.startswith("fp8"):   # e4m3 copies of the pools, scale 1/4
         kp = (kp.float() * 4).to(torch.float8_e4m3fn)
         vp = (vp.float() * 4).to(torch.float8_e4m3fn)
-    layout = "dim" if mode in ("dim", "fp8_dim") else "token"
+    layout = "dim" if mode in ("dim", "fp8_dim", "fused_dim") else "token"
+    fused = mode.startswith("fused")
     if layout == "dim" and mode.startswith("fp8"):
         vp = vp.view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn)
     elif layout == "dim":
@@ -45,6 +46,10 @@ def test_capture_and_replay(mode):
                      dtype=torch.uint8, device="cuda")
 
     def step():
+        if fused:   # one launch, no tables
+            cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"], w.max_chunk_len,
+                                      out=out, lse=lse, v_layout=layout)
+            return
         if mode == "bits":
             cpa.build_block_tables_bits(bits, w.nkvb_max, dv["pb"], dv["cb"], w.Hkv, tables=tables, counts=counts)
         else:
@@ -56,6 +61,12 @@ def test_capture_and_replay(mode):
     step()
     torch.cuda.synchronize()
     o_ref, l_ref, t_ref = out.clone(), lse.clone(), tables.clone()
+    if fused:   # the same bits as the two separate launches
+        tb, cn = cpa.build_block_tables(dv["masks"], dv["pb"], dv["cb"], w.Hkv)
+        o_sep, l_sep = cpa.chunked_prefill(dv["q"], kp, vp, dv["pm"], tb, cn, dv["cu"], dv["pl"], w.max_chunk_len,
+                                           return_lse=True, v_layout=layout)
+        torch.cuda.synchronize()
+        assert torch.equal(o_ref, o_sep) and torch.equal(l_ref, l_sep)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -74,5 +85,6 @@ def test_capture_and_replay(mode):
         (x * 2).sum().item()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(tables, t_ref), f"replay {i}: tables"
+        if not fused:
+            assert torch.equal(tables, t_ref), f"replay {i}: tables"
         assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), f"replay {i}: output"

@@ -9,7 +9,8 @@ not.  It then runs the path as a caller would, against the oracle at every step:
   append   the chunk's own K/V rows into the paged pools: bit-exact against the oracle's copy;
   tables   from byte masks and from bit-packed masks: bit-exact;
   attend   over the appended pools: the bars of the hand-picked cases, LSE included;
-  direct   (bf16 cases) the per-head baseline's plans bit-exact and its output within the bars.
+  direct   (bf16 cases) the per-head baseline's plans bit-exact and its output within the bars;
+  fused    (bf16 cases) the table build in the prefill's prologue, bitwise the separate launches.
 """
 import os
 
@@ -158,6 +159,16 @@ def run_case(i, c, wseed, rseed):
         compare(w, od, Od, f"sweep {i} direct")
         check_lse(ld, Ld, 2 ** -7)
 
+        # the table build in the prefill's prologue: bitwise the separate (unsplit) launches
+        of, lf = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"],
+                                           w.max_chunk_len, return_lse=True, v_layout=c["v_layout"])
+        ou, lu = (o, lse) if not c["split"] else cpa.chunked_prefill(
+            dv["q"], kp, vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len, return_lse=True,
+            v_layout=c["v_layout"])
+        torch.cuda.synchronize()
+        assert torch.equal(of.view(torch.int16), ou.view(torch.int16)), f"sweep {i} fused output"
+        assert torch.equal(lf.view(torch.int32), lu.view(torch.int32)), f"sweep {i} fused LSE"
+
 
 N_LONG = int(os.environ.get("CPA_SWEEP_LONG_CASES", "12"))
 
@@ -197,3 +208,12 @@ def test_sweep_long(i):
     h = torch.from_numpy(S[:, 1]).cuda()
     compare(w, o[r, h].float().cpu().numpy(), Os, f"long sweep {i}")
     assert np.max(np.abs(lse[r, h].cpu().numpy() - Ls)) < (1e-4 if c["mode"] == "f32" else 2 ** -7)
+    if c["mode"] == "bf16":   # the fused launch expands these long tables from its bitmap, window by window
+        of, lf = cpa.chunked_prefill_fused(dv["q"], dv["kp"], vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"],
+                                           w.max_chunk_len, return_lse=True, v_layout=c["v_layout"])
+        ou, lu = (o, lse) if not c["split"] else cpa.chunked_prefill(
+            dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len, return_lse=True,
+            v_layout=c["v_layout"])
+        torch.cuda.synchronize()
+        assert torch.equal(of.view(torch.int16), ou.view(torch.int16)), f"long sweep {i} fused output"
+        assert torch.equal(lf.view(torch.int32), lu.view(torch.int32)), f"long sweep {i} fused LSE"
