@@ -325,7 +325,8 @@ def time_fused(cpa, batches, steps, warmup=3):
         for o, l, bt in zip(outs, lses, batches):
             dim = bt.v_layout == "dim"
             cpa.chunked_prefill_fused(bt.q, bt.kp, bt.vp_dim if dim else bt.vp, bt.pm, bt.masks, bt.cu, bt.pl,
-                                      bt.w.max_chunk_len, out=o, lse=l, v_layout=bt.v_layout)
+                                      bt.w.max_chunk_len, out=o, lse=l, v_layout=bt.v_layout,
+                                      split_pages=bt.split_pages, workspace=bt.workspace)
 
     def separate_step():
         for bt in batches:
@@ -614,19 +615,17 @@ def main():
                              "unit": "TFLOP/s", "frac": round(fp8kv["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
         log(f"[bench] fp8 KV cache: prefill {fp8kv['prefill_ms']:.3f} ms ({fp8kv['prefill_tflops']:.0f} TFLOP/s), "
             f"cache {fp8kv['kv_bytes'] / 2**20:.0f} MiB vs {fp8kv['kv_bytes_bf16'] / 2**20:.0f} MiB bf16")
-    fused = None
-    if all(bt.split_pages == 0 for bt in batches):
-        fu = time_fused(cpa, batches, max(5, args.steps))
-        fused = {"step_ms": round(fu["step_ms"], 4), "step_ms_median": round(fu["step_ms_median"], 4),
-                 "step_ms_min": round(fu["step_ms_min"], 4), "separate_step_ms": round(fu["separate_step_ms"], 4),
-                 "speedup_over_separate": round(fu["separate_step_ms"] / fu["step_ms"], 4),
-                 "launches_per_step": fu["launches_per_step"],
-                 "outputs_equal_separate": fu["outputs_equal_separate"],
-                 "note": "cpa_chunked_prefill_fused: each prefill workgroup builds its group's union from the "
-                         "masks in its prologue; one launch per launch pair instead of two; timed step by step "
-                         "in turn with the separate launches"}
-        log(f"[bench] fused union in the prefill prologue: step {fu['step_ms']:.3f} ms vs separate "
-            f"{fu['separate_step_ms']:.3f} ms (interleaved), outputs equal: {fu['outputs_equal_separate']}")
+    fu = time_fused(cpa, batches, max(5, args.steps))   # every workload, split-KV included
+    fused = {"step_ms": round(fu["step_ms"], 4), "step_ms_median": round(fu["step_ms_median"], 4),
+             "step_ms_min": round(fu["step_ms_min"], 4), "separate_step_ms": round(fu["separate_step_ms"], 4),
+             "speedup_over_separate": round(fu["separate_step_ms"] / fu["step_ms"], 4),
+             "launches_per_step": fu["launches_per_step"],
+             "outputs_equal_separate": fu["outputs_equal_separate"],
+             "note": "cpa_chunked_prefill_fused: each prefill workgroup builds its group's union from the "
+                     "masks in its prologue; one launch per launch pair instead of two; timed step by step "
+                     "in turn with the separate launches"}
+    log(f"[bench] fused union in the prefill prologue: step {fu['step_ms']:.3f} ms vs separate "
+        f"{fu['separate_step_ms']:.3f} ms (interleaved), outputs equal: {fu['outputs_equal_separate']}")
     bits = time_build_bits(cpa, batches, max(5, args.steps))
     log(f"[bench] table build from bit-packed masks: {bits['us']:.1f} us ({bits['mask_bytes']} mask bytes), "
         f"tables equal: {bits['tables_equal_byte_masks']}")
@@ -702,8 +701,7 @@ def main():
     if append is not None:
         result["kv_append"] = append
     result["table_build_bit_masks"] = bits
-    if fused is not None:
-        result["fused_union"] = fused
+    result["fused_union"] = fused
     if graph is not None:
         result["graph_replay"] = graph
     if fp8kv is not None:

@@ -360,12 +360,18 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
 
 
 def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len, sm_scale=0.0,
-                          out=None, lse=None, return_lse=False, stream=None, v_layout="token"):
+                          out=None, lse=None, return_lse=False, stream=None, v_layout="token", split_pages=0,
+                          workspace=None):
     """The table build and the prefill in one launch (cpa_chunked_prefill_fused): every
     workgroup ORs its KV group's rows of masks (uint8 [B][Hq][nqb_max][nkvb_max]) itself, with
     prefix_blocks = prefix_len / 64 and chunk_blocks = ceil(chunk length / 64).  Bitwise the
-    result of build_block_tables followed by chunked_prefill on the same inputs.  bf16 q and
-    pools; k_pages / v_pages / v_layout as in chunked_prefill."""
+    result of build_block_tables followed by chunked_prefill on the same inputs (tables of
+    capacity nkvb_max).  bf16 q and pools; k_pages / v_pages / v_layout as in chunked_prefill.
+    split_pages > 0 (or "auto") runs split-KV as chunked_prefill does, with nkvb_max as the table
+    capacity; the workspace is allocated here when not given."""
+    auto = isinstance(split_pages, str)
+    if auto and split_pages != "auto":
+        raise ValueError('split_pages must be an int or "auto"')
     if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("the fused path runs bf16 q, k_pages and v_pages")
     if q.dim() != 3 or not q.is_contiguous():
@@ -394,14 +400,26 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
         raise ValueError("inconsistent B across cu_q / prefix_len / page_map / masks")
     dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, masks=masks, cu_q=cu_q,
               prefix_len=prefix_len)
+    nqb_max, nkvb_max = masks.shape[2], masks.shape[3]
+    if auto:
+        splittable = max(k_pages.stride(2), v_pages.stride(2)) <= (1 << 24)
+        n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        split_pages = plan_split_pages(B, Hq, Hkv, max_chunk_len, nkvb_max, n_cus) if splittable else 0
+    split = bool(split_pages and split_pages > 0)
     out, lse = _out_buffers(out, lse, return_lse, q, dev)
     with torch.cuda.device(dev):
+        if split:
+            need = split_workspace_bytes(Tq, Hq, d, nkvb_max, split_pages)
+            if workspace is None:
+                workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            _on(dev, workspace=workspace)
         st = load().cpa_chunked_prefill_fused(
             _ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
             1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages,
-            _ptr(page_map), page_map.shape[1], _ptr(masks), masks.shape[2], masks.shape[3], _ptr(cu_q),
-            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse),
-            _stream(stream, dev))
+            _ptr(page_map), page_map.shape[1], _ptr(masks), nqb_max, nkvb_max, _ptr(cu_q),
+            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq,
+            int(split_pages) if split else 0, _ptr(workspace) if split else None,
+            workspace.numel() * workspace.element_size() if split else 0, _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_chunked_prefill_fused")
     return out, lse

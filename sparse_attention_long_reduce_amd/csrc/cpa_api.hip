@@ -312,21 +312,11 @@ size_t cpa_split_workspace_bytes(int total_q, int Hq, int d, int table_cap, int 
 }  // extern "C"
 
 namespace {
-// the split-KV call for either V layout (split_pages >= 1)
-cpa_status prefill_split(const void* q, cpa_dtype dtype, const void* k_pages, const void* v_pages,
-                         int64_t page_stride, int64_t head_stride, int64_t token_stride, const VLayout& vl,
-                         int64_t n_pages, const int32_t* page_map, int page_map_stride,
-                         const int32_t* tables, int table_cap, const int32_t* counts, const int32_t* cu_q,
-                         const int32_t* prefix_len, int B, int Hq, int Hkv, int d, int max_chunk_len,
-                         float sm_scale, void* o, float* lse, int total_q, int split_pages, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
-  if (split_pages <= 0 || total_q < 0) return CPA_ERR_SHAPE;
-  cpa::PrefillArgs a;
-  bool nothing;
-  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
-                                        n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
-                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
-  if (st != CPA_OK || nothing) return st;
+// The split-KV launches for prepared arguments a: ranges of split_pages pages of tables that
+// hold at most table_cap ids, the partials in the workspace, then the merge.
+cpa_status launch_split(cpa::PrefillArgs& a, cpa_dtype dtype, int64_t token_stride, const VLayout& vl,
+                        int table_cap, int Hq, int d, void* o, float* lse, int total_q, int split_pages,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const int64_t n_splits = ((int64_t)table_cap + split_pages - 1) / split_pages;
   if (n_splits <= 1)   // one range: the plain path
     return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
@@ -345,6 +335,25 @@ cpa_status prefill_split(const void* q, cpa_dtype dtype, const void* k_pages, co
   if (cpa::launch_prefill(a, true, d, stream) != hipSuccess) return CPA_ERR_LAUNCH;
   cpa::MergeArgs m{a.part_o, a.part_lse, a.n_splits, total_q, Hq, o, lse};
   return cpa::launch_split_merge(m, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+
+// the split-KV call for either V layout (split_pages >= 1)
+cpa_status prefill_split(const void* q, cpa_dtype dtype, const void* k_pages, const void* v_pages,
+                         int64_t page_stride, int64_t head_stride, int64_t token_stride, const VLayout& vl,
+                         int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                         const int32_t* tables, int table_cap, const int32_t* counts, const int32_t* cu_q,
+                         const int32_t* prefix_len, int B, int Hq, int Hkv, int d, int max_chunk_len,
+                         float sm_scale, void* o, float* lse, int total_q, int split_pages, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (split_pages <= 0 || total_q < 0) return CPA_ERR_SHAPE;
+  cpa::PrefillArgs a;
+  bool nothing;
+  const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
+                                        n_pages, page_map, page_map_stride, tables, table_cap, counts, cu_q,
+                                        prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing);
+  if (st != CPA_OK || nothing) return st;
+  return launch_split(a, dtype, token_stride, vl, table_cap, Hq, d, o, lse, total_q, split_pages, workspace,
+                      workspace_bytes, stream);
 }
 }  // namespace
 
@@ -390,15 +399,18 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
   return cpa::launch_prefill(a, dtype == CPA_BF16, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
 
-cpa_status cpa_chunked_prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
-                                     int64_t head_stride, int64_t token_stride, const void* v_pages, int v_dim_major,
-                                     int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride,
-                                     int64_t n_pages, const int32_t* page_map, int page_map_stride,
-                                     const uint8_t* masks, int nqb_max, int nkvb_max, const int32_t* cu_q,
-                                     const int32_t* prefix_len, int B, int Hq, int Hkv, int d, int max_chunk_len,
-                                     float sm_scale, void* o, float* lse, hipStream_t stream) {
+}  // extern "C"
+
+extern "C" cpa_status cpa_chunked_prefill_fused(
+    const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride, int64_t head_stride,
+    int64_t token_stride, const void* v_pages, int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
+    int64_t v_row_stride, int64_t n_pages, const int32_t* page_map, int page_map_stride, const uint8_t* masks,
+    int nqb_max, int nkvb_max, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+    int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
   if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
   if (nqb_max < 0 || nkvb_max < 0 || nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
+  if (split_pages > 0 && total_q < 0) return CPA_ERR_SHAPE;
   cpa::PrefillArgs a;
   bool nothing;
   const VLayout vl{v_page_stride, v_head_stride, v_row_stride, v_dim_major == 1};
@@ -415,10 +427,11 @@ cpa_status cpa_chunked_prefill_fused(const void* q, cpa_dtype dtype, const void*
   a.mask_nqb = nqb_max;
   a.mask_nkvb = nkvb_max;
   a.mask_vec = (nkvb_max % 16 == 0 && aligned16(masks)) ? 1 : 0;
+  if (split_pages > 0)   // a group's table holds at most nkvb_max ids
+    return launch_split(a, dtype, token_stride, vl, nkvb_max, Hq, d, o, lse, total_q, split_pages, workspace,
+                        workspace_bytes, stream);
   return cpa::launch_prefill(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
 }
-
-}  // extern "C"
 
 // ---- split-KV without a caller workspace ---------------------------------------------------
 // cpa_chunked_prefill_split_static keeps the split partials in `scratch`, a device array of

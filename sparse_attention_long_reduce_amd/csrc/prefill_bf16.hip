@@ -76,8 +76,8 @@
 // 64-bit word.  Table position p is the p-th set bit in ascending order, so the page ids are
 // expanded from the bitmap a window chunk at a time, and the pages visited and their order are
 // exactly those of the separate table-build launch: the output is bitwise the same.  Every tile
-// of a group repeats the union (its masks are read from L2 after the first tile), which costs a
-// few microseconds per workgroup against a separate launch.
+// (and with SPLIT every range of a tile) repeats the union (its masks are read from L2 after the
+// first), which costs a few microseconds per workgroup against a separate launch.
 #include "prefill_common.h"
 #include "union_common.h"
 
@@ -163,7 +163,7 @@ using IC = std::integral_constant<int, I>;
 // The K scale is folded into the softmax scale and the V scale into the output (a.out_scale).
 template <int D, bool SPLIT, bool VT, bool F8, bool FU>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
-  static_assert(!(FU && (SPLIT || F8)), "the fused union runs the plain bf16 path");
+  static_assert(!(FU && F8), "the fused union runs the bf16 paths");
   using GE = Geo<D>;
   constexpr bool VOP = VT || F8;   // V tiles in operand order (8 keys of one dim per slot)
   constexpr int NPW = F8 ? (GE::NPW / 2 > 0 ? GE::NPW / 2 : 1) : GE::NPW;   // copies per wave and page
@@ -291,11 +291,13 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     n_iter = cnt - count_above(tab, cnt, nqb, qb0 + qi_last, lane);
     n_vis = active ? cnt - count_above(tab, cnt, nqb, qb0 + qi_w, lane) : 0;
   }
+  int toff = 0;   // FU: table position of this range's first page
   if (SPLIT) {   // this workgroup's range: the tile's pages cut into n_splits near-equal ranges
     const int len = (n_iter + a.n_splits - 1) / a.n_splits;
     const int lo = min(n_iter, split * len);
     const int hi = min(n_iter, lo + len);
-    tab += lo;
+    if constexpr (FU) toff = lo;
+    else tab += lo;
     n_vis = max(0, min(n_vis, hi) - lo);
     n_iter = max(0, hi - lo);
   }
@@ -428,16 +430,17 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
   };
   auto load_chunk = [&](int base) __attribute__((always_inline)) {
     if constexpr (FU) {
-      // entry p is the p-th set bit: lane l of the wave on word w holds entry upre[w] + (its
-      // rank among the word's set bits) when bit l is set
-      const int hi = min(base + CH, n_iter);
+      // table position p is the p-th set bit: lane l of the wave on word w holds position
+      // upre[w] + (its rank among the word's set bits) when bit l is set; the range's entry j
+      // is position toff + j
+      const int lo_p = toff + base, hi_p = toff + min(base + CH, n_iter);
       for (int w = wave; w < nwords; w += THREADS / 64) {
         const unsigned long long word = uw[w];
         const int p0 = upre[w];
-        if (p0 >= hi || p0 + (int)__popcll(word) <= base) continue;
+        if (p0 >= hi_p || p0 + (int)__popcll(word) <= lo_p) continue;
         const int pos = p0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(word >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)word, 0u));
-        if (((word >> lane) & 1ull) && pos >= base && pos < hi) resolve(pos, (w << 6) + lane);
+        if (((word >> lane) & 1ull) && pos >= lo_p && pos < hi_p) resolve(pos - toff, (w << 6) + lane);
       }
     } else {
       for (int j = tid; j < CH && base + j < n_iter; j += THREADS) resolve(base + j, tab[base + j]);
@@ -900,9 +903,14 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   const bool split = a.n_splits > 1;
   const dim3 g(grid), t(THREADS);
-  if (a.fused) {   // bf16 pages, no split
-    if (a.v_dmajor) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false, true>), g, t, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, true>), g, t, 0, s, a);
+  if (a.fused) {   // bf16 pages
+    if (a.v_dmajor) {
+      if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false, true>), g, t, 0, s, a);
+      else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false, true>), g, t, 0, s, a);
+    } else {
+      if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false, true>), g, t, 0, s, a);
+      else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false, true>), g, t, 0, s, a);
+    }
     return hipGetLastError();
   }
   if (a.kv_fp8) {   // fp8 pages, no split
@@ -932,7 +940,7 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
-  if (a.fused)   // the caller has checked: bf16, no split, no fp8, row strides within 32-bit offsets
+  if (a.fused)   // the caller has checked: bf16, no fp8, row strides within 32-bit offsets
     return d == 64 ? launch_bf16<64>(a, s) : launch_bf16<128>(a, s);
   if (a.kv_fp8 && (a.n_splits > 1 || a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
     return launch_prefill_regstaged(a, true, d, s);   // fp8 forms the direct-to-LDS kernel does not take

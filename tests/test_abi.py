@@ -223,14 +223,15 @@ def pfv(lib, dtype=1, total_q=256, split=0, ws=NULL, ws_bytes=0, vps=8 * 128 * 6
                                       a["lse"], total_q, split, ws, ws_bytes, None)
 
 
-def pfu(lib, dtype=1, vdm=1, vps=8 * 128 * 64, vhs=128 * 64, vrs=64, masks=FAKE, nqb=4, nkvb=16, **kw):
+def pfu(lib, dtype=1, vdm=1, vps=8 * 128 * 64, vhs=128 * 64, vrs=64, masks=FAKE, nqb=4, nkvb=16, total_q=256,
+        split=0, ws=NULL, ws_bytes=0, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
              cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL)
     a.update(kw)
     return lib.cpa_chunked_prefill_fused(a["q"], dtype, a["k"], a["ps"], a["hs"], a["ts"], a["v"], vdm, vps, vhs,
                                          vrs, a["npages"], a["pm"], a["pms"], masks, nqb,
                                          nkvb, a["cu"], a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["mcl"],
-                                         a["scale"], a["o"], a["lse"], None)
+                                         a["scale"], a["o"], a["lse"], total_q, split, ws, ws_bytes, None)
 
 
 def test_fused_validation(lib):
@@ -253,6 +254,13 @@ def test_fused_validation(lib):
     assert pfu(lib, npages=0) == 2
     assert pfu(lib, B=0, q=NULL, masks=NULL) == 0     # nothing to do
     assert pfu(lib, mcl=0) == 0
+    # split-KV: ranges of nkvb_max ids, the checks of cpa_chunked_prefill_split
+    assert pfu(lib, split=4) == 1                     # 4 ranges and no workspace
+    assert pfu(lib, split=4, total_q=-1) == 2
+    assert pfu(lib, split=4, ws=FAKE + 8, ws_bytes=1 << 30) == 3
+    assert pfu(lib, split=4, ws=FAKE, ws_bytes=16) == 5
+    assert lib.cpa_split_workspace_bytes(256, 32, 128, 16, 4) == 4 * 256 * 32 * 129 * 4
+    assert pfu(lib, split=16, ws=NULL, masks=NULL, nkvb=0, dtype=0) == 4   # no mask columns: NULL masks pass, dtype still checked
 
 
 def test_vt_validation(lib):

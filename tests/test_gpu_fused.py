@@ -52,21 +52,22 @@ def dim_major(vp):
     return vp.transpose(2, 3).contiguous()
 
 
-def fused(dv, w, layout, masks=None, vp=None):
+def fused(dv, w, layout, masks=None, vp=None, split=0):
     if vp is None:
         vp = dim_major(dv["vp"]) if layout == "dim" else dv["vp"]
     return cpa.chunked_prefill_fused(dv["q"], dv["kp"], vp, dv["pm"], dv["masks"] if masks is None else masks,
-                                     dv["cu"], dv["pl"], w.max_chunk_len, return_lse=True, v_layout=layout)
+                                     dv["cu"], dv["pl"], w.max_chunk_len, return_lse=True, v_layout=layout,
+                                     split_pages=split)
 
 
-def separate(dv, w, layout, masks=None, vp=None):
-    """The table-build launch, then the prefill launch on its tables."""
+def separate(dv, w, layout, masks=None, vp=None, split=0):
+    """The table-build launch, then the prefill launch on its tables (capacity: the masks' width)."""
     if vp is None:
         vp = dim_major(dv["vp"]) if layout == "dim" else dv["vp"]
     m = dv["masks"] if masks is None else masks
     tables, counts = cpa.build_block_tables(m, dv["pb"], dv["cb"], w.Hkv, table_cap=max(m.shape[3], 1))
     return cpa.chunked_prefill(dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
-                               return_lse=True, v_layout=layout)
+                               return_lse=True, v_layout=layout, split_pages=split)
 
 
 def assert_bitwise(a, b, what):
@@ -75,14 +76,15 @@ def assert_bitwise(a, b, what):
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), f"{what}: LSEs differ"
 
 
+@pytest.mark.parametrize("split", [0, 3])
 @pytest.mark.parametrize("layout", ["dim", "token"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_fused_small(name, layout):
+def test_fused_small(name, layout, split):
     w = make_small(name)
-    print(f"\n[case] fused {name} v_layout={layout}", flush=True)
+    print(f"\n[case] fused {name} v_layout={layout} split_pages={split}", flush=True)
     dv = upload(w)
-    got = fused(dv, w, layout)
-    ref = separate(dv, w, layout)
+    got = fused(dv, w, layout, split=split)
+    ref = separate(dv, w, layout, split=split)
     torch.cuda.synchronize()
     assert_bitwise(got, ref, name)
     T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
@@ -151,13 +153,19 @@ def test_fused_nothing_to_do():
 
 @pytest.mark.parametrize("name,layout", [("c3_128k_last_chunk", "dim"), ("c3_128k_last_chunk", "token"),
                                          ("c5b_varlen_independent", "dim"), ("c3g7_128k_gqa7", "dim"),
-                                         ("c4_128k_chunked_batch", "dim")])
+                                         ("c4_128k_chunked_batch", "dim"), ("c3s_128k_one_group", "dim"),
+                                         ("c3s_128k_one_group", "token")])
 def test_fused_full_size(name, layout):
     print(f"\n[case] fused full {name} v_layout={layout}", flush=True)
     w = chunked_sequence_batch() if name == "c4_128k_chunked_batch" else make_config(name)
     dv = upload(w)
-    got = fused(dv, w, layout)
-    ref = separate(dv, w, layout)
+    sp = 0
+    if name.startswith("c3s"):   # one KV group: split-KV, as the bench runs it
+        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+        sp = cpa.plan_split_pages(w.B, w.Hq, w.Hkv, w.max_chunk_len, w.nkvb_max, n_cus)
+        assert sp > 0
+    got = fused(dv, w, layout, split=sp)
+    ref = separate(dv, w, layout, split=sp)
     torch.cuda.synchronize()
     assert_bitwise(got, ref, name)
     o, lse = got

@@ -159,15 +159,13 @@ def run_case(i, c, wseed, rseed):
         compare(w, od, Od, f"sweep {i} direct")
         check_lse(ld, Ld, 2 ** -7)
 
-        # the table build in the prefill's prologue: bitwise the separate (unsplit) launches
+        # the table build in the prefill's prologue: bitwise the separate launches, split or not
         of, lf = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"],
-                                           w.max_chunk_len, return_lse=True, v_layout=c["v_layout"])
-        ou, lu = (o, lse) if not c["split"] else cpa.chunked_prefill(
-            dv["q"], kp, vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len, return_lse=True,
-            v_layout=c["v_layout"])
+                                           w.max_chunk_len, return_lse=True, v_layout=c["v_layout"],
+                                           split_pages=c["split"])
         torch.cuda.synchronize()
-        assert torch.equal(of.view(torch.int16), ou.view(torch.int16)), f"sweep {i} fused output"
-        assert torch.equal(lf.view(torch.int32), lu.view(torch.int32)), f"sweep {i} fused LSE"
+        assert torch.equal(of.view(torch.int16), o.view(torch.int16)), f"sweep {i} fused output"
+        assert torch.equal(lf.view(torch.int32), lse.view(torch.int32)), f"sweep {i} fused LSE"
 
 
 N_LONG = int(os.environ.get("CPA_SWEEP_LONG_CASES", "12"))
@@ -210,10 +208,8 @@ def test_sweep_long(i):
     assert np.max(np.abs(lse[r, h].cpu().numpy() - Ls)) < (1e-4 if c["mode"] == "f32" else 2 ** -7)
     if c["mode"] == "bf16":   # the fused launch expands these long tables from its bitmap, window by window
         of, lf = cpa.chunked_prefill_fused(dv["q"], dv["kp"], vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"],
-                                           w.max_chunk_len, return_lse=True, v_layout=c["v_layout"])
-        ou, lu = (o, lse) if not c["split"] else cpa.chunked_prefill(
-            dv["q"], dv["kp"], vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len, return_lse=True,
-            v_layout=c["v_layout"])
+                                           w.max_chunk_len, return_lse=True, v_layout=c["v_layout"],
+                                           split_pages=c["split"])
         torch.cuda.synchronize()
-        assert torch.equal(of.view(torch.int16), ou.view(torch.int16)), f"long sweep {i} fused output"
-        assert torch.equal(lf.view(torch.int32), lu.view(torch.int32)), f"long sweep {i} fused LSE"
+        assert torch.equal(of.view(torch.int16), o.view(torch.int16)), f"long sweep {i} fused output"
+        assert torch.equal(lf.view(torch.int32), lse.view(torch.int32)), f"long sweep {i} fused LSE"
