@@ -318,15 +318,21 @@ def time_fused(cpa, batches, steps, warmup=3):
     events around each step.  Also checks that their outputs are equal bit for bit."""
     import numpy as np
     import torch
+    from workloads.configs import pack_mask_bits
     outs = [torch.empty_like(bt.q) for bt in batches]
     lses = [torch.empty_like(bt.lse) for bt in batches]
+    outs_b = [torch.empty_like(bt.q) for bt in batches]
+    lses_b = [torch.empty_like(bt.lse) for bt in batches]
+    bits = [torch.from_numpy(pack_mask_bits(bt.w.masks).view(np.int64)).to(bt.q.device) for bt in batches]
 
-    def fused_step():
-        for o, l, bt in zip(outs, lses, batches):
+    def fused_step(from_bits=False):
+        for i, bt in enumerate(batches):
             dim = bt.v_layout == "dim"
-            cpa.chunked_prefill_fused(bt.q, bt.kp, bt.vp_dim if dim else bt.vp, bt.pm, bt.masks, bt.cu, bt.pl,
+            m, o, l = (bits[i], outs_b[i], lses_b[i]) if from_bits else (bt.masks, outs[i], lses[i])
+            cpa.chunked_prefill_fused(bt.q, bt.kp, bt.vp_dim if dim else bt.vp, bt.pm, m, bt.cu, bt.pl,
                                       bt.w.max_chunk_len, out=o, lse=l, v_layout=bt.v_layout,
-                                      split_pages=bt.split_pages, workspace=bt.workspace)
+                                      split_pages=bt.split_pages, workspace=bt.workspace,
+                                      nkvb_max=bt.w.nkvb_max if from_bits else None)
 
     def separate_step():
         for bt in batches:
@@ -336,7 +342,8 @@ def time_fused(cpa, batches, steps, warmup=3):
     for _ in range(warmup):
         separate_step()
         fused_step()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        fused_step(True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     for e in ev:
         e[0].record()
         separate_step()
@@ -344,15 +351,22 @@ def time_fused(cpa, batches, steps, warmup=3):
         e[2].record()
         fused_step()
         e[3].record()
+        e[4].record()
+        fused_step(True)
+        e[5].record()
     torch.cuda.synchronize()
     sep = np.array([e[0].elapsed_time(e[1]) for e in ev])
     fu = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    equal = all(torch.equal(o.view(torch.int16), bt.out.view(torch.int16))
-                and torch.equal(l.view(torch.int32), bt.lse.view(torch.int32))
-                for o, l, bt in zip(outs, lses, batches))
+    fb = np.array([e[4].elapsed_time(e[5]) for e in ev])
+
+    def same(os_, ls_):
+        return all(torch.equal(o.view(torch.int16), bt.out.view(torch.int16))
+                   and torch.equal(l.view(torch.int32), bt.lse.view(torch.int32))
+                   for o, l, bt in zip(os_, ls_, batches))
     return {"step_ms": float(fu.mean()), "step_ms_median": float(np.median(fu)), "step_ms_min": float(fu.min()),
             "separate_step_ms": float(sep.mean()), "separate_step_ms_median": float(np.median(sep)),
-            "launches_per_step": len(batches), "outputs_equal_separate": bool(equal)}
+            "bits_step_ms": float(fb.mean()), "launches_per_step": len(batches),
+            "outputs_equal_separate": bool(same(outs, lses) and same(outs_b, lses_b))}
 
 
 def time_graph(cpa, batches, steps):
@@ -619,13 +633,16 @@ def main():
     fused = {"step_ms": round(fu["step_ms"], 4), "step_ms_median": round(fu["step_ms_median"], 4),
              "step_ms_min": round(fu["step_ms_min"], 4), "separate_step_ms": round(fu["separate_step_ms"], 4),
              "speedup_over_separate": round(fu["separate_step_ms"] / fu["step_ms"], 4),
+             "bit_masks_step_ms": round(fu["bits_step_ms"], 4),
              "launches_per_step": fu["launches_per_step"],
              "outputs_equal_separate": fu["outputs_equal_separate"],
              "note": "cpa_chunked_prefill_fused: each prefill workgroup builds its group's union from the "
                      "masks in its prologue; one launch per launch pair instead of two; timed step by step "
-                     "in turn with the separate launches"}
-    log(f"[bench] fused union in the prefill prologue: step {fu['step_ms']:.3f} ms vs separate "
-        f"{fu['separate_step_ms']:.3f} ms (interleaved), outputs equal: {fu['outputs_equal_separate']}")
+                     "in turn with the separate launches and with the same launch from bit-packed masks "
+                     "(cpa_chunked_prefill_fused_bits); outputs_equal_separate covers both"}
+    log(f"[bench] fused union in the prefill prologue: step {fu['step_ms']:.3f} ms ({fu['bits_step_ms']:.3f} ms from "
+        f"bit masks) vs separate {fu['separate_step_ms']:.3f} ms (in turn), outputs equal: "
+        f"{fu['outputs_equal_separate']}")
     bits = time_build_bits(cpa, batches, max(5, args.steps))
     log(f"[bench] table build from bit-packed masks: {bits['us']:.1f} us ({bits['mask_bytes']} mask bytes), "
         f"tables equal: {bits['tables_equal_byte_masks']}")

@@ -303,6 +303,28 @@ cpa_status cpa_chunked_prefill_fused(const void* q, cpa_dtype dtype, const void*
                                      hipStream_t stream);
 
 /*
+ * cpa_chunked_prefill_fused_bits - cpa_chunked_prefill_fused from bit-packed masks: the union in
+ * each workgroup's prologue reads one bit per (query head, query block, KV block), 8x fewer
+ * mask bytes.  The result is bitwise that of cpa_chunked_prefill_fused on the unpacked masks
+ * (and of cpa_build_block_tables_bits followed by cpa_chunked_prefill(_vt)).
+ *
+ *   mask_bits, mask_words  as cpa_build_block_tables_bits (uint64 [B][Hq][nqb_max][mask_words],
+ *            mask_words >= ceil(nkvb_max / 64), 8-byte aligned; bits at or past nkvb_max and
+ *            outside the causal region are ignored).
+ * Other arguments, support and errors as cpa_chunked_prefill_fused, plus CPA_ERR_SHAPE for
+ * mask_words < ceil(nkvb_max / 64) and CPA_ERR_ALIGN for a misaligned mask_bits.
+ */
+cpa_status cpa_chunked_prefill_fused_bits(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                                          int64_t head_stride, int64_t token_stride, const void* v_pages,
+                                          int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
+                                          int64_t v_row_stride, int64_t n_pages, const int32_t* page_map,
+                                          int page_map_stride, const uint64_t* mask_bits, int nqb_max, int nkvb_max,
+                                          int mask_words, const int32_t* cu_q, const int32_t* prefix_len, int B,
+                                          int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o,
+                                          float* lse, int total_q, int split_pages, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
+
+/*
  * cpa_append_kv - write each sequence's chunk of new K and V rows into the paged cache, the step
  * before attention in chunked prefill (CompactAttention abstract: the chunk attends over KV
  * blocks that live in a paged cache and are read in place, so its own K/V must be there).

@@ -7,6 +7,7 @@ LIB_PATH = os.path.join(_HERE, "libcpa.so")
 
 EXPORTS = ("cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables", "cpa_build_block_tables_bits",
            "cpa_chunked_prefill", "cpa_chunked_prefill_direct", "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_fused",
+           "cpa_chunked_prefill_fused_bits",
            "cpa_chunked_prefill_split", "cpa_chunked_prefill_split_static", "cpa_chunked_prefill_vt",
            "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version")
 
@@ -40,6 +41,10 @@ def load():
     lib.cpa_chunked_prefill_fused.argtypes = [vp, i32, vp, i64, i64, i64, vp, i32, i64, i64, i64, i64, vp, i32, vp,
                                               i32, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, i32, i32,
                                               vp, c.c_size_t, vp]
+    lib.cpa_chunked_prefill_fused_bits.restype = i32
+    lib.cpa_chunked_prefill_fused_bits.argtypes = [vp, i32, vp, i64, i64, i64, vp, i32, i64, i64, i64, i64, vp, i32,
+                                                   vp, i32, i32, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp,
+                                                   i32, i32, vp, c.c_size_t, vp]
     lib.cpa_chunked_prefill.restype = i32
     lib.cpa_chunked_prefill.argtypes = [vp, i32, vp, vp, i64, i64, i64, i64, vp, i32, vp, i32, vp,
                                         vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]

@@ -361,12 +361,14 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
 
 def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len, sm_scale=0.0,
                           out=None, lse=None, return_lse=False, stream=None, v_layout="token", split_pages=0,
-                          workspace=None):
+                          workspace=None, nkvb_max=None):
     """The table build and the prefill in one launch (cpa_chunked_prefill_fused): every
     workgroup ORs its KV group's rows of masks (uint8 [B][Hq][nqb_max][nkvb_max]) itself, with
     prefix_blocks = prefix_len / 64 and chunk_blocks = ceil(chunk length / 64).  Bitwise the
     result of build_block_tables followed by chunked_prefill on the same inputs (tables of
     capacity nkvb_max).  bf16 q and pools; k_pages / v_pages / v_layout as in chunked_prefill.
+    Bit-packed masks (int64 [B][Hq][nqb_max][mask_words], as build_block_tables_bits takes them)
+    need nkvb_max and run cpa_chunked_prefill_fused_bits.
     split_pages > 0 (or "auto") runs split-KV as chunked_prefill does, with nkvb_max as the table
     capacity; the workspace is allocated here when not given."""
     auto = isinstance(split_pages, str)
@@ -388,9 +390,13 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
         raise ValueError("v_layout must be 'token' or 'dim'")
     if v_pages.dim() != 4 or tuple(v_pages.shape) != vshape or v_pages.stride(3) != 1:
         raise ValueError(f"v_pages must be {list(vshape)} with the last dimension contiguous")
-    if not (isinstance(masks, torch.Tensor) and masks.dtype == torch.uint8 and masks.dim() == 4
+    if not (isinstance(masks, torch.Tensor) and masks.dtype in (torch.uint8, torch.int64) and masks.dim() == 4
             and masks.is_contiguous()):
-        raise TypeError("masks must be a contiguous uint8 [B][Hq][nqb_max][nkvb_max] tensor")
+        raise TypeError("masks must be a contiguous uint8 [B][Hq][nqb_max][nkvb_max] or int64 "
+                        "[B][Hq][nqb_max][mask_words] (bit-packed) tensor")
+    bits = masks.dtype == torch.int64
+    if bits and nkvb_max is None:
+        raise ValueError("bit-packed masks need nkvb_max")
     for t, nm in ((page_map, "page_map"), (cu_q, "cu_q"), (prefix_len, "prefix_len")):
         _i32(t, nm)
     B = prefix_len.numel()
@@ -400,7 +406,8 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
         raise ValueError("inconsistent B across cu_q / prefix_len / page_map / masks")
     dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, masks=masks, cu_q=cu_q,
               prefix_len=prefix_len)
-    nqb_max, nkvb_max = masks.shape[2], masks.shape[3]
+    nqb_max = masks.shape[2]
+    nkvb_max = int(nkvb_max) if bits else masks.shape[3]
     if auto:
         splittable = max(k_pages.stride(2), v_pages.stride(2)) <= (1 << 24)
         n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -413,15 +420,20 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             _on(dev, workspace=workspace)
-        st = load().cpa_chunked_prefill_fused(
-            _ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
-            1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages,
-            _ptr(page_map), page_map.shape[1], _ptr(masks), nqb_max, nkvb_max, _ptr(cu_q),
-            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq,
-            int(split_pages) if split else 0, _ptr(workspace) if split else None,
-            workspace.numel() * workspace.element_size() if split else 0, _stream(stream, dev))
+        head = (_ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
+                _ptr(v_pages), 1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2),
+                n_pages, _ptr(page_map), page_map.shape[1], _ptr(masks), nqb_max, nkvb_max)
+        tail = (_ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
+                _ptr(lse), Tq, int(split_pages) if split else 0, _ptr(workspace) if split else None,
+                workspace.numel() * workspace.element_size() if split else 0, _stream(stream, dev))
+        if bits:
+            name = "cpa_chunked_prefill_fused_bits"
+            st = load().cpa_chunked_prefill_fused_bits(*head, masks.shape[3], *tail)
+        else:
+            name = "cpa_chunked_prefill_fused"
+            st = load().cpa_chunked_prefill_fused(*head, *tail)
     if st != 0:
-        raise CpaError(st, "cpa_chunked_prefill_fused")
+        raise CpaError(st, name)
     return out, lse
 
 

@@ -111,59 +111,11 @@ __global__ __launch_bounds__(UT) void block_union_kernel(const UnionArgs a) {
   __syncthreads();
 
   // ---- phase 1: OR over (head in group, query block), causal clip per row -----------------
-  if (BITS) {
-    // column c = word c (KV blocks 64c .. 64c+63); row t as in the byte path below
-    int lgw = 0;
-    while ((1 << lgw) < nwords && (1 << lgw) < UT) ++lgw;
-    const int colw = 1 << lgw;
-    const int rs = UT >> lgw;
-    const size_t wstride = (size_t)a.mask_words;
+  if (BITS) {   // union_bit_rows (union_common.h)
     const unsigned long long* wbase =
-        a.mask_bits + ((size_t)b * a.Hq + (size_t)g * G) * a.nqb_max * wstride;
-    unsigned long long* redw = reinterpret_cast<unsigned long long*>(red);
-    for (int c0 = 0; c0 < nwords; c0 += colw) {
-      const int c = c0 + (tid & (colw - 1));
-      const int s = tid >> lgw;
-      unsigned long long acc = 0ull;
-      if (c < nwords) {
-        const int kb0 = c << 6;
-        const int qi_lo = max(0, kb0 - qb0);
-        const int nq = nqb - qi_lo;   // >= 1: c < nwords
-        const int nrows = G * nq;
-        // row t = (head hh, query block qi_lo + qr), walked from t = s in steps of rs rows
-        // without a division per row
-        int hh = s / nq, qr = s - (s / nq) * nq;
-        const int dh = rs / nq, dq = rs - (rs / nq) * nq;
-        for (int t0 = s; t0 < nrows; t0 += 4 * rs) {
-          unsigned long long v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            v[u] = 0ull;
-            if (t0 + u * rs < nrows) {
-              const int qi = qi_lo + qr;
-              v[u] = wbase[((size_t)hh * a.nqb_max + qi) * wstride + c];
-              const int nallow = qb0 + qi - kb0 + 1;   // bits 0 .. nallow-1 are causally reachable (>= 1)
-              if (nallow < 64) v[u] &= (1ull << nallow) - 1ull;
-            }
-            qr += dq;
-            hh += dh;
-            if (qr >= nq) {
-              qr -= nq;
-              ++hh;
-            }
-          }
-          acc |= (v[0] | v[1]) | (v[2] | v[3]);
-        }
-      }
-      redw[tid] = acc;
-      __syncthreads();
-      for (int h = rs >> 1; h >= 1; h >>= 1) {   // tree OR over the row splits of a column
-        if (s < h) redw[tid] |= redw[tid + (h << lgw)];
-        __syncthreads();
-      }
-      if (s == 0 && c < nwords) words[c] = redw[tid];
-      __syncthreads();
-    }
+        a.mask_bits + ((size_t)b * a.Hq + (size_t)g * G) * a.nqb_max * (size_t)a.mask_words;
+    union_bit_rows<UT, 4>(wbase, (size_t)a.mask_words, a.nqb_max, G, qb0, nqb, words,
+                          reinterpret_cast<unsigned long long*>(red));
   } else {   // union_byte_rows (union_common.h)
     const uint8_t* gbase = a.masks + ((size_t)b * a.Hq + (size_t)g * G) * a.nqb_max * (size_t)a.nkvb_max;
     union_byte_rows<UT, 4, VEC>(gbase, (size_t)a.nkvb_max, a.nqb_max, G, qb0, nqb, a.nkvb_max, words, red);

@@ -401,15 +401,21 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
 
 }  // extern "C"
 
-extern "C" cpa_status cpa_chunked_prefill_fused(
-    const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride, int64_t head_stride,
-    int64_t token_stride, const void* v_pages, int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
-    int64_t v_row_stride, int64_t n_pages, const int32_t* page_map, int page_map_stride, const uint8_t* masks,
-    int nqb_max, int nkvb_max, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
-    int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages, void* workspace,
-    size_t workspace_bytes, hipStream_t stream) {
+namespace {
+// The fused entry points: argument checks shared with the table-based calls, then one launch
+// (or the split launches) with the masks in place of the tables.  bits: mask_bits / mask_words
+// instead of the byte masks.
+cpa_status prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
+                         int64_t head_stride, int64_t token_stride, const void* v_pages, int v_dim_major,
+                         int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride, int64_t n_pages,
+                         const int32_t* page_map, int page_map_stride, const uint8_t* masks,
+                         const uint64_t* mask_bits, bool bits, int nqb_max, int nkvb_max, int mask_words,
+                         const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+                         int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
   if (nqb_max < 0 || nkvb_max < 0 || nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
+  if (bits && (mask_words < 0 || mask_words < (nkvb_max + 63) / 64)) return CPA_ERR_SHAPE;
   if (split_pages > 0 && total_q < 0) return CPA_ERR_SHAPE;
   cpa::PrefillArgs a;
   bool nothing;
@@ -419,18 +425,52 @@ extern "C" cpa_status cpa_chunked_prefill_fused(
                                         B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing,
                                         /*kv_elem_bytes=*/0, /*with_tables=*/false);
   if (st != CPA_OK || nothing) return st;
-  if (!masks && nqb_max > 0 && nkvb_max > 0) return CPA_ERR_NULL;
+  const bool need = nqb_max > 0 && nkvb_max > 0;   // there are mask entries to read
+  if (bits ? (need && !mask_bits) : (need && !masks)) return CPA_ERR_NULL;
+  if (bits && ((uintptr_t)mask_bits & 7u) != 0) return CPA_ERR_ALIGN;
   // the direct-to-LDS bf16 kernel: 32-bit offsets within a page
   if (dtype != CPA_BF16 || token_stride > (1 << 24) || v_row_stride > (1 << 24)) return CPA_ERR_UNSUPPORTED;
   a.fused = 1;
-  a.masks = masks;
   a.mask_nqb = nqb_max;
   a.mask_nkvb = nkvb_max;
-  a.mask_vec = (nkvb_max % 16 == 0 && aligned16(masks)) ? 1 : 0;
+  if (bits) {   // a NULL mask_bits (nothing to read) runs the byte path, which then reads nothing
+    a.mask_bits = reinterpret_cast<const unsigned long long*>(mask_bits);
+    a.mask_words = mask_words;
+  } else {
+    a.masks = masks;
+    a.mask_vec = (nkvb_max % 16 == 0 && aligned16(masks)) ? 1 : 0;
+  }
   if (split_pages > 0)   // a group's table holds at most nkvb_max ids
     return launch_split(a, dtype, token_stride, vl, nkvb_max, Hq, d, o, lse, total_q, split_pages, workspace,
                         workspace_bytes, stream);
   return cpa::launch_prefill(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" cpa_status cpa_chunked_prefill_fused(
+    const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride, int64_t head_stride,
+    int64_t token_stride, const void* v_pages, int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
+    int64_t v_row_stride, int64_t n_pages, const int32_t* page_map, int page_map_stride, const uint8_t* masks,
+    int nqb_max, int nkvb_max, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
+    int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  return prefill_fused(q, dtype, k_pages, page_stride, head_stride, token_stride, v_pages, v_dim_major,
+                       v_page_stride, v_head_stride, v_row_stride, n_pages, page_map, page_map_stride, masks, nullptr,
+                       false, nqb_max, nkvb_max, 0, cu_q, prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse,
+                       total_q, split_pages, workspace, workspace_bytes, stream);
+}
+
+extern "C" cpa_status cpa_chunked_prefill_fused_bits(
+    const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride, int64_t head_stride,
+    int64_t token_stride, const void* v_pages, int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
+    int64_t v_row_stride, int64_t n_pages, const int32_t* page_map, int page_map_stride, const uint64_t* mask_bits,
+    int nqb_max, int nkvb_max, int mask_words, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq,
+    int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return prefill_fused(q, dtype, k_pages, page_stride, head_stride, token_stride, v_pages, v_dim_major,
+                       v_page_stride, v_head_stride, v_row_stride, n_pages, page_map, page_map_stride, nullptr,
+                       mask_bits, true, nqb_max, nkvb_max, mask_words, cu_q, prefix_len, B, Hq, Hkv, d,
+                       max_chunk_len, sm_scale, o, lse, total_q, split_pages, workspace, workspace_bytes, stream);
 }
 
 // ---- split-KV without a caller workspace ---------------------------------------------------

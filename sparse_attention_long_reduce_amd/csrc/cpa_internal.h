@@ -74,6 +74,10 @@ struct PrefillArgs {
   int fused;
   const uint8_t* masks;
   int mask_nqb, mask_nkvb, mask_vec;
+  // fused from bit-packed masks (masks unused): uint64 [B][Hq][mask_nqb][mask_words], bit kb % 64
+  // of word kb / 64 = block kb selected
+  const unsigned long long* mask_bits;
+  int mask_words;
 };
 
 struct MergeArgs {

@@ -72,7 +72,8 @@
 //
 // Fused block union (FU): no table is given.  Each workgroup first ORs the masks of its KV
 // group (the G heads over the chunk's query blocks, causally clipped) into an LDS bitmap with
-// the table-build kernel's own routine (union_byte_rows), and counts the set bits before each
+// the table-build kernel's own routines (union_byte_rows, or union_bit_rows for bit-packed
+// masks), and counts the set bits before each
 // 64-bit word.  Table position p is the p-th set bit in ascending order, so the page ids are
 // expanded from the bitmap a window chunk at a time, and the pages visited and their order are
 // exactly those of the separate table-build launch: the output is bitwise the same.  Every tile
@@ -222,12 +223,19 @@ __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs
     for (int w = tid; w < nwords; w += THREADS) uw[w] = 0ull;
     __syncthreads();
     uint4* red = reinterpret_cast<uint4*>(kR0);   // scratch until the first page copies
-    const uint8_t* gbase = a.masks + ((size_t)b * a.Hq + (size_t)g * a.G) * a.mask_nqb * (size_t)a.mask_nkvb;
-    if (a.mask_vec)
-      union_byte_rows<THREADS, 8, true>(gbase, (size_t)a.mask_nkvb, a.mask_nqb, a.G, uqb0, unqb, a.mask_nkvb, uw, red);
-    else
-      union_byte_rows<THREADS, 8, false>(gbase, (size_t)a.mask_nkvb, a.mask_nqb, a.G, uqb0, unqb, a.mask_nkvb, uw,
-                                         red);
+    const size_t grow = ((size_t)b * a.Hq + (size_t)g * a.G) * a.mask_nqb;   // the group's first row
+    if (a.mask_bits != nullptr) {
+      union_bit_rows<THREADS, 8>(a.mask_bits + grow * a.mask_words, (size_t)a.mask_words, a.mask_nqb, a.G, uqb0, unqb,
+                                 uw, reinterpret_cast<unsigned long long*>(red));
+    } else {
+      const uint8_t* gbase = a.masks + grow * a.mask_nkvb;
+      if (a.mask_vec)
+        union_byte_rows<THREADS, 8, true>(gbase, (size_t)a.mask_nkvb, a.mask_nqb, a.G, uqb0, unqb, a.mask_nkvb, uw,
+                                          red);
+      else
+        union_byte_rows<THREADS, 8, false>(gbase, (size_t)a.mask_nkvb, a.mask_nqb, a.G, uqb0, unqb, a.mask_nkvb, uw,
+                                           red);
+    }
     // exclusive prefix of the set bits over words: within waves by shuffles, then over the
     // wave totals
     constexpr int WPT = MAX_KV_WORDS / THREADS;

@@ -135,4 +135,67 @@ __device__ __forceinline__ void union_byte_rows(const uint8_t* gbase, size_t row
   }
 }
 
+// OR of the bit-packed mask rows of one (sequence, KV group) into a bitmap, called by all NT
+// threads of a workgroup: the same union and causal clip as union_byte_rows, for rows of
+// mask_words 64-bit words (bit kb % 64 of word kb / 64 = block kb selected).  Row (head hh,
+// query block qi) starts at wbase + (hh * nqb_rows + qi) * wstride.  words[] holds
+// ceil((qb0 + nqb) / 64) words and must be zero on entry; redw is NT x 8 bytes of LDS scratch.
+// Ends with a barrier.  A thread ORs whole words of its column over its rows (RIF loads in
+// flight), the clip is a word mask, and the row splits of a column meet by a tree.
+template <int NT, int RIF>
+__device__ __forceinline__ void union_bit_rows(const unsigned long long* wbase, size_t wstride, int nqb_rows,
+                                               int G, int qb0, int nqb, unsigned long long* words,
+                                               unsigned long long* redw) {
+  const int tid = threadIdx.x;
+  const int nwords = (qb0 + nqb + 63) >> 6;
+  int lgw = 0;
+  while ((1 << lgw) < nwords && (1 << lgw) < NT) ++lgw;
+  const int colw = 1 << lgw;
+  const int rs = NT >> lgw;
+  for (int c0 = 0; c0 < nwords; c0 += colw) {
+    const int c = c0 + (tid & (colw - 1));
+    const int s = tid >> lgw;
+    unsigned long long acc = 0ull;
+    const int kb0 = c << 6;
+    const int qi_lo = max(0, kb0 - qb0);
+    const int nq = nqb - qi_lo;
+    if (c < nwords && nq > 0) {
+      const int nrows = G * nq;
+      // row t = (head hh, query block qi_lo + qr), walked from t = s in steps of rs rows
+      // without a division per row
+      int hh = s / nq, qr = s - (s / nq) * nq;
+      const int dh = rs / nq, dq = rs - (rs / nq) * nq;
+      for (int t0 = s; t0 < nrows; t0 += RIF * rs) {
+        unsigned long long v[RIF];
+#pragma unroll
+        for (int u = 0; u < RIF; ++u) {
+          v[u] = 0ull;
+          if (t0 + u * rs < nrows) {
+            const int qi = qi_lo + qr;
+            v[u] = wbase[((size_t)hh * nqb_rows + qi) * wstride + c];
+            const int nallow = qb0 + qi - kb0 + 1;   // bits 0 .. nallow-1 are causally reachable (>= 1)
+            if (nallow < 64) v[u] &= (1ull << nallow) - 1ull;
+          }
+          qr += dq;
+          hh += dh;
+          if (qr >= nq) {
+            qr -= nq;
+            ++hh;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < RIF; ++u) acc |= v[u];
+      }
+    }
+    redw[tid] = acc;
+    __syncthreads();
+    for (int h = rs >> 1; h >= 1; h >>= 1) {   // tree OR over the row splits of a column
+      if (s < h) redw[tid] |= redw[tid + (h << lgw)];
+      __syncthreads();
+    }
+    if (s == 0 && c < nwords) words[c] = redw[tid];
+    __syncthreads();
+  }
+}
+
 }  // namespace cpa

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"cpa_append_kv", "cpa_build_block_plans", "cpa_build_block_tables",
                           "cpa_build_block_tables_bits", "cpa_chunked_prefill", "cpa_chunked_prefill_direct",
-                          "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_fused", "cpa_chunked_prefill_split",
+                          "cpa_chunked_prefill_fp8kv", "cpa_chunked_prefill_fused", "cpa_chunked_prefill_fused_bits",
+                          "cpa_chunked_prefill_split",
                           "cpa_chunked_prefill_split_static",
                           "cpa_chunked_prefill_vt", "cpa_split_workspace_bytes", "cpa_status_string", "cpa_version"}
     for n in names:
@@ -261,6 +262,27 @@ def test_fused_validation(lib):
     assert pfu(lib, split=4, ws=FAKE, ws_bytes=16) == 5
     assert lib.cpa_split_workspace_bytes(256, 32, 128, 16, 4) == 4 * 256 * 32 * 129 * 4
     assert pfu(lib, split=16, ws=NULL, masks=NULL, nkvb=0, dtype=0) == 4   # no mask columns: NULL masks pass, dtype still checked
+
+
+def pfb(lib, masks=FAKE, nqb=4, nkvb=100, words=2, dtype=1, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
+             cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL)
+    a.update(kw)
+    return lib.cpa_chunked_prefill_fused_bits(a["q"], dtype, a["k"], a["ps"], a["hs"], a["ts"], a["v"], 1,
+                                              8 * 128 * 64, 128 * 64, 64, a["npages"], a["pm"], a["pms"], masks, nqb,
+                                              nkvb, words, a["cu"], a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"],
+                                              a["mcl"], a["scale"], a["o"], a["lse"], 256, 0, NULL, 0, None)
+
+
+def test_fused_bits_validation(lib):
+    assert pfb(lib, words=1) == 2                     # 100 blocks need two 64-bit words per row
+    assert pfb(lib, nkvb=65537, words=1025) == 2
+    assert pfb(lib, masks=NULL) == 1
+    assert pfb(lib, masks=FAKE + 4) == 3              # 8-byte alignment
+    assert pfb(lib, dtype=0) == 4
+    assert pfb(lib, masks=NULL, nkvb=0, words=0, dtype=0) == 4   # nothing to read: NULL passes
+    assert pfb(lib, q=NULL) == 1
+    assert pfb(lib, B=0, q=NULL, masks=NULL) == 0
 
 
 def test_vt_validation(lib):

@@ -9,7 +9,7 @@ import torch
 import oracle
 import sparse_attention_long_reduce_amd as cpa
 from workloads import make_config, make_workload
-from workloads.configs import chunked_sequence_batch, mask_all, mask_bernoulli
+from workloads.configs import chunked_sequence_batch, mask_all, mask_bernoulli, pack_mask_bits
 
 from _gpu import compare, error_stats, report, upload
 
@@ -60,6 +60,14 @@ def fused(dv, w, layout, masks=None, vp=None, split=0):
                                      split_pages=split)
 
 
+def fused_bits(dv, w, layout, split=0):
+    """The fused launch from the bit-packed form of the workload's masks."""
+    vp = dim_major(dv["vp"]) if layout == "dim" else dv["vp"]
+    bits = torch.from_numpy(pack_mask_bits(w.masks).view(np.int64)).cuda()
+    return cpa.chunked_prefill_fused(dv["q"], dv["kp"], vp, dv["pm"], bits, dv["cu"], dv["pl"], w.max_chunk_len,
+                                     return_lse=True, v_layout=layout, split_pages=split, nkvb_max=w.nkvb_max)
+
+
 def separate(dv, w, layout, masks=None, vp=None, split=0):
     """The table-build launch, then the prefill launch on its tables (capacity: the masks' width)."""
     if vp is None:
@@ -87,6 +95,7 @@ def test_fused_small(name, layout, split):
     ref = separate(dv, w, layout, split=split)
     torch.cuda.synchronize()
     assert_bitwise(got, ref, name)
+    assert_bitwise(fused_bits(dv, w, layout, split=split), ref, f"{name} from bit-packed masks")
     T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
     O, L = oracle.paged_attention(w.q, w.k_pages, w.v_pages, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
     o, lse = got
@@ -143,6 +152,27 @@ def test_fused_mask_values_do_not_matter():
     assert_bitwise(fused(dv, w, "dim", masks=m), fused(dv, w, "dim"), "byte values")
 
 
+def test_fused_bits_wider_rows_and_validation():
+    # rows of more words than the blocks need (the extra bits are noise the clip drops), and the
+    # binding's refusal of bit-packed masks without their block count
+    w = make_small("g4_bf16_d64_noise")
+    dv = upload(w)
+    packed = pack_mask_bits(w.masks).view(np.int64)
+    wide = np.full(packed.shape[:-1] + (packed.shape[-1] + 2,), -1, dtype=np.int64)
+    wide[..., :packed.shape[-1]] = packed
+    last = w.nkvb_max % 64
+    if last:   # noise past nkvb_max in the last real word
+        wide[..., packed.shape[-1] - 1] |= np.int64(-1) << np.int64(last)
+    m = torch.from_numpy(wide).cuda()
+    for layout in ("dim", "token"):
+        vp = dim_major(dv["vp"]) if layout == "dim" else dv["vp"]
+        got = cpa.chunked_prefill_fused(dv["q"], dv["kp"], vp, dv["pm"], m, dv["cu"], dv["pl"], w.max_chunk_len,
+                                        return_lse=True, v_layout=layout, nkvb_max=w.nkvb_max)
+        assert_bitwise(got, separate(dv, w, layout), f"wide bit rows {layout}")
+    with pytest.raises(ValueError, match="nkvb_max"):
+        cpa.chunked_prefill_fused(dv["q"], dv["kp"], dv["vp"], dv["pm"], m, dv["cu"], dv["pl"], w.max_chunk_len)
+
+
 def test_fused_nothing_to_do():
     w = make_small("g4_bf16_d128")
     dv = upload(w)
@@ -168,6 +198,7 @@ def test_fused_full_size(name, layout):
     ref = separate(dv, w, layout, split=sp)
     torch.cuda.synchronize()
     assert_bitwise(got, ref, name)
+    assert_bitwise(fused_bits(dv, w, layout, split=sp), ref, f"{name} from bit-packed masks")
     o, lse = got
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     # every tile is checked through the bitwise equality with the separate launches, whose own

@@ -163,9 +163,14 @@ def run_case(i, c, wseed, rseed):
         of, lf = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"],
                                            w.max_chunk_len, return_lse=True, v_layout=c["v_layout"],
                                            split_pages=c["split"])
+        ob, lb = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], bits, dv["cu"], dv["pl"], w.max_chunk_len,
+                                           return_lse=True, v_layout=c["v_layout"], split_pages=c["split"],
+                                           nkvb_max=w.nkvb_max)
         torch.cuda.synchronize()
         assert torch.equal(of.view(torch.int16), o.view(torch.int16)), f"sweep {i} fused output"
         assert torch.equal(lf.view(torch.int32), lse.view(torch.int32)), f"sweep {i} fused LSE"
+        assert torch.equal(ob.view(torch.int16), o.view(torch.int16)), f"sweep {i} fused output (bit masks)"
+        assert torch.equal(lb.view(torch.int32), lse.view(torch.int32)), f"sweep {i} fused LSE (bit masks)"
 
 
 N_LONG = int(os.environ.get("CPA_SWEEP_LONG_CASES", "12"))
