@@ -94,3 +94,24 @@ def test_direct_refuses_mis_shaped_plan_counts():
                 torch.zeros(1, 2, 1, dtype=torch.int32)):        # two heads for Hq = 4
         with pytest.raises(ValueError, match="plan_counts"):
             cpa.chunked_prefill_direct(q, kp, vd, pm, plans, bad, cu, pl, 64)
+
+
+def test_fused_checks_masks_before_the_device():
+    # the fused binding checks the masks' dtype, shape and (bit-packed) block count before it
+    # looks at devices, so these run on the CPU
+    q, kp, vp, pm, t, c, cu, pl = _cpu_args()
+    good = torch.zeros(1, 4, 1, 2, dtype=torch.uint8)
+    with pytest.raises(TypeError, match="masks"):
+        cpa.chunked_prefill_fused(q, kp, vp, pm, good.float(), cu, pl, 64)
+    with pytest.raises(TypeError, match="masks"):
+        cpa.chunked_prefill_fused(q, kp, vp, pm, good[0], cu, pl, 64)
+    with pytest.raises(ValueError, match="nkvb_max"):
+        cpa.chunked_prefill_fused(q, kp, vp, pm, torch.zeros(1, 4, 1, 1, dtype=torch.int64), cu, pl, 64)
+    with pytest.raises(ValueError, match=r"\[B\]\[Hq\]"):
+        cpa.chunked_prefill_fused(q, kp, vp, pm, torch.zeros(2, 4, 1, 2, dtype=torch.uint8), cu, pl, 64)
+    with pytest.raises(ValueError, match=r"\[B\]\[Hq\]"):
+        cpa.chunked_prefill_fused(q, kp, vp, pm, torch.zeros(1, 3, 1, 2, dtype=torch.uint8), cu, pl, 64)
+    with pytest.raises(TypeError, match="bf16"):
+        cpa.chunked_prefill_fused(q.float(), kp.float(), vp.float(), pm, good, cu, pl, 64)
+    with pytest.raises(TypeError, match="CUDA"):
+        cpa.chunked_prefill_fused(q, kp, vp, pm, good, cu, pl, 64)
