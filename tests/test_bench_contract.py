@@ -56,3 +56,8 @@ def test_bench_prints_one_json_line():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert d["speedup_vs_dense"]["kernel"] > 0
     assert d["table_build_bit_masks"]["tables_equal_byte_masks"] is True
+    fu = d["fused_union"]   # the fused launches, timed in turn with the separate pair
+    assert fu["outputs_equal_separate"] is True
+    assert fu["step_ms"] > 0 and fu["separate_step_ms"] > 0 and fu["bit_masks_step_ms"] > 0
+    mp = rf["measured_peak"]
+    assert mp["achieved_tflops"] > 0 and mp["engine_clock_mhz"] > 0
