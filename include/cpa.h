@@ -12,7 +12,9 @@
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise.  The caller allocates
  *     and owns every buffer; the library allocates no device memory and keeps no global state,
- *     so concurrent calls on different streams are safe.
+ *     so concurrent calls on different streams are safe.  The one exception is
+ *     cpa_chunked_prefill_split_static, whose partials live in a device array of the library
+ *     (see there).
  *   - Calls only enqueue work on `stream` (0 = the default stream) and return without
  *     synchronising.  Results are visible in stream order.
  *   - Block size: query blocks, KV blocks and KV pages all hold CPA_BLOCK = 64 tokens.
