@@ -114,8 +114,8 @@ cpa_status cpa_build_block_tables_bits(const uint64_t* mask_bits, int B, int Hq,
  * position p = prefix_len[b] + r), attends over the key tokens t of the blocks
  * tables[b][g][0 .. counts[b][g]) with t <= p (causal cut on the chunk's own blocks), reading
  * K/V in place from the paged cache through page_map; fp32 online softmax with scale sm_scale.
- * This is the "selected KV blocks accessed in place without explicit KV compaction" step of
- * the CompactAttention abstract.
+ * This is the step of the CompactAttention abstract that reads the selected KV blocks where
+ * they lie in the cache, without first gathering them into a compact copy.
  *
  *   q        [Tq][Hq][d] in `dtype`, d contiguous; rows of sequence b are cu_q[b] .. cu_q[b+1]
  *            (Tq = cu_q[B]).  16-byte aligned.
@@ -361,8 +361,8 @@ cpa_status cpa_append_kv(const void* k_new, const void* v_new, cpa_dtype dtype, 
 /*
  * cpa_build_block_plans - per-(head, query block) KV block plans: the direct block-sparse
  * execution that the Q-block and intra-group unions of the CompactAttention abstract replace
- * (the abstract's point of comparison: block-sparse kernels that run each head's mask as it is
- * lose efficiency when the query length is bounded by the chunk size).  No union: row
+ * (the abstract's point of comparison: running every head's mask directly pays off poorly when
+ * a chunk holds only a few query blocks).  No union: row
  * (b, h, qi) of the plan lists the blocks kb with masks[b][h][qi][kb] != 0 and
  * kb <= prefix_blocks[b] + qi, ascending, then -1 up to plan_cap; rows qi >= chunk_blocks[b]
  * are empty.

@@ -1,11 +1,12 @@
 // Per-(head, query block) KV block plans: the direct block-sparse execution the union replaces.
 //
 // "CompactAttention: Accelerating Chunked Prefill with Block-Union KV Selection", abstract:
-// block-sparse kernels that run each head's mask as it is lose efficiency when the query length
-// is bounded by the chunk size; the union tables are the method's answer.  To measure that
-// trade on the same hardware, this kernel builds the plans such a kernel runs: for every
-// (sequence b, query head h, query block qi) the KV blocks kb its own mask row selects, with
-// kb <= prefix_blocks[b] + qi (causally reachable), in ascending order, -1 after the last.
+// the method argues that executing every head's mask directly as a block-sparse kernel pays off
+// poorly in chunked prefill, where a chunk holds only a few query blocks, and builds the union
+// tables instead.  To measure that trade on the same hardware, this kernel builds the plans such
+// a direct kernel runs: for every (sequence b, query head h, query block qi) the KV blocks kb
+// its own mask row selects, with kb <= prefix_blocks[b] + qi (causally reachable), in ascending
+// order, -1 after the last.
 //
 // One wave per mask row.  Lane l reads 16 mask bytes (16 KV blocks) per step, turns them into
 // 16 bits, and the wave's prefix sum over the lanes' bit counts places every lane's ids.

@@ -1,9 +1,9 @@
 // Direct block-sparse chunked prefill: the baseline the union tables are measured against.
 //
 // "CompactAttention: Accelerating Chunked Prefill with Block-Union KV Selection", abstract:
-// running each head's block mask as its own block-sparse execution loses efficiency when the
-// query length is bounded by the chunk size; the union tables trade extra blocks for page reuse
-// across a group's heads and query blocks.  This kernel is that direct execution on the same
+// executing every head's block mask directly pays off poorly when a chunk holds only a few query
+// blocks, which is the method's reason for the union tables: they trade extra blocks for page
+// reuse across a group's heads and query blocks.  This kernel is that direct execution on the same
 // hardware and numerics: every (sequence, query head, query block) attends over exactly the KV
 // blocks of its own plan (cpa_build_block_plans), with no union and no page shared between
 // heads or query blocks.
