@@ -54,6 +54,21 @@ def _i32(x, name):
     return x
 
 
+def _chunk_cap(cu_q, max_chunk_len, stream, dev):
+    """max_chunk_len as given, or (None) the longest chunk cu_q[b+1] - cu_q[b], read from the
+    device on the call's stream (`stream`, else dev's current one), after the work queued there:
+    one synchronisation with that stream, so a call under graph capture must pass it."""
+    if max_chunk_len is not None:
+        return int(max_chunk_len)
+    if cu_q.numel() < 2:
+        return 0
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    if s.device != dev:
+        raise ValueError(f"the stream belongs to {s.device}, the tensors to {dev}")
+    with torch.cuda.device(dev), torch.cuda.stream(s):
+        return max(int((cu_q[1:] - cu_q[:-1]).max().item()), 0)
+
+
 def _out_buffers(out, lse, return_lse, q, dev):
     """Validate caller-given o / lse (contiguous, q's shape and dtype / float32 [Tq][Hq]) or
     allocate them."""
@@ -164,11 +179,12 @@ def build_block_plans(masks, prefix_blocks, chunk_blocks, plan_cap=None, plans=N
     return plans, plan_counts
 
 
-def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu_q, prefix_len, max_chunk_len,
+def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu_q, prefix_len, max_chunk_len=None,
                            sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None):
     """Direct block-sparse baseline: each (head, query block) over its own plan.  q bf16
     [Tq][Hq][d]; k_pages [n_pages][Hkv][64][d]; v_pages dim-major [n_pages][Hkv][d][64] (strided
-    views allowed as in chunked_prefill); plans / plan_counts from build_block_plans."""
+    views allowed as in chunked_prefill); plans / plan_counts from build_block_plans;
+    max_chunk_len as in chunked_prefill."""
     if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("the direct baseline runs bf16 q, k_pages and v_pages")
     if q.dim() != 3 or not q.is_contiguous():
@@ -192,6 +208,7 @@ def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu
         raise ValueError("inconsistent B across cu_q / prefix_len / page_map")
     dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, plans=plans,
               plan_counts=plan_counts, cu_q=cu_q, prefix_len=prefix_len)
+    max_chunk_len = _chunk_cap(cu_q, max_chunk_len, stream, dev)
     out, lse = _out_buffers(out, lse, return_lse, q, dev)
     with torch.cuda.device(dev):
         st = load().cpa_chunked_prefill_direct(
@@ -249,7 +266,7 @@ def split_workspace_bytes(total_q, Hq, d, table_cap, split_pages):
     return int(load().cpa_split_workspace_bytes(int(total_q), int(Hq), int(d), int(table_cap), int(split_pages)))
 
 
-def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len,
+def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len=None,
                     sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None, split_pages=0,
                     workspace=None, v_layout="token", k_scale=1.0, v_scale=1.0):
     """Attention of each sequence's chunk over its group's table blocks, K/V read in place.
@@ -258,7 +275,8 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     v_pages the same (v_layout "token") or dim-major [n_pages][Hkv][d][64] (v_layout "dim", any
     strided view with the token dimension contiguous); page_map int32 [B][stride]; tables int32
     [B][Hkv][cap]; counts int32 [B][Hkv]; cu_q int32 [B+1]; prefix_len int32 [B]; max_chunk_len
-    host int.  Returns (o, lse-or-None).
+    a host int at least the longest chunk, or None to read it from cu_q (one synchronisation
+    with the device).  Returns (o, lse-or-None).
 
     split_pages > 0 runs split-KV (cpa_chunked_prefill_split) with ranges of that many pages;
     the workspace (a CUDA uint8 tensor of split_workspace_bytes(...) bytes) is allocated here
@@ -307,6 +325,7 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     cap = tables.shape[2]
     dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, tables=tables,
               counts=counts, cu_q=cu_q, prefix_len=prefix_len)
+    max_chunk_len = _chunk_cap(cu_q, max_chunk_len, stream, dev)
     if auto:
         # the split kernel takes bf16 pools whose rows (tokens, or dims of dim-major V) are at
         # most 2^24 elements apart
@@ -359,7 +378,7 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
         return out, lse
 
 
-def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len, sm_scale=0.0,
+def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len=None, sm_scale=0.0,
                           out=None, lse=None, return_lse=False, stream=None, v_layout="token", split_pages=0,
                           workspace=None, nkvb_max=None):
     """The table build and the prefill in one launch (cpa_chunked_prefill_fused): every
@@ -370,7 +389,7 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
     Bit-packed masks (int64 [B][Hq][nqb_max][mask_words], as build_block_tables_bits takes them)
     need nkvb_max and run cpa_chunked_prefill_fused_bits.
     split_pages > 0 (or "auto") runs split-KV as chunked_prefill does, with nkvb_max as the table
-    capacity; the workspace is allocated here when not given."""
+    capacity; the workspace is allocated here when not given.  max_chunk_len as in chunked_prefill."""
     auto = isinstance(split_pages, str)
     if auto and split_pages != "auto":
         raise ValueError('split_pages must be an int or "auto"')
@@ -406,6 +425,7 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
         raise ValueError("inconsistent B across cu_q / prefix_len / page_map / masks")
     dev = _on(_cuda_device(q, "q"), k_pages=k_pages, v_pages=v_pages, page_map=page_map, masks=masks, cu_q=cu_q,
               prefix_len=prefix_len)
+    max_chunk_len = _chunk_cap(cu_q, max_chunk_len, stream, dev)
     nqb_max = masks.shape[2]
     nkvb_max = int(nkvb_max) if bits else masks.shape[3]
     if auto:
@@ -479,12 +499,12 @@ def chunked_prefill_split_static(q, k_pages, v_pages, page_map, tables, counts, 
     return out, lse
 
 
-def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len, v_layout="token",
+def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_chunk_len=None, v_layout="token",
               stream=None):
     """Write each sequence's chunk rows k_new / v_new [Tq][Hkv][d] into their slots of the paged
     pools in place (cpa_append_kv).  k_pages [n_pages][Hkv][64][d]; v_pages the same (v_layout
     "token") or [n_pages][Hkv][d][64] (v_layout "dim"), strided views allowed as in
-    chunked_prefill."""
+    chunked_prefill; max_chunk_len as there."""
     if k_new.dtype not in _KV_DTYPES or v_new.dtype != k_new.dtype or k_pages.dtype != k_new.dtype \
             or v_pages.dtype != k_new.dtype:
         raise TypeError("k_new, v_new and the pools must share dtype float32, bfloat16 or float8_e4m3fn")
@@ -512,6 +532,7 @@ def append_kv(k_new, v_new, k_pages, v_pages, page_map, cu_q, prefix_len, max_ch
     if cu_q.numel() != B + 1 or page_map.dim() != 2 or page_map.shape[0] != B:
         raise ValueError("inconsistent B across cu_q / prefix_len / page_map")
     _on(dev, page_map=page_map, cu_q=cu_q, prefix_len=prefix_len)
+    max_chunk_len = _chunk_cap(cu_q, max_chunk_len, stream, dev)
     with torch.cuda.device(dev):
         st = load().cpa_append_kv(_ptr(k_new), _ptr(v_new), _KV_DTYPES[k_new.dtype], _ptr(k_pages),
                                   k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),

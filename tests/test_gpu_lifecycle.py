@@ -81,3 +81,43 @@ def test_sequence_prefilled_chunk_by_chunk(v_layout, d, split):
     others = torch.ones(n_pages, dtype=torch.bool, device="cuda")
     others[pages] = False
     assert bool(torch.isnan(kp[others].float()).all()) and bool(torch.isnan(got_v[others].float()).all())
+
+
+def test_max_chunk_len_read_from_cu_q():
+    """Leaving max_chunk_len out makes the binding read the longest chunk from cu_q: every entry
+    point that takes it returns the same bits as when it is passed."""
+    print("\n[case] max_chunk_len read from cu_q", flush=True)
+    from _gpu import upload
+    w = make_workload("mcl", [128, 0, 640], [100, 256, 64], 8, 2, 64, "bf16", bern(0.4), 17)
+    dv = upload(w)
+    vdim = dv["vp"].transpose(2, 3).contiguous()
+    tables, counts = cpa.build_block_tables(dv["masks"], dv["pb"], dv["cb"], w.Hkv)
+    args = (dv["q"], dv["kp"])
+    for layout, vp in (("token", dv["vp"]), ("dim", vdim)):
+        unsplit = None
+        for split in (0, 2):
+            o1, l1 = cpa.chunked_prefill(*args, vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                                         return_lse=True, v_layout=layout, split_pages=split)
+            o2, l2 = cpa.chunked_prefill(*args, vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], return_lse=True,
+                                         v_layout=layout, split_pages=split)
+            assert torch.equal(o1, o2) and torch.equal(l1, l2), (layout, split)
+            if split == 0:
+                unsplit = o1
+        f1, _ = cpa.chunked_prefill_fused(*args, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"], w.max_chunk_len,
+                                          v_layout=layout)
+        f2, _ = cpa.chunked_prefill_fused(*args, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"], v_layout=layout)
+        assert torch.equal(f1, f2) and torch.equal(f1, unsplit), layout
+    plans, plan_counts = cpa.build_block_plans(dv["masks"], dv["pb"], dv["cb"])
+    d1, _ = cpa.chunked_prefill_direct(*args, vdim, dv["pm"], plans, plan_counts, dv["cu"], dv["pl"], w.max_chunk_len)
+    d2, _ = cpa.chunked_prefill_direct(*args, vdim, dv["pm"], plans, plan_counts, dv["cu"], dv["pl"])
+    assert torch.equal(d1, d2)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    rows = torch.randn((dv["q"].shape[0], w.Hkv, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    pools = []
+    for mcl in (w.max_chunk_len, None):
+        kp, vp = dv["kp"].clone(), dv["vp"].clone()
+        cpa.append_kv(rows, rows, kp, vp, dv["pm"], dv["cu"], dv["pl"], mcl)
+        pools.append((kp, vp))
+    assert torch.equal(pools[0][0], pools[1][0]) and torch.equal(pools[0][1], pools[1][1])
+    assert not torch.equal(pools[0][0], dv["kp"])   # the rows did land
