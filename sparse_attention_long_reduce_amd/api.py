@@ -69,6 +69,11 @@ def _chunk_cap(cu_q, max_chunk_len, stream, dev):
         return max(int((cu_q[1:] - cu_q[:-1]).max().item()), 0)
 
 
+def _scale(sm_scale):
+    """The softmax scale for the C ABI: 0 (the library then takes 1/sqrt(d)) for None."""
+    return 0.0 if sm_scale is None else float(sm_scale)
+
+
 def _out_buffers(out, lse, return_lse, q, dev):
     """Validate caller-given o / lse (contiguous, q's shape and dtype / float32 [Tq][Hq]) or
     allocate them."""
@@ -180,7 +185,7 @@ def build_block_plans(masks, prefix_blocks, chunk_blocks, plan_cap=None, plans=N
 
 
 def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu_q, prefix_len, max_chunk_len=None,
-                           sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None):
+                           sm_scale=None, out=None, lse=None, return_lse=False, stream=None):
     """Direct block-sparse baseline: each (head, query block) over its own plan.  q bf16
     [Tq][Hq][d]; k_pages [n_pages][Hkv][64][d]; v_pages dim-major [n_pages][Hkv][d][64] (strided
     views allowed as in chunked_prefill); plans / plan_counts from build_block_plans;
@@ -215,7 +220,7 @@ def chunked_prefill_direct(q, k_pages, v_pages, page_map, plans, plan_counts, cu
             _ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), _ptr(v_pages),
             v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1],
             _ptr(plans), cap, _ptr(plan_counts), nqb_max, _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
-            int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), _stream(stream, dev))
+            int(max_chunk_len), _scale(sm_scale), _ptr(out), _ptr(lse), _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_chunked_prefill_direct")
     return out, lse
@@ -267,7 +272,7 @@ def split_workspace_bytes(total_q, Hq, d, table_cap, split_pages):
 
 
 def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len=None,
-                    sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None, split_pages=0,
+                    sm_scale=None, out=None, lse=None, return_lse=False, stream=None, split_pages=0,
                     workspace=None, v_layout="token", k_scale=1.0, v_scale=1.0):
     """Attention of each sequence's chunk over its group's table blocks, K/V read in place.
 
@@ -276,7 +281,8 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     strided view with the token dimension contiguous); page_map int32 [B][stride]; tables int32
     [B][Hkv][cap]; counts int32 [B][Hkv]; cu_q int32 [B+1]; prefix_len int32 [B]; max_chunk_len
     a host int at least the longest chunk, or None to read it from cu_q (one synchronisation
-    with the device).  Returns (o, lse-or-None).
+    with the device).  sm_scale: the softmax scale, None or 0 for 1/sqrt(d).  Returns
+    (o, lse-or-None).
 
     split_pages > 0 runs split-KV (cpa_chunked_prefill_split) with ranges of that many pages;
     the workspace (a CUDA uint8 tensor of split_workspace_bytes(...) bytes) is allocated here
@@ -338,14 +344,14 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
         hs = _stream(stream, dev)
         args = (_ptr(q), _DTYPES[q.dtype], _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1),
                 k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
-                _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
+                _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out),
                 _ptr(lse))
         if fp8:
             st = load().cpa_chunked_prefill_fp8kv(
                 _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
                 1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), float(k_scale),
                 float(v_scale), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
-                _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), hs)
+                _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out), _ptr(lse), hs)
             if st != 0:
                 raise CpaError(st, "cpa_chunked_prefill_fp8kv")
             return out, lse
@@ -360,7 +366,7 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
                 _ptr(q), _DTYPES[q.dtype], _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
                 _ptr(v_pages), v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), n_pages, _ptr(page_map),
                 page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d,
-                int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq, int(split_pages) if split else 0,
+                int(max_chunk_len), _scale(sm_scale), _ptr(out), _ptr(lse), Tq, int(split_pages) if split else 0,
                 _ptr(workspace) if split else None,
                 workspace.numel() * workspace.element_size() if split else 0, hs)
             if st != 0:
@@ -378,7 +384,7 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
         return out, lse
 
 
-def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len=None, sm_scale=0.0,
+def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len=None, sm_scale=None,
                           out=None, lse=None, return_lse=False, stream=None, v_layout="token", split_pages=0,
                           workspace=None, nkvb_max=None):
     """The table build and the prefill in one launch (cpa_chunked_prefill_fused): every
@@ -443,7 +449,7 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
         head = (_ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
                 _ptr(v_pages), 1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2),
                 n_pages, _ptr(page_map), page_map.shape[1], _ptr(masks), nqb_max, nkvb_max)
-        tail = (_ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out),
+        tail = (_ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out),
                 _ptr(lse), Tq, int(split_pages) if split else 0, _ptr(workspace) if split else None,
                 workspace.numel() * workspace.element_size() if split else 0, _stream(stream, dev))
         if bits:
@@ -461,7 +467,7 @@ STATIC_SCRATCH_BYTES = 64 * 1024 * 1024   # CPA_STATIC_SCRATCH_BYTES
 
 
 def chunked_prefill_split_static(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_len, max_chunk_len,
-                                 split_pages, sm_scale=0.0, out=None, lse=None, return_lse=False, stream=None):
+                                 split_pages, sm_scale=None, out=None, lse=None, return_lse=False, stream=None):
     """Split-KV attention (token-major V pools, bf16) whose partials live in the library's own
     per-device array instead of a workspace (cpa_chunked_prefill_split_static): the call
     allocates nothing when out (and lse, if wanted) are given.  Same results as
@@ -492,7 +498,7 @@ def chunked_prefill_split_static(q, k_pages, v_pages, page_map, tables, counts, 
         st = load().cpa_chunked_prefill_split_static(
             _ptr(q), BF16, _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
             n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
-            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), float(sm_scale), _ptr(out), _ptr(lse), Tq,
+            _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out), _ptr(lse), Tq,
             int(split_pages), _stream(stream, dev))
     if st != 0:
         raise CpaError(st, "cpa_chunked_prefill_split_static")
