@@ -403,20 +403,20 @@ cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void
 /*
  * cpa_chunked_prefill_fp8kv - cpa_chunked_prefill with bf16 q / o and a KV cache of fp8 pages
  * (OCP e4m3, one byte per element): the same attention over the same tables (CompactAttention
- * abstract), over the keys decode(k) * k_scale and values decode(v) * v_scale.  Pages are
- * converted to bf16 once per workgroup, in LDS (dim-major V) or on their way into LDS
- * (token-major V); the conversion is exact, as bf16 holds every e4m3 value.  The K scale
- * joins the softmax scale and the V scale multiplies the normalised output, both in fp32.  The
- * attention is the bf16 path's (bf16 MFMA, fp32 softmax, bf16 P).  The cache takes half the
- * memory of bf16.
+ * abstract), over the keys decode(k) * k_scale and values decode(v) * v_scale.  Each page is
+ * copied into LDS as codes and, once they have landed, converted to bf16 once per workgroup
+ * into the operand-order tiles that the bf16 dim-major path reads (token-major V is transposed
+ * on the way by byte-transposing LDS reads); the conversion is exact, as bf16 holds every e4m3
+ * value.  The K scale joins the softmax scale and the V scale multiplies the normalised output,
+ * both in fp32.  The attention is the bf16 path's (bf16 MFMA, fp32 softmax, bf16 P).  The cache
+ * takes half the memory of bf16.
  *
  *   k_pages     e4m3 pool, token-major, strides (page, head, token) in elements = bytes.
  *   v_pages     e4m3 pool, token-major (v_dim_major = 0, v_row_stride = token stride) or
  *               dim-major (v_dim_major = 1, v_row_stride = dim stride), strides in bytes.
  *   k_scale, v_scale  finite, > 0 (else CPA_ERR_SHAPE): the per-tensor dequantization scales.
  * Other arguments and errors as cpa_chunked_prefill (dtype bf16 for q and o; pool strides are
- * in bytes and must be 16-byte multiples, else CPA_ERR_ALIGN).  With dim-major V the pages are staged in LDS as codes and converted at operand
- * read; with token-major V they are converted on their way into LDS.  No split-KV form.
+ * in bytes and must be 16-byte multiples, else CPA_ERR_ALIGN).  No split-KV form.
  */
 cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const void* v_pages, int64_t page_stride,
                                      int64_t head_stride, int64_t token_stride, int v_dim_major,
