@@ -403,7 +403,7 @@ def time_graph(cpa, batches, steps):
 def time_fp8kv(cpa, bt, steps, warmup=3):
     """The batch's prefill over an fp8 (e4m3) copy of its KV cache, per-tensor scale 1/4
     (cpa_chunked_prefill_fp8kv), with dim-major and with token-major V, HIP events around each
-    launch."""
+    launch (and the merge, when the batch runs split-KV: the same ranges as its bf16 prefill)."""
     import numpy as np
     import torch
     w = bt.w
@@ -416,7 +416,8 @@ def time_fp8kv(cpa, bt, steps, warmup=3):
     def timed_ms(vp, layout):
         def run():
             cpa.chunked_prefill(bt.q, kp8, vp, bt.pm, bt.tables, bt.counts, bt.cu, bt.pl, w.max_chunk_len,
-                                out=out, k_scale=0.25, v_scale=0.25, v_layout=layout)
+                                out=out, k_scale=0.25, v_scale=0.25, v_layout=layout, split_pages=bt.split_pages,
+                                workspace=bt.workspace)
         for _ in range(warmup):
             run()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -431,8 +432,10 @@ def time_fp8kv(cpa, bt, steps, warmup=3):
     ms_tok = timed_ms(vp8, "token")
     return {"prefill_ms": round(ms_dim, 4), "prefill_ms_token_major_v": round(ms_tok, 4),
             "kv_bytes": int(kp8.numel() + vp8.numel()), "kv_bytes_bf16": int(2 * (kp8.numel() + vp8.numel())),
+            "split_pages": int(bt.split_pages),
             "note": "codes staged in LDS and converted to bf16 once per workgroup; token-major V transposed "
-                    "by ds_read_b64_tr_b8 on the way"}
+                    "by ds_read_b64_tr_b8 on the way" + ("; split-KV ranges and merge as the bf16 prefill"
+                                                        if bt.split_pages else "")}
 
 
 def time_build_bits(cpa, batches, steps):
@@ -622,7 +625,7 @@ def main():
             f"{direct['prefill_ms']:.3f} ms ({direct['prefill_tflops']:.0f} TFLOP/s on {direct['flop']:.3e} "
             f"FLOP, {direct['plan_blocks']} plan blocks)")
     fp8kv = None
-    if len(batches) == 1 and batches[0].split_pages == 0:
+    if len(batches) == 1:
         fp8kv = time_fp8kv(cpa, batches[0], max(5, args.steps // 2))
         fp8kv["prefill_tflops"] = round(flops / (fp8kv["prefill_ms"] * 1e-3) / 1e12, 2)
         fp8kv["roofline"] = {"bound": "mfma", "achieved": fp8kv["prefill_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -415,8 +415,14 @@ cpa_status cpa_chunked_prefill_direct(const void* q, cpa_dtype dtype, const void
  *   v_pages     e4m3 pool, token-major (v_dim_major = 0, v_row_stride = token stride) or
  *               dim-major (v_dim_major = 1, v_row_stride = dim stride), strides in bytes.
  *   k_scale, v_scale  finite, > 0 (else CPA_ERR_SHAPE): the per-tensor dequantization scales.
+ *   total_q, split_pages, workspace, workspace_bytes  split-KV as cpa_chunked_prefill_split
+ *               (split_pages >= 1, pool row strides up to 2^24 bytes, else
+ *               CPA_ERR_UNSUPPORTED): each range's partial output already carries v_scale, and
+ *               the merge is the bf16 path's.  split_pages <= 0: no split (total_q and the
+ *               workspace are not used).
  * Other arguments and errors as cpa_chunked_prefill (dtype bf16 for q and o; pool strides are
- * in bytes and must be 16-byte multiples, else CPA_ERR_ALIGN).  No split-KV form.
+ * in bytes and must be 16-byte multiples, else CPA_ERR_ALIGN) and, with split_pages >= 1, those
+ * of cpa_chunked_prefill_split.
  */
 cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const void* v_pages, int64_t page_stride,
                                      int64_t head_stride, int64_t token_stride, int v_dim_major,
@@ -425,6 +431,7 @@ cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const v
                                      int page_map_stride, const int32_t* tables, int table_cap,
                                      const int32_t* counts, const int32_t* cu_q, const int32_t* prefix_len, int B,
                                      int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     int total_q, int split_pages, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (host pointer, never NULL). */

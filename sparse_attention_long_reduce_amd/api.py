@@ -288,9 +288,9 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     the workspace (a CUDA uint8 tensor of split_workspace_bytes(...) bytes) is allocated here
     when not given.  split_pages="auto" picks the range length with plan_split_pages for the
     device's compute units: a split when the call has fewer tiles than CUs and the split kernel
-    takes the pools (bf16, row strides up to 2^24 elements), else none.  v_layout "dim" calls
-    cpa_chunked_prefill_vt.  float8_e4m3fn pools with a bf16 q call cpa_chunked_prefill_fp8kv
-    with the dequantization scales k_scale / v_scale.
+    takes the pools (bf16 q, bf16 or fp8 pools, row strides up to 2^24 elements), else none.
+    v_layout "dim" calls cpa_chunked_prefill_vt.  float8_e4m3fn pools with a bf16 q call
+    cpa_chunked_prefill_fp8kv (split or not) with the dequantization scales k_scale / v_scale.
     """
     auto = isinstance(split_pages, str)
     if auto and split_pages != "auto":
@@ -299,8 +299,6 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
     if fp8:
         if q.dtype != torch.bfloat16 or v_pages.dtype != k_pages.dtype:
             raise TypeError("fp8 pools need float8_e4m3fn k_pages and v_pages and a bfloat16 q")
-        if split_pages and not auto:
-            raise ValueError("the fp8 KV path has no split-KV form")
     elif q.dtype not in _DTYPES or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
         raise TypeError("q, k_pages and v_pages must share dtype float32 or bfloat16")
     if q.dim() != 3 or not q.is_contiguous():
@@ -333,10 +331,9 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
               counts=counts, cu_q=cu_q, prefix_len=prefix_len)
     max_chunk_len = _chunk_cap(cu_q, max_chunk_len, stream, dev)
     if auto:
-        # the split kernel takes bf16 pools whose rows (tokens, or dims of dim-major V) are at
-        # most 2^24 elements apart
-        splittable = (q.dtype == torch.bfloat16 and not fp8
-                      and max(k_pages.stride(2), v_pages.stride(2)) <= (1 << 24))
+        # the split kernel takes bf16 or fp8 pools whose rows (tokens, or dims of dim-major V)
+        # are at most 2^24 elements apart
+        splittable = q.dtype == torch.bfloat16 and max(k_pages.stride(2), v_pages.stride(2)) <= (1 << 24)
         n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
         split_pages = plan_split_pages(B, Hq, Hkv, max_chunk_len, cap, n_cus) if splittable else 0
     out, lse = _out_buffers(out, lse, return_lse, q, dev)
@@ -346,21 +343,23 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
                 k_pages.stride(2), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts),
                 _ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out),
                 _ptr(lse))
-        if fp8:
-            st = load().cpa_chunked_prefill_fp8kv(
-                _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
-                1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), float(k_scale),
-                float(v_scale), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
-                _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out), _ptr(lse), hs)
-            if st != 0:
-                raise CpaError(st, "cpa_chunked_prefill_fp8kv")
-            return out, lse
         split = bool(split_pages and split_pages > 0)
         if split:
             need = split_workspace_bytes(Tq, Hq, d, cap, split_pages)
             if workspace is None:
                 workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             _on(dev, workspace=workspace)
+        if fp8:
+            st = load().cpa_chunked_prefill_fp8kv(
+                _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
+                1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2), float(k_scale),
+                float(v_scale), n_pages, _ptr(page_map), page_map.shape[1], _ptr(tables), cap, _ptr(counts), _ptr(cu_q),
+                _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out), _ptr(lse), Tq,
+                int(split_pages) if split else 0, _ptr(workspace) if split else None,
+                workspace.numel() * workspace.element_size() if split else 0, hs)
+            if st != 0:
+                raise CpaError(st, "cpa_chunked_prefill_fp8kv")
+            return out, lse
         if v_layout == "dim":
             st = load().cpa_chunked_prefill_vt(
                 _ptr(q), _DTYPES[q.dtype], _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),

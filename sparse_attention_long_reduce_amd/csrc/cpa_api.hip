@@ -105,6 +105,12 @@ cpa_status prepare_prefill(const void* q, cpa_dtype dtype, const void* k_pages,
   return CPA_OK;
 }
 
+// Runs a prepared prefill split into ceil(table_cap / split_pages) ranges per tile plus the
+// merge (the plain path when that is one range); defined with the split entry points below.
+cpa_status launch_split(cpa::PrefillArgs& a, cpa_dtype dtype, int64_t token_stride, const VLayout& vl,
+                        int table_cap, int Hq, int d, void* o, float* lse, int total_q, int split_pages,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -225,9 +231,11 @@ cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const v
                                      int page_map_stride, const int32_t* tables, int table_cap,
                                      const int32_t* counts, const int32_t* cu_q, const int32_t* prefix_len, int B,
                                      int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+                                     int total_q, int split_pages, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
   if (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale)) return CPA_ERR_SHAPE;
   if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
+  if (split_pages >= 1 && total_q < 0) return CPA_ERR_SHAPE;
   cpa::PrefillArgs a;
   bool nothing;
   const VLayout vl{v_page_stride, v_head_stride, v_row_stride, v_dim_major == 1};
@@ -238,7 +246,10 @@ cpa_status cpa_chunked_prefill_fp8kv(const void* q, const void* k_pages, const v
   if (st != CPA_OK || nothing) return st;
   a.kv_fp8 = 1;
   a.scale_log2 *= k_scale;   // scores of the stored values times the K scale
-  a.out_scale = v_scale;     // the output is linear in V
+  a.out_scale = v_scale;     // the output is linear in V (each split range's partial is scaled too)
+  if (split_pages >= 1)
+    return launch_split(a, CPA_BF16, token_stride, vl, table_cap, Hq, d, o, lse, total_q, split_pages, workspace,
+                        workspace_bytes, stream);
   // either V layout: the direct-to-LDS kernel stages codes and converts each page once per
   // workgroup; pools whose strides overflow its 32-bit offsets go to the register-staged kernel
   return cpa::launch_prefill(a, true, d, stream) == hipSuccess ? CPA_OK : CPA_ERR_LAUNCH;

@@ -921,9 +921,14 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if (a.kv_fp8) {   // fp8 pages, no split
-    if (a.v_dmajor) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true, false>), g, t, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true, false>), g, t, 0, s, a);
+  if (a.kv_fp8) {   // fp8 pages
+    if (a.v_dmajor) {
+      if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true, false>), g, t, 0, s, a);
+      else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true, false>), g, t, 0, s, a);
+    } else {
+      if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, true, false>), g, t, 0, s, a);
+      else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true, false>), g, t, 0, s, a);
+    }
     return hipGetLastError();
   }
   if (a.v_dmajor) {
@@ -950,8 +955,8 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
   if (a.fused)   // the caller has checked: bf16, no fp8, row strides within 32-bit offsets
     return d == 64 ? launch_bf16<64>(a, s) : launch_bf16<128>(a, s);
-  if (a.kv_fp8 && (a.n_splits > 1 || a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
-    return launch_prefill_regstaged(a, true, d, s);   // fp8 forms the direct-to-LDS kernel does not take
+  if (a.kv_fp8 && (a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
+    return launch_prefill_regstaged(a, true, d, s);   // fp8 strides past the direct-to-LDS kernel's offsets
   if (!bf16) return launch_prefill_regstaged(a, false, d, s);
   if (a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24))   // 32-bit offsets within a page
     return launch_prefill_regstaged(a, true, d, s);

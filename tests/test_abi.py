@@ -374,9 +374,9 @@ def test_direct_validation(lib):
 
 def pf8(lib, q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, vdm=0, vps=8 * 64 * 128, vhs=64 * 128,
         vrs=128, ks=1.0, vs=1.0, npages=10, pm=FAKE, pms=16, tab=FAKE, cap=16, cnt=FAKE, cu=FAKE, pl=FAKE, B=1, Hq=32,
-        Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL):
+        Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL, tq=256, sp=0, ws=NULL, wsb=0):
     return lib.cpa_chunked_prefill_fp8kv(q, k, v, ps, hs, ts, vdm, vps, vhs, vrs, ks, vs, npages, pm, pms, tab, cap,
-                                         cnt, cu, pl, B, Hq, Hkv, d, mcl, scale, o, lse, None)
+                                         cnt, cu, pl, B, Hq, Hkv, d, mcl, scale, o, lse, tq, sp, ws, wsb, None)
 
 
 def test_fp8kv_validation(lib):
@@ -395,6 +395,16 @@ def test_fp8kv_validation(lib):
     assert pf8(lib, vdm=1, vrs=72, vhs=128 * 72, vps=8 * 128 * 72) == 3
     assert pf8(lib, vrs=136, vhs=64 * 136, vps=8 * 64 * 136) == 3
     assert pf8(lib, npages=0) == 2               # a call with work needs a non-empty pool
+    # split-KV: the checks of cpa_chunked_prefill_split (ranges of 4 pages over a 16-entry table)
+    assert pf8(lib, sp=4, tq=-1) == 2
+    assert pf8(lib, sp=4) == 1                   # no workspace
+    assert pf8(lib, sp=4, ws=FAKE + 8, wsb=1 << 30) == 3
+    assert pf8(lib, sp=4, ws=FAKE, wsb=16) == 5  # workspace too small
+    need = lib.cpa_split_workspace_bytes(256, 32, 128, 16, 4)
+    assert need == 4 * 256 * 32 * 129 * 4
+    assert pf8(lib, sp=4, ws=FAKE, wsb=need - 1) == 5
+    big = 1 << 25                                # rows past the split kernel's 32-bit offsets
+    assert pf8(lib, sp=4, ws=FAKE, wsb=need, ts=big, hs=64 * big, ps=8 * 64 * big) == 4
     assert pf8(lib, B=0, q=NULL, k=NULL, v=NULL, pm=NULL, tab=NULL, cnt=NULL, cu=NULL, pl=NULL, o=NULL) == 0
 
 

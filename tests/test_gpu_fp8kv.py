@@ -3,7 +3,7 @@
 The pools hold OCP e4m3 codes; the oracle attends over its own dequantization of the same codes,
 decode(x) * scale, so the bars are those of the bf16 path.  Both V layouts run the direct-to-LDS
 kernel (codes staged in LDS, each page converted to bf16 once per workgroup; token-major V through
-transposed byte reads).  The append of fp8 rows is checked bit for bit.
+transposed byte reads), unsplit and split-KV.  The append of fp8 rows is checked bit for bit.
 """
 import numpy as np
 import pytest
@@ -51,13 +51,13 @@ def fp8_setup(w):
     return kc, vc, kdq, vdq
 
 
-def run(dv, w, tables, counts, kc, vc, v_layout):
+def run(dv, w, tables, counts, kc, vc, v_layout, split_pages=0):
     k8 = torch.from_numpy(kc).cuda().view(torch.float8_e4m3fn)
     v8 = torch.from_numpy(vc).cuda().view(torch.float8_e4m3fn)
     if v_layout == "dim":
         v8 = v8.view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn)
     return cpa.chunked_prefill(dv["q"], k8, v8, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
-                               return_lse=True, v_layout=v_layout, k_scale=KS, v_scale=VS)
+                               return_lse=True, v_layout=v_layout, k_scale=KS, v_scale=VS, split_pages=split_pages)
 
 
 @pytest.mark.parametrize("v_layout", ["token", "dim"])
@@ -80,6 +80,59 @@ def test_fp8kv_small(name, v_layout):
     assert np.array_equal(np.isfinite(lg), fin)
     if fin.any():
         assert np.max(np.abs(lg[fin] - L.T[fin])) < 2 ** -7
+
+
+@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+@pytest.mark.parametrize("name", ["g2_varlen_d128", "g4_ragged_multi", "g16_d64_ragged", "g3_ragged", "all_zero",
+                                  "zero_len_chunk"])
+def test_fp8kv_split_small(name, v_layout, split):
+    # split-KV over fp8 pages: every range's partial carries the V scale and the merge is the
+    # bf16 path's; ranges of 1 page leave many ranges empty, which must weigh nothing
+    print(f"\n[case] fp8 kv split {name} {v_layout} {split}", flush=True)
+    kw = dict(SMALL[name])
+    w = make_workload(name, kw.pop("prefix_len"), kw.pop("chunk_len"), kw.pop("Hq"), kw.pop("Hkv"), kw.pop("d"),
+                      "bf16", kw.pop("mask_fn"), 61, **kw)
+    kc, vc, kdq, vdq = fp8_setup(w)
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    o, lse = run(dv, w, tables, counts, kc, vc, v_layout, split_pages=split)
+    o1, _ = run(dv, w, tables, counts, kc, vc, v_layout)
+    torch.cuda.synchronize()
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    O, L = oracle.paged_attention(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
+    compare(w, o, O, f"fp8 split {name} {v_layout} {split}")
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(L.T)
+    assert np.array_equal(np.isfinite(lg), fin)
+    if fin.any():
+        assert np.max(np.abs(lg[fin] - L.T[fin])) < 2 ** -7
+    # the unsplit launch on the same codes: the same attention up to the partials' rounding
+    assert float((o.float() - o1.float()).abs().max()) <= 2 ** -7
+
+
+@pytest.mark.parametrize("v_layout", ["token", "dim"])
+def test_fp8kv_split_full_size_one_group(v_layout):
+    # one KV group of the 128K last chunk (the per-GPU share of an 8-way head split) over fp8
+    # pages, split for this device's CUs; sampled rows reach every tile
+    print(f"\n[case] fp8 kv split full c3s {v_layout}", flush=True)
+    w = make_config("c3s_128k_one_group")
+    kc, vc, kdq, vdq = fp8_setup(w)
+    dv = upload(w)
+    tables, counts = gpu_tables(dv, w)
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sp = cpa.plan_split_pages(w.B, w.Hq, w.Hkv, w.max_chunk_len, w.nkvb_max, n_cus)
+    assert sp > 0
+    o, lse = run(dv, w, tables, counts, kc, vc, v_layout, split_pages=sp)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    S = sample_rows(w, 256, seed=12)
+    Os, Ls = oracle.attention_rows(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv, S)
+    r = torch.from_numpy(w.cu_q[S[:, 0]] + S[:, 2]).cuda()
+    h = torch.from_numpy(S[:, 1]).cuda()
+    compare(w, o[r, h].float().cpu().numpy(), Os, f"fp8 c3s split {sp} {v_layout}")
+    assert np.max(np.abs(lse[r, h].cpu().numpy() - Ls)) < 2e-2
 
 
 @pytest.mark.parametrize("v_layout", ["token", "dim"])

@@ -147,7 +147,8 @@ def test_split_full_size(name):
 @pytest.mark.parametrize("name", ["g4_d64", "g4_ragged_multi"])
 def test_auto_split(name):
     # split_pages="auto" runs the range length plan_split_pages gives for this device: the same
-    # launch, bit for bit, as passing that length; fp8 and fp32 pools (no split-KV form) run unsplit
+    # launch, bit for bit, as passing that length, for bf16 and fp8 pools; fp32 pools (no
+    # split-KV form) run unsplit
     print(f"\n[case] auto split {name}", flush=True)
     w = make_small(name)
     dv = upload(w)
@@ -167,7 +168,7 @@ def test_auto_split(name):
     f1 = cpa.chunked_prefill(dv["q"], kq, vq, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
                              return_lse=True, split_pages="auto", k_scale=0.5, v_scale=0.5)
     f2 = cpa.chunked_prefill(dv["q"], kq, vq, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
-                             return_lse=True, k_scale=0.5, v_scale=0.5)
+                             return_lse=True, split_pages=sp, k_scale=0.5, v_scale=0.5)
     torch.cuda.synchronize()
     assert torch.equal(f1[0], f2[0]) and torch.equal(f1[1], f2[1])
     q32, k32, v32 = dv["q"].float(), dv["kp"].float(), dv["vp"].float()
