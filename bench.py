@@ -400,11 +400,32 @@ def time_graph(cpa, batches, steps):
     return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
 
 
+def alternate_ms(fns, steps, warmup):
+    """HIP-event time of each callable in `fns`, the callables taking turns launch by launch so
+    that all of them see the same clock and thermal state (the engine clock follows the power
+    drawn, and timing one after the other favours whichever runs in the cooler slot); returns
+    the mean ms of each over `steps` turns."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+          for _ in range(steps)]
+    for row in ev:
+        for f, (e0, e1) in zip(fns, row):
+            e0.record()
+            f()
+            e1.record()
+    torch.cuda.synchronize()
+    return [float(np.mean([row[i][0].elapsed_time(row[i][1]) for row in ev])) for i in range(len(fns))]
+
+
 def time_fp8kv(cpa, bt, steps, warmup=3):
     """The batch's prefill over an fp8 (e4m3) copy of its KV cache, per-tensor scale 1/4
-    (cpa_chunked_prefill_fp8kv), with dim-major and with token-major V, HIP events around each
-    launch (and the merge, when the batch runs split-KV: the same ranges as its bf16 prefill)."""
-    import numpy as np
+    (cpa_chunked_prefill_fp8kv), with dim-major and with token-major V taking turns, HIP events
+    around each launch (and the merge, when the batch runs split-KV: the same ranges as its bf16
+    prefill)."""
     import torch
     w = bt.w
     f8 = torch.float8_e4m3fn
@@ -413,23 +434,14 @@ def time_fp8kv(cpa, bt, steps, warmup=3):
     vp8d = vp8.view(torch.uint8).transpose(2, 3).contiguous().view(f8)   # dim-major copy
     out = torch.empty_like(bt.q)
 
-    def timed_ms(vp, layout):
+    def launch(vp, layout):
         def run():
             cpa.chunked_prefill(bt.q, kp8, vp, bt.pm, bt.tables, bt.counts, bt.cu, bt.pl, w.max_chunk_len,
                                 out=out, k_scale=0.25, v_scale=0.25, v_layout=layout, split_pages=bt.split_pages,
                                 workspace=bt.workspace)
-        for _ in range(warmup):
-            run()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for e0, e1 in ev:
-            e0.record()
-            run()
-            e1.record()
-        torch.cuda.synchronize()
-        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+        return run
 
-    ms_dim = timed_ms(vp8d, "dim")
-    ms_tok = timed_ms(vp8, "token")
+    ms_dim, ms_tok = alternate_ms([launch(vp8d, "dim"), launch(vp8, "token")], steps, warmup)
     return {"prefill_ms": round(ms_dim, 4), "prefill_ms_token_major_v": round(ms_tok, 4),
             "kv_bytes": int(kp8.numel() + vp8.numel()), "kv_bytes_bf16": int(2 * (kp8.numel() + vp8.numel())),
             "split_pages": int(bt.split_pages),
@@ -609,13 +621,17 @@ def main():
 
     layout_ab = None
     if not args.no_layout_ab:
-        for bt in batches:
-            bt.v_layout = other
-        alt = timed(cpa, batches, (False,), max(5, args.steps // 2), 2)[0]
+        # the two V layouts take turns launch by launch (prefill only, the tables built above)
+        def in_layout(layout):
+            def run():
+                for bt in batches:
+                    bt.v_layout = layout
+                    bt.prefill(cpa, False)
+            return run
+        ms_main, ms_other = alternate_ms([in_layout(args.v_layout), in_layout(other)], max(5, args.steps // 2), 2)
         for bt in batches:
             bt.v_layout = args.v_layout
-        again = timed(cpa, batches, (False,), max(5, args.steps // 2), 2)[0]
-        layout_ab = {args.v_layout: round(again["prefill_ms"], 4), other: round(alt["prefill_ms"], 4)}
+        layout_ab = {args.v_layout: round(ms_main, 4), other: round(ms_other, 4)}
         log(f"[bench] V layout A/B prefill ms: {layout_ab}")
 
     direct = None
