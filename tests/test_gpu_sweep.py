@@ -39,12 +39,15 @@ def draw(i):
         chunk[0] = int(rng.integers(1, 200))
     G = int(rng.choice([1, 2, 4, 8, 12, 16]))
     mode = str(rng.choice(["bf16", "bf16", "f32", "fp8"]))
-    return dict(prefix=(64 * rng.integers(0, 41, size=B)).tolist(), chunk=chunk.tolist(), G=G,
-                Hkv=int(rng.integers(1, 3 if G >= 8 else 4)), d=int(rng.choice([64, 128])),
-                p=float(rng.choice([-1.0, 0.0, 0.02, 0.1, 0.4, 1.0])), local=int(rng.integers(0, 3)),
-                mode=mode, v_layout=str(rng.choice(["token", "dim"])),
-                split=int(rng.choice([0, 0, 1, 3, 8])) if mode == "bf16" else 0,
-                scales=(float(rng.choice([0.25, 1.0, 3.0])), float(rng.choice([0.5, 2.0]))))
+    c = dict(prefix=(64 * rng.integers(0, 41, size=B)).tolist(), chunk=chunk.tolist(), G=G,
+             Hkv=int(rng.integers(1, 3 if G >= 8 else 4)), d=int(rng.choice([64, 128])),
+             p=float(rng.choice([-1.0, 0.0, 0.02, 0.1, 0.4, 1.0])), local=int(rng.integers(0, 3)),
+             mode=mode, v_layout=str(rng.choice(["token", "dim"])),
+             split=int(rng.choice([0, 0, 1, 3, 8])) if mode == "bf16" else 0,
+             scales=(float(rng.choice([0.25, 1.0, 3.0])), float(rng.choice([0.5, 2.0]))))
+    if mode == "fp8":   # fp8 pools split too; a stream of their own leaves every other draw as it was
+        c["split"] = int(np.random.default_rng(7300 + i).choice([0, 0, 1, 3, 8]))
+    return c
 
 
 def mask_fn(c):
