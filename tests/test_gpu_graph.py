@@ -20,7 +20,8 @@ def bern(p, local=1):
     return lambda rng, *a: mask_bernoulli(rng, *a, p=p, local=local)
 
 
-@pytest.mark.parametrize("mode", ["plain", "split", "dim", "bits", "fp8_token", "fp8_dim", "fused_token", "fused_dim"])
+@pytest.mark.parametrize("mode", ["plain", "split", "dim", "bits", "fp8_token", "fp8_dim", "fp8_split", "fused_token",
+                                  "fused_dim"])
 def test_capture_and_replay(mode):
     w = make_workload("graph", [0, 192, 4096], [37, 130, 255], 8, 2, 128, "bf16", bern(0.05), 81)
     dv = upload(w)
@@ -36,7 +37,7 @@ def test_capture_and_replay(mode):
     elif layout == "dim":
         vp = vp.transpose(2, 3).contiguous()
     scale = 0.25 if mode.startswith("fp8") else 1.0
-    sp = 2 if mode == "split" else 0
+    sp = 2 if mode in ("split", "fp8_split") else 0
     bits = torch.from_numpy(pack_mask_bits(w.masks).view(np.int64)).cuda()
     tables = torch.empty((w.B, w.Hkv, w.nkvb_max), dtype=torch.int32, device="cuda")
     counts = torch.empty((w.B, w.Hkv), dtype=torch.int32, device="cuda")
