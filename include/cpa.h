@@ -58,7 +58,8 @@ typedef enum {
 typedef enum {
   CPA_F32 = 0,
   CPA_BF16 = 1,
-  CPA_FP8_E4M3 = 2 /* OCP e4m3 (bias 7, no infinities); KV pools only (cpa_chunked_prefill_fp8kv, cpa_append_kv) */
+  CPA_FP8_E4M3 = 2 /* OCP e4m3 (bias 7, no infinities); KV pools only (cpa_chunked_prefill_fp8kv,
+                      cpa_chunked_prefill_fused(_bits), cpa_append_kv) */
 } cpa_dtype;
 
 /*
@@ -268,7 +269,8 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
  * bitwise that of cpa_build_block_tables with prefix_blocks[b] = prefix_len[b] / 64 and
  * chunk_blocks[b] = ceil(chunk length / 64), followed by cpa_chunked_prefill (v_dim_major = 0)
  * or cpa_chunked_prefill_vt (v_dim_major = 1) on those tables with table_cap = nkvb_max (the
- * same split ranges when split_pages >= 1).
+ * same split ranges when split_pages >= 1); with fp8 pools, followed by
+ * cpa_chunked_prefill_fp8kv with the same scales.
  *
  * Why: chunked prefill repeats the table build at every chunk (CompactAttention abstract); one
  * launch instead of two removes a launch and its gap per chunk.  Every tile of a group repeats
@@ -282,14 +284,18 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
  *   v_dim_major, v_page_stride, v_head_stride, v_row_stride  the V pool as cpa_append_kv
  *            describes it: token-major (0, v_row_stride = token stride) or dim-major (1,
  *            v_row_stride = dim stride).
+ *   kv_dtype, k_scale, v_scale  the pools' element type: CPA_BF16 (the scales are not used), or
+ *            CPA_FP8_E4M3 with the per-tensor dequantization scales of
+ *            cpa_chunked_prefill_fp8kv (finite, > 0, else CPA_ERR_SHAPE; pool strides in bytes,
+ *            16-byte multiples).  Any other kv_dtype: CPA_ERR_UNSUPPORTED.
  *   total_q, split_pages, workspace, workspace_bytes  split-KV as cpa_chunked_prefill_split, with
  *            nkvb_max in the place of table_cap: n_splits = ceil(nkvb_max / split_pages), and the
  *            workspace needs cpa_split_workspace_bytes(total_q, Hq, d, nkvb_max, split_pages)
  *            bytes.  split_pages <= 0: no split (total_q and the workspace are not used).  Each
  *            range's workgroup builds the union itself.
  * Other arguments as cpa_chunked_prefill.
- * Supported: CPA_BF16, d in {64, 128}, any G, row strides (token_stride, v_row_stride) up to
- * 2^24 elements (else CPA_ERR_UNSUPPORTED).
+ * Supported: dtype (of q and o) CPA_BF16, d in {64, 128}, any G, row strides (token_stride,
+ * v_row_stride) up to 2^24 elements (else CPA_ERR_UNSUPPORTED).
  * Errors: those of cpa_chunked_prefill (without the table checks) and, with split_pages >= 1, of
  * cpa_chunked_prefill_split; CPA_ERR_SHAPE (v_dim_major not 0 or 1, nqb_max or nkvb_max
  * negative, nkvb_max > CPA_MAX_KV_BLOCKS), CPA_ERR_NULL (masks NULL with nqb_max, nkvb_max > 0).
@@ -297,8 +303,9 @@ cpa_status cpa_chunked_prefill_vt(const void* q, cpa_dtype dtype, const void* k_
 cpa_status cpa_chunked_prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
                                      int64_t head_stride, int64_t token_stride, const void* v_pages,
                                      int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
-                                     int64_t v_row_stride, int64_t n_pages, const int32_t* page_map,
-                                     int page_map_stride, const uint8_t* masks, int nqb_max, int nkvb_max,
+                                     int64_t v_row_stride, cpa_dtype kv_dtype, float k_scale, float v_scale,
+                                     int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                                     const uint8_t* masks, int nqb_max, int nkvb_max,
                                      const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv,
                                      int d, int max_chunk_len, float sm_scale, void* o, float* lse, int total_q,
                                      int split_pages, void* workspace, size_t workspace_bytes,
@@ -319,8 +326,9 @@ cpa_status cpa_chunked_prefill_fused(const void* q, cpa_dtype dtype, const void*
 cpa_status cpa_chunked_prefill_fused_bits(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
                                           int64_t head_stride, int64_t token_stride, const void* v_pages,
                                           int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
-                                          int64_t v_row_stride, int64_t n_pages, const int32_t* page_map,
-                                          int page_map_stride, const uint64_t* mask_bits, int nqb_max, int nkvb_max,
+                                          int64_t v_row_stride, cpa_dtype kv_dtype, float k_scale, float v_scale,
+                                          int64_t n_pages, const int32_t* page_map, int page_map_stride,
+                                          const uint64_t* mask_bits, int nqb_max, int nkvb_max,
                                           int mask_words, const int32_t* cu_q, const int32_t* prefix_len, int B,
                                           int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o,
                                           float* lse, int total_q, int split_pages, void* workspace,

@@ -39,11 +39,13 @@ def load():
                                               vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, i32, i32, vp,
                                               c.c_size_t, vp]
     lib.cpa_chunked_prefill_fused.restype = i32
-    lib.cpa_chunked_prefill_fused.argtypes = [vp, i32, vp, i64, i64, i64, vp, i32, i64, i64, i64, i64, vp, i32, vp,
+    lib.cpa_chunked_prefill_fused.argtypes = [vp, i32, vp, i64, i64, i64, vp, i32, i64, i64, i64, i32, f32, f32, i64, vp,
+                                              i32, vp,
                                               i32, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, i32, i32,
                                               vp, c.c_size_t, vp]
     lib.cpa_chunked_prefill_fused_bits.restype = i32
-    lib.cpa_chunked_prefill_fused_bits.argtypes = [vp, i32, vp, i64, i64, i64, vp, i32, i64, i64, i64, i64, vp, i32,
+    lib.cpa_chunked_prefill_fused_bits.argtypes = [vp, i32, vp, i64, i64, i64, vp, i32, i64, i64, i64, i32, f32, f32,
+                                                   i64, vp, i32,
                                                    vp, i32, i32, i32, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp,
                                                    i32, i32, vp, c.c_size_t, vp]
     lib.cpa_chunked_prefill.restype = i32

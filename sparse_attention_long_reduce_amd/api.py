@@ -385,12 +385,14 @@ def chunked_prefill(q, k_pages, v_pages, page_map, tables, counts, cu_q, prefix_
 
 def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len, max_chunk_len=None, sm_scale=None,
                           out=None, lse=None, return_lse=False, stream=None, v_layout="token", split_pages=0,
-                          workspace=None, nkvb_max=None):
+                          workspace=None, nkvb_max=None, k_scale=1.0, v_scale=1.0):
     """The table build and the prefill in one launch (cpa_chunked_prefill_fused): every
     workgroup ORs its KV group's rows of masks (uint8 [B][Hq][nqb_max][nkvb_max]) itself, with
     prefix_blocks = prefix_len / 64 and chunk_blocks = ceil(chunk length / 64).  Bitwise the
     result of build_block_tables followed by chunked_prefill on the same inputs (tables of
-    capacity nkvb_max).  bf16 q and pools; k_pages / v_pages / v_layout as in chunked_prefill.
+    capacity nkvb_max).  bf16 q; bf16 pools, or float8_e4m3fn pools with the dequantization
+    scales k_scale / v_scale as chunked_prefill takes them; k_pages / v_pages / v_layout as in
+    chunked_prefill.
     Bit-packed masks (int64 [B][Hq][nqb_max][mask_words], as build_block_tables_bits takes them)
     need nkvb_max and run cpa_chunked_prefill_fused_bits.
     split_pages > 0 (or "auto") runs split-KV as chunked_prefill does, with nkvb_max as the table
@@ -398,8 +400,9 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
     auto = isinstance(split_pages, str)
     if auto and split_pages != "auto":
         raise ValueError('split_pages must be an int or "auto"')
-    if q.dtype != torch.bfloat16 or k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
-        raise TypeError("the fused path runs bf16 q, k_pages and v_pages")
+    if (q.dtype != torch.bfloat16 or k_pages.dtype not in (torch.bfloat16, torch.float8_e4m3fn)
+            or v_pages.dtype != k_pages.dtype):
+        raise TypeError("the fused path runs a bf16 q over bf16 or float8_e4m3fn k_pages and v_pages")
     if q.dim() != 3 or not q.is_contiguous():
         raise TypeError("q must be a contiguous [Tq][Hq][d] tensor")
     Tq, Hq, d = q.shape
@@ -447,7 +450,8 @@ def chunked_prefill_fused(q, k_pages, v_pages, page_map, masks, cu_q, prefix_len
             _on(dev, workspace=workspace)
         head = (_ptr(q), BF16, _ptr(k_pages), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2),
                 _ptr(v_pages), 1 if v_layout == "dim" else 0, v_pages.stride(0), v_pages.stride(1), v_pages.stride(2),
-                n_pages, _ptr(page_map), page_map.shape[1], _ptr(masks), nqb_max, nkvb_max)
+                _KV_DTYPES[k_pages.dtype], float(k_scale), float(v_scale), n_pages, _ptr(page_map),
+                page_map.shape[1], _ptr(masks), nqb_max, nkvb_max)
         tail = (_ptr(cu_q), _ptr(prefix_len), B, Hq, Hkv, d, int(max_chunk_len), _scale(sm_scale), _ptr(out),
                 _ptr(lse), Tq, int(split_pages) if split else 0, _ptr(workspace) if split else None,
                 workspace.numel() * workspace.element_size() if split else 0, _stream(stream, dev))

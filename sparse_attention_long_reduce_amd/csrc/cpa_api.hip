@@ -418,13 +418,18 @@ namespace {
 // instead of the byte masks.
 cpa_status prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride,
                          int64_t head_stride, int64_t token_stride, const void* v_pages, int v_dim_major,
-                         int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride, int64_t n_pages,
+                         int64_t v_page_stride, int64_t v_head_stride, int64_t v_row_stride, cpa_dtype kv_dtype,
+                         float k_scale, float v_scale, int64_t n_pages,
                          const int32_t* page_map, int page_map_stride, const uint8_t* masks,
                          const uint64_t* mask_bits, bool bits, int nqb_max, int nkvb_max, int mask_words,
                          const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
                          int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (v_dim_major != 0 && v_dim_major != 1) return CPA_ERR_SHAPE;
+  if (kv_dtype != CPA_BF16 && kv_dtype != CPA_FP8_E4M3) return CPA_ERR_UNSUPPORTED;
+  const bool fp8 = kv_dtype == CPA_FP8_E4M3;
+  if (fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f) || std::isinf(k_scale) || std::isinf(v_scale)))
+    return CPA_ERR_SHAPE;
   if (nqb_max < 0 || nkvb_max < 0 || nkvb_max > CPA_MAX_KV_BLOCKS) return CPA_ERR_SHAPE;
   if (bits && (mask_words < 0 || mask_words < (nkvb_max + 63) / 64)) return CPA_ERR_SHAPE;
   if (split_pages > 0 && total_q < 0) return CPA_ERR_SHAPE;
@@ -434,7 +439,7 @@ cpa_status prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, in
   const cpa_status st = prepare_prefill(q, dtype, k_pages, v_pages, page_stride, head_stride, token_stride, vl,
                                         n_pages, page_map, page_map_stride, nullptr, 0, nullptr, cu_q, prefix_len,
                                         B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse, a, &nothing,
-                                        /*kv_elem_bytes=*/0, /*with_tables=*/false);
+                                        /*kv_elem_bytes=*/fp8 ? 1 : 0, /*with_tables=*/false);
   if (st != CPA_OK || nothing) return st;
   const bool need = nqb_max > 0 && nkvb_max > 0;   // there are mask entries to read
   if (bits ? (need && !mask_bits) : (need && !masks)) return CPA_ERR_NULL;
@@ -442,6 +447,11 @@ cpa_status prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, in
   // the direct-to-LDS bf16 kernel: 32-bit offsets within a page
   if (dtype != CPA_BF16 || token_stride > (1 << 24) || v_row_stride > (1 << 24)) return CPA_ERR_UNSUPPORTED;
   a.fused = 1;
+  if (fp8) {   // as cpa_chunked_prefill_fp8kv: the K scale joins the softmax scale, the V scale the output
+    a.kv_fp8 = 1;
+    a.scale_log2 *= k_scale;
+    a.out_scale = v_scale;
+  }
   a.mask_nqb = nqb_max;
   a.mask_nkvb = nkvb_max;
   if (bits) {   // a NULL mask_bits (nothing to read) runs the byte path, which then reads nothing
@@ -461,12 +471,13 @@ cpa_status prefill_fused(const void* q, cpa_dtype dtype, const void* k_pages, in
 extern "C" cpa_status cpa_chunked_prefill_fused(
     const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride, int64_t head_stride,
     int64_t token_stride, const void* v_pages, int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
-    int64_t v_row_stride, int64_t n_pages, const int32_t* page_map, int page_map_stride, const uint8_t* masks,
-    int nqb_max, int nkvb_max, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq, int Hkv, int d,
-    int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages, void* workspace,
-    size_t workspace_bytes, hipStream_t stream) {
+    int64_t v_row_stride, cpa_dtype kv_dtype, float k_scale, float v_scale, int64_t n_pages, const int32_t* page_map,
+    int page_map_stride, const uint8_t* masks, int nqb_max, int nkvb_max, const int32_t* cu_q,
+    const int32_t* prefix_len, int B, int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+    int total_q, int split_pages, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return prefill_fused(q, dtype, k_pages, page_stride, head_stride, token_stride, v_pages, v_dim_major,
-                       v_page_stride, v_head_stride, v_row_stride, n_pages, page_map, page_map_stride, masks, nullptr,
+                       v_page_stride, v_head_stride, v_row_stride, kv_dtype, k_scale, v_scale, n_pages, page_map,
+                       page_map_stride, masks, nullptr,
                        false, nqb_max, nkvb_max, 0, cu_q, prefix_len, B, Hq, Hkv, d, max_chunk_len, sm_scale, o, lse,
                        total_q, split_pages, workspace, workspace_bytes, stream);
 }
@@ -474,12 +485,13 @@ extern "C" cpa_status cpa_chunked_prefill_fused(
 extern "C" cpa_status cpa_chunked_prefill_fused_bits(
     const void* q, cpa_dtype dtype, const void* k_pages, int64_t page_stride, int64_t head_stride,
     int64_t token_stride, const void* v_pages, int v_dim_major, int64_t v_page_stride, int64_t v_head_stride,
-    int64_t v_row_stride, int64_t n_pages, const int32_t* page_map, int page_map_stride, const uint64_t* mask_bits,
-    int nqb_max, int nkvb_max, int mask_words, const int32_t* cu_q, const int32_t* prefix_len, int B, int Hq,
-    int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse, int total_q, int split_pages,
-    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int64_t v_row_stride, cpa_dtype kv_dtype, float k_scale, float v_scale, int64_t n_pages, const int32_t* page_map,
+    int page_map_stride, const uint64_t* mask_bits, int nqb_max, int nkvb_max, int mask_words, const int32_t* cu_q,
+    const int32_t* prefix_len, int B, int Hq, int Hkv, int d, int max_chunk_len, float sm_scale, void* o, float* lse,
+    int total_q, int split_pages, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return prefill_fused(q, dtype, k_pages, page_stride, head_stride, token_stride, v_pages, v_dim_major,
-                       v_page_stride, v_head_stride, v_row_stride, n_pages, page_map, page_map_stride, nullptr,
+                       v_page_stride, v_head_stride, v_row_stride, kv_dtype, k_scale, v_scale, n_pages, page_map,
+                       page_map_stride, nullptr,
                        mask_bits, true, nqb_max, nkvb_max, mask_words, cu_q, prefix_len, B, Hq, Hkv, d,
                        max_chunk_len, sm_scale, o, lse, total_q, split_pages, workspace, workspace_bytes, stream);
 }

@@ -164,7 +164,6 @@ using IC = std::integral_constant<int, I>;
 // The K scale is folded into the softmax scale and the V scale into the output (a.out_scale).
 template <int D, bool SPLIT, bool VT, bool F8, bool FU>
 __global__ __launch_bounds__(THREADS) void prefill_bf16_kernel(const PrefillArgs a) {
-  static_assert(!(FU && F8), "the fused union runs the bf16 paths");
   using GE = Geo<D>;
   constexpr bool VOP = VT || F8;   // V tiles in operand order (8 keys of one dim per slot)
   constexpr int NPW = F8 ? (GE::NPW / 2 > 0 ? GE::NPW / 2 : 1) : GE::NPW;   // copies per wave and page
@@ -911,6 +910,16 @@ hipError_t launch_bf16(const PrefillArgs& a, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   const bool split = a.n_splits > 1;
   const dim3 g(grid), t(THREADS);
+  if (a.fused && a.kv_fp8) {   // fp8 pages
+    if (a.v_dmajor) {
+      if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, true, true>), g, t, 0, s, a);
+      else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true, true>), g, t, 0, s, a);
+    } else {
+      if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, true, true>), g, t, 0, s, a);
+      else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true, true>), g, t, 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (a.fused) {   // bf16 pages
     if (a.v_dmajor) {
       if (split) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true, false, true>), g, t, 0, s, a);
@@ -953,7 +962,7 @@ hipError_t launch_split_merge(const MergeArgs& m, int d, hipStream_t s) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool bf16, int d, hipStream_t s) {
-  if (a.fused)   // the caller has checked: bf16, no fp8, row strides within 32-bit offsets
+  if (a.fused)   // the caller has checked: bf16 q, row strides within 32-bit offsets
     return d == 64 ? launch_bf16<64>(a, s) : launch_bf16<128>(a, s);
   if (a.kv_fp8 && (a.token_stride > (1 << 24) || a.v_row_stride > (1 << 24)))
     return launch_prefill_regstaged(a, true, d, s);   // fp8 strides past the direct-to-LDS kernel's offsets

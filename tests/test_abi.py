@@ -225,12 +225,12 @@ def pfv(lib, dtype=1, total_q=256, split=0, ws=NULL, ws_bytes=0, vps=8 * 128 * 6
 
 
 def pfu(lib, dtype=1, vdm=1, vps=8 * 128 * 64, vhs=128 * 64, vrs=64, masks=FAKE, nqb=4, nkvb=16, total_q=256,
-        split=0, ws=NULL, ws_bytes=0, **kw):
+        split=0, ws=NULL, ws_bytes=0, kvd=1, ks=1.0, vs=1.0, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
              cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL)
     a.update(kw)
     return lib.cpa_chunked_prefill_fused(a["q"], dtype, a["k"], a["ps"], a["hs"], a["ts"], a["v"], vdm, vps, vhs,
-                                         vrs, a["npages"], a["pm"], a["pms"], masks, nqb,
+                                         vrs, kvd, ks, vs, a["npages"], a["pm"], a["pms"], masks, nqb,
                                          nkvb, a["cu"], a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"], a["mcl"],
                                          a["scale"], a["o"], a["lse"], total_q, split, ws, ws_bytes, None)
 
@@ -262,14 +262,25 @@ def test_fused_validation(lib):
     assert pfu(lib, split=4, ws=FAKE, ws_bytes=16) == 5
     assert lib.cpa_split_workspace_bytes(256, 32, 128, 16, 4) == 4 * 256 * 32 * 129 * 4
     assert pfu(lib, split=16, ws=NULL, masks=NULL, nkvb=0, dtype=0) == 4   # no mask columns: NULL masks pass, dtype still checked
+    # the pools' element type: bf16, or fp8 with finite positive scales and 16-byte byte strides
+    assert pfu(lib, kvd=0) == 4                       # fp32 pools
+    assert pfu(lib, kvd=7) == 4
+    assert pfu(lib, kvd=2, ks=0.0) == 2
+    assert pfu(lib, kvd=2, vs=float("inf")) == 2
+    assert pfu(lib, kvd=2, vs=float("nan")) == 2
+    assert pfu(lib, kvd=2, ts=136, hs=64 * 136, ps=8 * 64 * 136) == 3   # fp8 strides are bytes
+    assert pfu(lib, kvd=2, vrs=72, vhs=128 * 72, vps=8 * 128 * 72) == 3
+    assert pfu(lib, kvd=2, split=4) == 1              # fp8 split: 4 ranges and no workspace
+    assert pfu(lib, kvd=2, split=4, ws=FAKE, ws_bytes=16) == 5
 
 
-def pfb(lib, masks=FAKE, nqb=4, nkvb=100, words=2, dtype=1, **kw):
+def pfb(lib, masks=FAKE, nqb=4, nkvb=100, words=2, dtype=1, kvd=1, ks=1.0, vs=1.0, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, ps=8 * 64 * 128, hs=64 * 128, ts=128, npages=10, pm=FAKE, pms=16,
              cu=FAKE, pl=FAKE, B=1, Hq=32, Hkv=8, d=128, mcl=256, scale=0.0, o=FAKE, lse=NULL)
     a.update(kw)
     return lib.cpa_chunked_prefill_fused_bits(a["q"], dtype, a["k"], a["ps"], a["hs"], a["ts"], a["v"], 1,
-                                              8 * 128 * 64, 128 * 64, 64, a["npages"], a["pm"], a["pms"], masks, nqb,
+                                              8 * 128 * 64, 128 * 64, 64, kvd, ks, vs, a["npages"], a["pm"], a["pms"],
+                                              masks, nqb,
                                               nkvb, words, a["cu"], a["pl"], a["B"], a["Hq"], a["Hkv"], a["d"],
                                               a["mcl"], a["scale"], a["o"], a["lse"], 256, 0, NULL, 0, None)
 
@@ -283,6 +294,8 @@ def test_fused_bits_validation(lib):
     assert pfb(lib, masks=NULL, nkvb=0, words=0, dtype=0) == 4   # nothing to read: NULL passes
     assert pfb(lib, q=NULL) == 1
     assert pfb(lib, B=0, q=NULL, masks=NULL) == 0
+    assert pfb(lib, kvd=2, ks=-1.0) == 2
+    assert pfb(lib, kvd=3) == 4
 
 
 def test_vt_validation(lib):

@@ -107,6 +107,66 @@ def test_fused_small(name, layout, split):
         assert np.max(np.abs(lg[fin] - L.T[fin])) < 2 ** -7
 
 
+KS, VS = 0.37, 1.9   # fp8 dequantization scales
+
+
+def fp8_pools(w, layout):
+    """e4m3 copies of the workload's pools (values / scale), V in the given layout, and the
+    oracle's dequantization of the same codes."""
+    f8 = torch.float8_e4m3fn
+    kc = (torch.from_numpy(w.k_pages) / KS).to(f8)
+    vc = (torch.from_numpy(w.v_pages) / VS).to(f8)
+    kdq = oracle.dequant_e4m3(kc.view(torch.uint8).numpy(), KS)
+    vdq = oracle.dequant_e4m3(vc.view(torch.uint8).numpy(), VS)
+    kp, vp = kc.cuda(), vc.cuda()
+    if layout == "dim":
+        vp = vp.view(torch.uint8).transpose(2, 3).contiguous().view(f8)
+    return kp, vp, kdq, vdq
+
+
+@pytest.mark.parametrize("split", [0, 3])
+@pytest.mark.parametrize("layout", ["dim", "token"])
+@pytest.mark.parametrize("name", ["g4_bf16_d128", "g2_varlen_d128", "g3_bf16_ragged", "g5_bf16_d64",
+                                  "g4_ragged_multi_8groups", "all_zero", "zero_len_chunk", "long_table_refills"])
+def test_fused_fp8_small(name, layout, split):
+    # fp8 pages: the fused launch reproduces the table build followed by the fp8 prefill (split or
+    # not) bit for bit, from byte and from bit-packed masks
+    w = make_small(name)
+    print(f"\n[case] fused fp8 {name} v_layout={layout} split_pages={split}", flush=True)
+    dv = upload(w)
+    kp, vp, kdq, vdq = fp8_pools(w, layout)
+    got = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"], w.max_chunk_len,
+                                    return_lse=True, v_layout=layout, split_pages=split, k_scale=KS, v_scale=VS)
+    bits = torch.from_numpy(pack_mask_bits(w.masks).view(np.int64)).cuda()
+    got_bits = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], bits, dv["cu"], dv["pl"], w.max_chunk_len,
+                                         return_lse=True, v_layout=layout, split_pages=split, nkvb_max=w.nkvb_max,
+                                         k_scale=KS, v_scale=VS)
+    tables, counts = cpa.build_block_tables(dv["masks"], dv["pb"], dv["cb"], w.Hkv, table_cap=max(w.nkvb_max, 1))
+    ref = cpa.chunked_prefill(dv["q"], kp, vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                              return_lse=True, v_layout=layout, split_pages=split, k_scale=KS, v_scale=VS)
+    torch.cuda.synchronize()
+    assert_bitwise(got, ref, f"fp8 {name}")
+    assert_bitwise(got_bits, ref, f"fp8 {name} from bit-packed masks")
+    T, C = oracle.block_union_tables(w.masks, w.prefix_blocks, w.chunk_blocks, w.Hkv, w.nkvb_max)
+    O, L = oracle.paged_attention(w.q, kdq, vdq, w.page_map, T, C, w.cu_q, w.prefix_len, w.Hkv)
+    compare(w, got[0], O, f"fp8 {name} fused")
+
+
+def test_fused_fp8_full_size_128k():
+    # the 128K last chunk over fp8 pages (dim-major V), fused against the separate launches
+    print("\n[case] fused fp8 c3 dim", flush=True)
+    w = make_config("c3_128k_last_chunk")
+    dv = upload(w)
+    kp, vp, _, _ = fp8_pools(w, "dim")
+    got = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"], w.max_chunk_len,
+                                    return_lse=True, v_layout="dim", k_scale=KS, v_scale=VS)
+    tables, counts = cpa.build_block_tables(dv["masks"], dv["pb"], dv["cb"], w.Hkv)
+    ref = cpa.chunked_prefill(dv["q"], kp, vp, dv["pm"], tables, counts, dv["cu"], dv["pl"], w.max_chunk_len,
+                              return_lse=True, v_layout="dim", k_scale=KS, v_scale=VS)
+    torch.cuda.synchronize()
+    assert_bitwise(got, ref, "fp8 c3")
+
+
 def test_fused_unaligned_and_odd_width_masks():
     # masks whose rows are not a multiple of 16 bytes, and masks at an odd address, take the
     # byte-at-a-time reads; padding columns past each sequence's extent hold noise that the

@@ -21,22 +21,23 @@ def bern(p, local=1):
 
 
 @pytest.mark.parametrize("mode", ["plain", "split", "dim", "bits", "fp8_token", "fp8_dim", "fp8_split", "fused_token",
-                                  "fused_dim"])
+                                  "fused_dim", "fused_fp8"])
 def test_capture_and_replay(mode):
     w = make_workload("graph", [0, 192, 4096], [37, 130, 255], 8, 2, 128, "bf16", bern(0.05), 81)
     dv = upload(w)
     kp = dv["kp"]
     vp = dv["vp"]
-    if mode.startswith("fp8"):   # e4m3 copies of the pools, scale 1/4
+    fp8 = mode.startswith("fp8") or mode == "fused_fp8"
+    if fp8:   # e4m3 copies of the pools, scale 1/4
         kp = (kp.float() * 4).to(torch.float8_e4m3fn)
         vp = (vp.float() * 4).to(torch.float8_e4m3fn)
-    layout = "dim" if mode in ("dim", "fp8_dim", "fused_dim") else "token"
+    layout = "dim" if mode in ("dim", "fp8_dim", "fused_dim", "fused_fp8") else "token"
     fused = mode.startswith("fused")
-    if layout == "dim" and mode.startswith("fp8"):
+    if layout == "dim" and fp8:
         vp = vp.view(torch.uint8).transpose(2, 3).contiguous().view(torch.float8_e4m3fn)
     elif layout == "dim":
         vp = vp.transpose(2, 3).contiguous()
-    scale = 0.25 if mode.startswith("fp8") else 1.0
+    scale = 0.25 if fp8 else 1.0
     sp = 2 if mode in ("split", "fp8_split") else 0
     bits = torch.from_numpy(pack_mask_bits(w.masks).view(np.int64)).cuda()
     tables = torch.empty((w.B, w.Hkv, w.nkvb_max), dtype=torch.int32, device="cuda")
@@ -49,7 +50,7 @@ def test_capture_and_replay(mode):
     def step():
         if fused:   # one launch, no tables
             cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"], w.max_chunk_len,
-                                      out=out, lse=lse, v_layout=layout)
+                                      out=out, lse=lse, v_layout=layout, k_scale=scale, v_scale=scale)
             return
         if mode == "bits":
             cpa.build_block_tables_bits(bits, w.nkvb_max, dv["pb"], dv["cb"], w.Hkv, tables=tables, counts=counts)
@@ -65,7 +66,7 @@ def test_capture_and_replay(mode):
     if fused:   # the same bits as the two separate launches
         tb, cn = cpa.build_block_tables(dv["masks"], dv["pb"], dv["cb"], w.Hkv)
         o_sep, l_sep = cpa.chunked_prefill(dv["q"], kp, vp, dv["pm"], tb, cn, dv["cu"], dv["pl"], w.max_chunk_len,
-                                           return_lse=True, v_layout=layout)
+                                           return_lse=True, v_layout=layout, k_scale=scale, v_scale=scale)
         torch.cuda.synchronize()
         assert torch.equal(o_ref, o_sep) and torch.equal(l_ref, l_sep)
 

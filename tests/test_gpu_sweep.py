@@ -149,6 +149,14 @@ def run_case(i, c, wseed, rseed):
     if c["p"] < 0:
         assert torch.all(o == 0)
 
+    if mode == "fp8":   # the fused launch over the same fp8 pools: bitwise the separate launches
+        of, lf = cpa.chunked_prefill_fused(dv["q"], kp, vp, dv["pm"], dv["masks"], dv["cu"], dv["pl"],
+                                           w.max_chunk_len, return_lse=True, v_layout=c["v_layout"],
+                                           split_pages=c["split"], k_scale=ks, v_scale=vs)
+        torch.cuda.synchronize()
+        assert torch.equal(of.view(torch.int16), o.view(torch.int16)), f"sweep {i} fused fp8 output"
+        assert torch.equal(lf.view(torch.int32), lse.view(torch.int32)), f"sweep {i} fused fp8 LSE"
+
     # the direct baseline on the same pools
     if mode == "bf16":
         plans, pc = cpa.build_block_plans(dv["masks"], dv["pb"], dv["cb"])
